@@ -1,0 +1,129 @@
+"""Pins of the oracle's window algebra (CPU only).
+
+* With quantisation disabled the buffered window form (what a decode kernel
+  computes: fixed window-start state plus buffered rank-one updates and
+  decay ratios, compensators at window position 0) must equal the exact
+  recurrence to 1e-10 for every window length, compensator count, GDN and
+  KDA, with staggered window starts.
+* With quantisation on, the plain definition and the buffered form must agree
+  (both quantise only at window ends).
+* A window of one token with no compensators must reduce to naive per-token
+  requantisation, here written element by element.
+"""
+import numpy as np
+import pytest
+
+from oracle import leapquant_oracle as lq
+from tests.oracle_inputs import planted_state, random_tokens
+
+
+def _exact(S, toks):
+    outs = []
+    for t in toks:
+        S, o, _ = lq.exact_step(S, t["q"], t["k"], t["v"], t["g"], t["beta"])
+        outs.append(o)
+    return np.array(outs), S
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 16, 32])
+def test_windowed_unquantised_equals_exact_recurrence(W, kda):
+    rng = np.random.default_rng(100 + W + 1000 * kda)
+    B, H, dk, dv, steps = 3, 2, 8, 6, 70
+    N = B * H
+    S0 = planted_state(rng, N, dk, dv)
+    toks = random_tokens(rng, steps, N, dk, dv, kda=kda, decay_scale=0.2)
+    off_seq = np.array([0, W // 2, W - 1])
+    win_len = np.full(N, W)
+    win_off = np.repeat(off_seq, H)
+    ref, _ = _exact(S0.copy(), toks)
+    for r in (0, 1, 2, 4):
+        out = lq.run_buffered(S0, toks, win_len, win_off, w_max=W, r=r, quantize=False, kda=kda)
+        err = np.max(np.abs(out["o"] - ref)) / np.max(np.abs(ref))
+        assert err <= 1e-10, (W, r, err)
+        # the plain definition with quantisation off is the exact recurrence too
+        dense = lq.run_dense(S0, toks, win_len, win_off, r=r, quantize=False)
+        assert np.max(np.abs(dense["o"] - ref)) / np.max(np.abs(ref)) <= 1e-10
+
+
+def test_windowed_unquantised_mixed_windows_and_partial_first_window():
+    """Per-sequence W (16 / 32) with offsets inside the first window."""
+    rng = np.random.default_rng(7)
+    H, dk, dv, steps = 2, 8, 8, 80
+    W_seq = np.array([16, 32, 16, 32])
+    off_seq = np.array([3, 15, 0, 9])
+    N = len(W_seq) * H
+    S0 = planted_state(rng, N, dk, dv)
+    toks = random_tokens(rng, steps, N, dk, dv)
+    ref, _ = _exact(S0.copy(), toks)
+    out = lq.run_buffered(S0, toks, np.repeat(W_seq, H), np.repeat(off_seq, H), w_max=32, r=2,
+                          quantize=False)
+    assert np.max(np.abs(out["o"] - ref)) / np.max(np.abs(ref)) <= 1e-10
+    # every sequence closed at the steps its schedule says
+    closes = {}
+    for ev in out["state"].closes:
+        for h in ev.heads:
+            closes.setdefault(int(h), []).append(ev.step)
+    for h in range(N):
+        b = h // H
+        expect = [t for t in range(steps) if (off_seq[b] + t + 1) % W_seq[b] == 0]
+        assert closes.get(h, []) == expect
+
+
+@pytest.mark.parametrize("kda,bits", [(False, 8), (True, 8), (False, 4), (True, 4)])
+def test_dense_and_buffered_agree_with_quantisation(kda, bits):
+    rng = np.random.default_rng(21 + bits + kda)
+    N, dk, dv, steps, W = 4, 16, 16, 50, 16
+    S0 = planted_state(rng, N, dk, dv)
+    toks = random_tokens(rng, steps, N, dk, dv, kda=kda)
+    off = np.array([0, 5, 0, 5])
+    dense = lq.run_dense(S0, toks, np.full(N, W), off, r=2, bits=bits)
+    buf = lq.run_buffered(S0, toks, np.full(N, W), off, w_max=W, r=2, bits=bits, kda=kda)
+    assert _rel(buf["o"], dense["o"]) <= 1e-12
+    assert _rel(buf["u"], dense["u"]) <= 1e-12
+
+
+@pytest.mark.parametrize("smoothing", [True, False])
+def test_window_one_no_compensators_is_per_token_requantisation(smoothing):
+    rng = np.random.default_rng(33)
+    N, dk, dv, steps = 2, 6, 5, 12
+    S0 = planted_state(rng, N, dk, dv, rows=1, cols=1)
+    toks = random_tokens(rng, steps, N, dk, dv)
+    naive = lq.run_per_token(S0, toks, bits=8, smoothing=smoothing)
+    dense = lq.run_dense(S0, toks, np.ones(N), np.zeros(N), r=0, bits=8, smoothing=smoothing)
+    buf = lq.run_buffered(S0, toks, np.ones(N), np.zeros(N), w_max=1, r=0, bits=8, smoothing=smoothing)
+    assert _rel(dense["o"], naive["o"]) <= 1e-12
+    assert _rel(buf["o"], naive["o"]) <= 1e-12
+    assert _rel(dense["S"], naive["S"]) <= 1e-12
+
+
+def test_output_at_window_end_uses_unquantised_state():
+    """The token that ends a window is answered before the state is requantised."""
+    rng = np.random.default_rng(44)
+    N, dk, dv, W = 2, 8, 8, 4
+    S0 = planted_state(rng, N, dk, dv)
+    toks = random_tokens(rng, W + 1, N, dk, dv)
+    res = lq.run_dense(S0, toks, np.full(N, W), np.zeros(N), r=1, record=True)
+    S = lq.decode(res["enc0"])
+    for t in toks[:W]:
+        S, o, _ = lq.exact_step(S, t["q"], t["k"], t["v"], t["g"], t["beta"])
+    np.testing.assert_allclose(res["o"][W - 1], o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(res["closes"][0].folded, S, rtol=1e-13, atol=1e-14)
+
+
+def test_per_window_error_is_smaller_than_per_token():
+    """The pages' claim in kind: quantising once per window (with compensators
+    and smoothing) accumulates less error than requantising every token."""
+    rng = np.random.default_rng(0)
+    N, d, steps = 4, 32, 64
+    S0 = planted_state(rng, N, d, d)
+    toks = random_tokens(rng, steps, N, d, d)
+    ref, _ = _exact(S0.copy(), toks)
+    lqo = lq.run_dense(S0, toks, np.full(N, 16), np.zeros(N), r=2)
+    naive = lq.run_dense(S0, toks, np.ones(N), np.zeros(N), r=0, smoothing=False)
+    e_lq, e_naive = _rel(lqo["o"], ref), _rel(naive["o"], ref)
+    assert e_lq < 0.5 * e_naive, (e_lq, e_naive)
