@@ -125,7 +125,9 @@ def _nearest_code(x, Q):
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("smoothing", [True, False])
 def test_quantiser_brute_force_4x4(bits, smoothing):
-    Q = lq.QMAX[bits]
+    # symmetric b-bit codes: the largest magnitude a signed b-bit integer
+    # holds on both sides of zero
+    Q = 2 ** (bits - 1) - 1
     rng = np.random.default_rng(5 + bits)
     R = rng.standard_normal((20, 4, 4)) * rng.uniform(0.1, 10, (20, 4, 1))
     R[0, :, 1] = 0.0            # zero column
