@@ -1,0 +1,177 @@
+/*
+ * leapquant.h -- C ABI of the LeapQuant decode path for delta-rule linear
+ * attention (Gated DeltaNet with scalar decay, Kimi Delta Attention with
+ * per-key-channel decay) on AMD MI355X (gfx950).
+ *
+ * Method: "LeapQuant: Efficient Linear Attention with Accurate Recurrent State
+ * Quantization" (original abstract) and the wink.run article "Linear attention
+ * has to move state every token it generates; LeapQuant compresses it to 8-bit
+ * without losing accuracy" (paragraphs on per-window quantization, compensator
+ * tokens and residual smoothing). Recurrences: Gated Delta Networks (Yang et
+ * al., ICLR 2025) and Kimi Delta Attention (Kimi Linear report, 2025).
+ *
+ * Per (sequence b, head h) -- a "head" below -- the recurrent state
+ * S in R^{d_k x d_v} (row i = key channel, column j = value channel) is held as
+ *   S_hat_0 = sum_l comp_k[l] comp_u[l]^T + diag(s) C diag(c)
+ * (r fp32 rank-one compensators plus a symmetric int8/int4 residual C with
+ * per-key-row smoothing scales s and per-value-column scales c), fixed for a
+ * window, plus an fp32 buffer of the window's token updates (k_m, u_m, G_m),
+ * G_m = cumulative log-decay since the window start.
+ *
+ * Conventions for every entry point:
+ *  - Every pointer is a DEVICE pointer unless marked (host). The caller
+ *    allocates and frees all memory; the library allocates nothing and keeps
+ *    no mutable global state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued asynchronously; the library never synchronises.
+ *  - Arguments are validated on the host before anything is enqueued. A
+ *    rejected call returns a negative LQ_ERR_* code and enqueues nothing.
+ *    Launch failures return LQ_ERR_LAUNCH. Faults inside a kernel surface at
+ *    the caller's next synchronisation.
+ *  - batch * heads == 0 is a valid empty call: it returns LQ_OK and enqueues
+ *    nothing.
+ *  - Layouts are dense and row-major in the order written; "head index"
+ *    bh = b * heads + h. Every float buffer must be 16-byte aligned, codes
+ *    16-byte aligned (LQ_ERR_ALIGN otherwise).
+ *  - Supported shapes (build-time limit): d_k == d_v in {32, 64, 128}.
+ */
+#ifndef LEAPQUANT_H
+#define LEAPQUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define LQ_OK 0
+#define LQ_ERR_NULL (-1)   /* a required pointer is NULL */
+#define LQ_ERR_SHAPE (-2)  /* unsupported batch/heads/d_k/d_v */
+#define LQ_ERR_BITS (-3)   /* bits not 4 or 8 */
+#define LQ_ERR_CONFIG (-4) /* w_max, n_comp, power_iters, flags or close list out of range */
+#define LQ_ERR_LAUNCH (-5) /* the HIP launch failed */
+#define LQ_ERR_ALIGN (-6)  /* a buffer is not 16-byte aligned */
+
+/* activation dtypes for q, k, v */
+#define LQ_ACT_F32 0
+#define LQ_ACT_BF16 1
+
+/* bits of the device error word lq_state.err */
+#define LQ_DEVERR_BUFFER_FULL 1 /* decode_step met a head whose buffer held w_max entries */
+#define LQ_DEVERR_BAD_SEQ 2     /* window_close met a sequence id outside [0, batch) */
+#define LQ_DEVERR_BAD_LEN 4     /* a head's buf_len was outside [0, w_max]; the head was skipped */
+
+/* Problem shape and method parameters (host struct, passed by pointer). */
+typedef struct lq_dims {
+  int32_t batch;             /* B sequences, >= 0 */
+  int32_t heads;             /* H heads per sequence, >= 0 */
+  int32_t d_k, d_v;          /* key / value head dims; equal, in {32, 64, 128} */
+  int32_t w_max;             /* buffer capacity per head, 1..64 (>= every window length used) */
+  int32_t n_comp;            /* r compensators, 0..8 */
+  int32_t bits;              /* 8 or 4 */
+  int32_t decay_per_channel; /* 0: GDN, g is [B][H]; 1: KDA, g is [B][H][d_k] */
+  int32_t act_dtype;         /* LQ_ACT_F32 or LQ_ACT_BF16 for q, k, v */
+  int32_t smoothing;         /* 1: per-key-row smoothing scales; 0: s == 1 */
+  int32_t power_iters;       /* T power iterations per compensator, 1..64 */
+} lq_dims;
+
+/* The LeapQuant state of all B*H heads (device buffers owned by the caller). */
+typedef struct lq_state {
+  void* codes;       /* int8 [B*H][d_v][d_k] two's complement, or int4 packed
+                        [B*H][d_v][d_k/2] with key channel 2m in the low nibble
+                        and 2m+1 in the high nibble of byte m; codes in [-Q, Q],
+                        Q = 127 (int8) or 7 (int4) */
+  float* row_scale;  /* s [B*H][d_k] key-row smoothing scales */
+  float* col_scale;  /* c [B*H][d_v] value-column scales */
+  float* comp_k;     /* [B*H][r][d_k] unit compensator keys (may be NULL if r == 0) */
+  float* comp_u;     /* [B*H][r][d_v] compensator values (may be NULL if r == 0) */
+  float* buf_k;      /* [B*H][w_max][d_k] buffered keys of the current window */
+  float* buf_u;      /* [B*H][w_max][d_v] buffered deltas u_m */
+  float* buf_g;      /* [B*H][w_max] (GDN) or [B*H][w_max][d_k] (KDA): cumulative
+                        log-decay G_m since the window start */
+  int32_t* buf_len;  /* [B*H] entries buffered per head */
+  int32_t* err;      /* [1] device error word (LQ_DEVERR_* bits), may be NULL */
+} lq_state;
+
+/* Number of device buffers in lq_state whose sizes lq_state_sizes reports,
+   in the field order above: codes, row_scale, col_scale, comp_k, comp_u,
+   buf_k, buf_u, buf_g, buf_len, err. */
+#define LQ_STATE_NBUF 10
+
+/* Host-only helper: bytes needed for each lq_state buffer (err: 4 bytes).
+   bytes_out (host) receives LQ_STATE_NBUF sizes. Validates dims. */
+int lq_state_sizes(const lq_dims* dims, size_t* bytes_out);
+
+/* Encode fp32 dense states into LeapQuant form: compensator extraction by a
+   T-step power method with deflation (start vectors from SplitMix64), key-row
+   smoothing, symmetric quantisation with per-value-column scales; empties
+   every buffer (buf_len = 0). Same arithmetic as a window close on an empty
+   buffer. Sources: LeapQuant abstract (compensator tokens, smoothing) and the
+   wink.run article's compensator and smoothing paragraphs.
+   S: fp32 [B*H][d_v][d_k] (element (j, i) = S[i][j], i.e. S transposed).
+   dbg_residual: NULL, or fp32 [B*H][d_v][d_k] receiving the residual after
+   the compensators are removed and before smoothing/rounding. */
+int leapquant_encode(const lq_dims* dims, const float* S, const lq_state* st,
+                     float* dbg_residual, void* stream);
+
+/* One decode token for every head (per-window quantization: the low-bit state
+   stays fixed and the token's update is buffered in fp32). Per head, with
+   G_t = G_{t-1} + g_t (G_{t-1} from the last buffered entry, 0 if empty):
+     y^x = Shat_0^T (exp(G_t) (.) x) + sum_m u_m (k_m . (exp(G_t - G_m) (.) x)),
+     u_t = beta_t (v_t - y^k),  o_t = y^q + (k_t . q_t) u_t,
+   then appends (k_t, u_t, G_t) to the buffer and increments buf_len.
+   q, k: [B][H][d_k]; v: [B][H][d_v] (fp32 or bf16 per act_dtype);
+   g: fp32 [B][H] (GDN) or [B][H][d_k] (KDA), the log-decay (alpha = exp(g));
+   beta: fp32 [B][H]; o: fp32 [B][H][d_v] (output).
+   Precondition: every head has buf_len < w_max. A head with a full buffer is
+   left unchanged (its o is not written) and LQ_DEVERR_BUFFER_FULL is or-ed
+   into *st->err when err is not NULL. */
+int leapquant_decode_step(const lq_dims* dims, const lq_state* st, const void* q, const void* k,
+                          const void* v, const float* g, const float* beta, float* o,
+                          void* stream);
+
+/* Window close for a list of sequences (all heads of each): fold the buffer
+   into the dense state S = exp(G_n) (.) Shat_0 + sum_m exp(G_n - G_m) (.) k_m u_m^T,
+   re-extract the compensators, re-smooth, requantise, and empty the buffer.
+   A partly filled buffer is legal (a partial window). Sources: LeapQuant
+   abstract (quantize once at the window end; compensators and smoothing).
+   seq_ids: int32 [n_seq] distinct sequence ids in [0, B), or NULL for all B
+   sequences (n_seq is then ignored). An id outside [0, B) is skipped and
+   LQ_DEVERR_BAD_SEQ is or-ed into *st->err. Duplicated ids race.
+   dbg_residual: NULL or fp32 [B*H][d_v][d_k]; rows of closed sequences get
+   the pre-quantisation residual. */
+int leapquant_window_close(const lq_dims* dims, const lq_state* st, const int32_t* seq_ids,
+                           int32_t n_seq, float* dbg_residual, void* stream);
+
+/* FP32-state baseline: one exact decode token of the gated delta rule with the
+   state kept in fp32 (no quantisation), decay first:
+     S' = alpha (.)_rows S,  u = beta (v - S'^T k),  S = S' + k u^T,  o = S^T q.
+   S: fp32 [B*H][d_v][d_k] (transposed, in/out). Other arguments as
+   leapquant_decode_step. Only batch, heads, d_k, d_v, decay_per_channel and
+   act_dtype of dims are used. */
+int gdn_decode_fp32_baseline(const lq_dims* dims, float* S, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, float* o,
+                             void* stream);
+
+/* Dense window-start state Shat_0 = sum_l comp_k comp_u^T + diag(s) C diag(c)
+   of every head into S_out: fp32 [B*H][d_v][d_k] (transposed). Test helper. */
+int leapquant_dequantize(const lq_dims* dims, const lq_state* st, float* S_out, void* stream);
+
+/* Host-only: sequences whose window ends with decode token `step` (0-based),
+   i.e. (win_off[b] + step + 1) % win_len[b] == 0, written in increasing order
+   to out_ids (host, capacity batch). win_len (host) [batch] window lengths
+   >= 1; win_off (host) [batch] start positions inside the first window, in
+   [0, win_len[b]). Returns the count, or a negative LQ_ERR_* code. */
+int32_t lq_close_list(const int32_t* win_len, const int32_t* win_off, int32_t batch, int64_t step,
+                      int32_t* out_ids);
+
+/* Host-only: static text for a status code. */
+const char* lq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LEAPQUANT_H */

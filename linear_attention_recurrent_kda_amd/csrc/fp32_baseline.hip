@@ -1,0 +1,154 @@
+// FP32-state decode baseline and the dense dequantiser (gfx950).
+//
+// The baseline is one exact token of the gated delta rule (Gated DeltaNet,
+// Yang et al.; per-channel decay as in Kimi Delta Attention) with the state
+// kept in fp32, the format the LeapQuant pages compare against: per head it
+// reads and writes the whole d_k x d_v state once.
+//
+// Layout [d_v][d_k] (the state transposed): value column j is d_k contiguous
+// floats, so each column's update is independent:
+//   u_j = beta (v_j - sum_i alpha_i S_ij k_i),
+//   S_ij <- alpha_i S_ij + k_i u_j,   o_j = sum_i S_ij q_i.
+// One workgroup of 2*D threads per head; D/16 lanes share a column, each lane
+// owns 16 key channels (64 bytes, four 16-byte loads).
+#include "lq_common.h"
+#include "lq_launch.h"
+
+namespace lq {
+
+namespace {
+
+template <int D, bool KDA, bool BF16>
+__global__ void __launch_bounds__(2 * D) baseline_kernel(BaselineArgs a) {
+  constexpr int NT = 2 * D;
+  constexpr int LPC = D / 16;
+  constexpr int NG = NT / LPC;
+  constexpr int CPT = D / NG;
+  __shared__ __align__(16) float s_k[D];
+  __shared__ __align__(16) float s_q[D];
+  __shared__ __align__(16) float s_al[KDA ? D : 4];
+
+  const int bh = blockIdx.x, t = threadIdx.x;
+  const int grp = t / LPC, li = t % LPC, i0 = li * 16;
+  const size_t hD = size_t(bh) * D;
+  float* Sh = a.S + hD * D;
+
+  float S[CPT][16];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) load16(Sh + size_t(grp + NG * c) * D + i0, S[c]);
+  float vj[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) vj[c] = load_act<BF16>(a.v, hD + grp + NG * c);
+  const float beta = a.beta[bh];
+  float alpha = 1.f;
+  if constexpr (!KDA) alpha = expf(a.g[bh]);
+  if (t < D) {
+    s_k[t] = load_act<BF16>(a.k, hD + t);
+    s_q[t] = load_act<BF16>(a.q, hD + t);
+    if constexpr (KDA) s_al[t] = expf(a.g[hD + t]);
+  }
+  __syncthreads();
+
+  float kk[16], qq[16], al[16];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float4 k4 = reinterpret_cast<const float4*>(&s_k[i0])[w];
+    const float4 q4 = reinterpret_cast<const float4*>(&s_q[i0])[w];
+    kk[4 * w] = k4.x, kk[4 * w + 1] = k4.y, kk[4 * w + 2] = k4.z, kk[4 * w + 3] = k4.w;
+    qq[4 * w] = q4.x, qq[4 * w + 1] = q4.y, qq[4 * w + 2] = q4.z, qq[4 * w + 3] = q4.w;
+    if constexpr (KDA) {
+      const float4 a4 = reinterpret_cast<const float4*>(&s_al[i0])[w];
+      al[4 * w] = a4.x, al[4 * w + 1] = a4.y, al[4 * w + 2] = a4.z, al[4 * w + 3] = a4.w;
+    } else {
+      al[4 * w] = al[4 * w + 1] = al[4 * w + 2] = al[4 * w + 3] = alpha;
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    float dk = 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      S[c][x] *= al[x];
+      dk = fmaf(S[c][x], kk[x], dk);
+    }
+    dk = group_sum<LPC>(dk);
+    const float u = beta * (vj[c] - dk);
+    float dq = 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      S[c][x] = fmaf(kk[x], u, S[c][x]);
+      dq = fmaf(S[c][x], qq[x], dq);
+    }
+    dq = group_sum<LPC>(dq);
+    store16(Sh + size_t(grp + NG * c) * D + i0, S[c]);
+    if (li == 0) a.o[hD + grp + NG * c] = dq;
+  }
+}
+
+// Shat_0 = sum_l comp_k[l] comp_u[l]^T + diag(s) C diag(c), written [d_v][d_k].
+template <int D, int BITS>
+__global__ void __launch_bounds__(256) dequant_kernel(lq_state st, int r, float* out) {
+  const int bh = blockIdx.x;
+  const size_t hD = size_t(bh) * D;
+  for (int idx = threadIdx.x; idx < D * D; idx += 256) {
+    const int j = idx / D, i = idx % D;
+    int code;
+    if constexpr (BITS == 8) {
+      code = static_cast<const int8_t*>(st.codes)[(hD + j) * D + i];
+    } else {
+      const uint8_t byte = static_cast<const uint8_t*>(st.codes)[(hD + j) * (D / 2) + i / 2];
+      const uint32_t nib = (i & 1) ? (byte >> 4) : (byte & 0xFu);
+      code = int(nib ^ 0x8u) - 8;
+    }
+    float val = (st.row_scale[hD + i] * float(code)) * st.col_scale[hD + j];
+    for (int l = 0; l < r; ++l)
+      val = fmaf(st.comp_k[(size_t(bh) * r + l) * D + i], st.comp_u[(size_t(bh) * r + l) * D + j], val);
+    out[(hD + j) * D + i] = val;
+  }
+}
+
+template <int D, bool KDA, bool BF16>
+hipError_t launch(const lq_dims& d, const BaselineArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((baseline_kernel<D, KDA, BF16>), dim3(d.batch * d.heads), dim3(2 * D), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const lq_dims& d, const BaselineArgs& a, hipStream_t s) {
+  const bool kda = d.decay_per_channel != 0, bf16 = d.act_dtype == LQ_ACT_BF16;
+  if (kda) return bf16 ? launch<D, true, true>(d, a, s) : launch<D, true, false>(d, a, s);
+  return bf16 ? launch<D, false, true>(d, a, s) : launch<D, false, false>(d, a, s);
+}
+
+template <int D, int BITS>
+hipError_t launch_dq(const lq_dims& d, const lq_state& st, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL((dequant_kernel<D, BITS>), dim3(d.batch * d.heads), dim3(256), 0, stream, st,
+                     d.n_comp, out);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_d(const lq_dims& d, const lq_state& st, float* out, hipStream_t s) {
+  return d.bits == 8 ? launch_dq<D, 8>(d, st, out, s) : launch_dq<D, 4>(d, st, out, s);
+}
+
+}  // namespace
+
+hipError_t launch_baseline(const lq_dims& d, const BaselineArgs& a, hipStream_t stream) {
+  switch (d.d_k) {
+    case 32: return launch_d<32>(d, a, stream);
+    case 64: return launch_d<64>(d, a, stream);
+    default: return launch_d<128>(d, a, stream);
+  }
+}
+
+hipError_t launch_dequantize(const lq_dims& d, const lq_state& st, float* out, hipStream_t stream) {
+  switch (d.d_k) {
+    case 32: return launch_dq_d<32>(d, st, out, stream);
+    case 64: return launch_dq_d<64>(d, st, out, stream);
+    default: return launch_dq_d<128>(d, st, out, stream);
+  }
+}
+
+}  // namespace lq

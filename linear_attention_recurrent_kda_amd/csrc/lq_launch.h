@@ -1,0 +1,71 @@
+// Host-side kernel launchers (internal). Arguments are already validated by
+// the C ABI layer; each launcher enqueues on `stream` and returns hipError_t
+// of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "leapquant.h"
+
+namespace lq {
+
+// Kernel-side view of the state plus the per-call activations.
+struct StepArgs {
+  const void* codes;
+  const float* s;
+  const float* c;
+  const float* ck;
+  const float* cu;
+  float* bk;
+  float* bu;
+  float* bg;
+  int32_t* blen;
+  int32_t* err;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  float* o;
+  int r;
+  int w_max;
+};
+
+struct CloseArgs {
+  const float* S;          // dense input (encode) or NULL (close)
+  void* codes;
+  float* s;
+  float* c;
+  float* ck;
+  float* cu;
+  const float* bk;
+  const float* bu;
+  const float* bg;
+  int32_t* blen;
+  int32_t* err;
+  const int32_t* seq_ids;  // NULL: all sequences
+  float* dbg;              // NULL or residual output
+  int batch;
+  int heads;
+  int r;
+  int w_max;
+  int T;
+  int smoothing;
+};
+
+struct BaselineArgs {
+  float* S;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  float* o;
+};
+
+hipError_t launch_decode_step(const lq_dims& d, const StepArgs& a, hipStream_t stream);
+hipError_t launch_close(const lq_dims& d, const CloseArgs& a, int n_blocks, hipStream_t stream);
+hipError_t launch_baseline(const lq_dims& d, const BaselineArgs& a, hipStream_t stream);
+hipError_t launch_dequantize(const lq_dims& d, const lq_state& st, float* out, hipStream_t stream);
+
+}  // namespace lq

@@ -1,0 +1,368 @@
+// LeapQuant window close and initial encode on gfx950.
+//
+// At a window boundary (LeapQuant abstract: quantize once at the window end)
+// the buffered token updates are folded into the dense state, the largest
+// outliers are re-extracted as r rank-one compensator tokens (abstract and
+// wink.run article, compensator tokens; here a T-step power method with
+// deflation from fixed SplitMix64 start vectors), the remaining residual is
+// balanced per key row (article, residual smoothing) and requantised to
+// symmetric int8/int4 with per-value-column scales.
+//
+// One workgroup of 256 threads per head. The d_k x d_v fp32 state lives in
+// registers: the 16 x 16 thread grid gives thread (ti, tj) the block of key
+// rows [ti*B, ti*B+B) and value columns [tj*B, tj*B+B), B = D/16. A 16-lane
+// DPP row holds one block row (all tj), so sums over value columns are DPP
+// reductions; sums over key rows combine the four rows of a wave with the
+// gfx950 row-swap instructions and the four waves through LDS. Reductions
+// run in a fixed order, so the result is deterministic.
+#include "lq_common.h"
+#include "lq_launch.h"
+
+namespace lq {
+
+namespace {
+
+template <int B>
+__device__ __forceinline__ void loadB(const float* p, float (&x)[B]) {
+  if constexpr (B % 4 == 0) {
+#pragma unroll
+    for (int w = 0; w < B / 4; ++w) {
+      const float4 t = reinterpret_cast<const float4*>(p)[w];
+      x[4 * w] = t.x;
+      x[4 * w + 1] = t.y;
+      x[4 * w + 2] = t.z;
+      x[4 * w + 3] = t.w;
+    }
+  } else {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    x[0] = t.x;
+    x[1] = t.y;
+  }
+}
+
+template <int B>
+__device__ __forceinline__ void storeB(float* p, const float (&x)[B]) {
+  if constexpr (B % 4 == 0) {
+#pragma unroll
+    for (int w = 0; w < B / 4; ++w)
+      reinterpret_cast<float4*>(p)[w] = make_float4(x[4 * w], x[4 * w + 1], x[4 * w + 2], x[4 * w + 3]);
+  } else {
+    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+  }
+}
+
+// B codes of one value column (key channels i0..i0+B-1) -> signed ints
+template <int B, int BITS>
+__device__ __forceinline__ void load_codes(const uint8_t* p, int (&c)[B]) {
+  if constexpr (BITS == 8) {
+    uint64_t w = 0;
+    if constexpr (B == 8) w = *reinterpret_cast<const uint64_t*>(p);
+    else if constexpr (B == 4) w = *reinterpret_cast<const uint32_t*>(p);
+    else w = *reinterpret_cast<const uint16_t*>(p);
+#pragma unroll
+    for (int a = 0; a < B; ++a) c[a] = int(int8_t(uint8_t(w >> (8 * a))));
+  } else {
+    uint32_t w = 0;
+    if constexpr (B == 8) w = *reinterpret_cast<const uint32_t*>(p);
+    else if constexpr (B == 4) w = *reinterpret_cast<const uint16_t*>(p);
+    else w = *p;
+#pragma unroll
+    for (int a = 0; a < B; ++a) c[a] = int(((w >> (4 * a)) & 0xFu) ^ 0x8u) - 8;
+  }
+}
+
+template <int B, int BITS>
+__device__ __forceinline__ void store_codes(uint8_t* p, const int (&c)[B]) {
+  if constexpr (BITS == 8) {
+    uint64_t w = 0;
+#pragma unroll
+    for (int a = 0; a < B; ++a) w |= uint64_t(uint8_t(c[a])) << (8 * a);
+    if constexpr (B == 8) *reinterpret_cast<uint64_t*>(p) = w;
+    else if constexpr (B == 4) *reinterpret_cast<uint32_t*>(p) = uint32_t(w);
+    else *reinterpret_cast<uint16_t*>(p) = uint16_t(w);
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int a = 0; a < B; ++a) w |= (uint32_t(c[a]) & 0xFu) << (4 * a);
+    if constexpr (B == 8) *reinterpret_cast<uint32_t*>(p) = w;
+    else if constexpr (B == 4) *reinterpret_cast<uint16_t*>(p) = uint16_t(w);
+    else *p = uint8_t(w);
+  }
+}
+
+template <int D, int BITS, bool KDA, bool DENSE>
+__global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
+  constexpr int B = D / 16;
+  constexpr int Q = BITS == 8 ? 127 : 7;
+  constexpr int CB = D * BITS / 8;  // code bytes per value column
+  __shared__ float sh_n[16];
+  __shared__ float sh_c[4][D];
+
+  const int t = threadIdx.x, tj = t & 15, ti = t >> 4, lane = t & 63, wave = t >> 6;
+  const int H = a.heads;
+  int b = blockIdx.x / H;
+  const int h = blockIdx.x % H;
+  if (a.seq_ids) {
+    b = a.seq_ids[b];
+    if (b < 0 || b >= a.batch) {
+      if (t == 0 && a.err) atomicOr(a.err, LQ_DEVERR_BAD_SEQ);
+      return;
+    }
+  }
+  const int bh = b * H + h;
+  const size_t hD = size_t(bh) * D;
+  const int i0 = ti * B, j0 = tj * B;
+  const int r = a.r;
+
+  // ---- the dense state block M[a][bb] = S[i0 + a][j0 + bb]
+  float M[B][B];
+  if constexpr (DENSE) {
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) {
+      float col[B];
+      loadB<B>(a.S + (hD + j0 + bb) * D + i0, col);
+#pragma unroll
+      for (int x = 0; x < B; ++x) M[x][bb] = col[x];
+    }
+  } else {
+    // fold: S = exp(G_n) (.) Shat_0 + sum_m exp(G_n - G_m) (.) k_m u_m^T
+    const int n = a.blen[bh];
+    if (n < 0 || n > a.w_max) {  // corrupted buffer length: leave the head untouched
+      if (t == 0 && a.err) atomicOr(a.err, LQ_DEVERR_BAD_LEN);
+      return;
+    }
+    const size_t brow = size_t(bh) * a.w_max;
+    float si[B], cj[B];
+    loadB<B>(a.s + hD + i0, si);
+    loadB<B>(a.c + hD + j0, cj);
+    const uint8_t* cb = static_cast<const uint8_t*>(a.codes) + hD * CB + i0 * BITS / 8;
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) {
+      int code[B];
+      load_codes<B, BITS>(cb + size_t(j0 + bb) * CB, code);
+#pragma unroll
+      for (int x = 0; x < B; ++x) M[x][bb] = (si[x] * float(code[x])) * cj[bb];
+    }
+    for (int l = 0; l < r; ++l) {
+      float kh[B], uh[B];
+      loadB<B>(a.ck + (size_t(bh) * r + l) * D + i0, kh);
+      loadB<B>(a.cu + (size_t(bh) * r + l) * D + j0, uh);
+#pragma unroll
+      for (int x = 0; x < B; ++x)
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb) M[x][bb] = fmaf(kh[x], uh[bb], M[x][bb]);
+    }
+    if constexpr (KDA) {
+      float Gn[B];
+      if (n > 0) loadB<B>(a.bg + (brow + n - 1) * D + i0, Gn);
+      else
+#pragma unroll
+        for (int x = 0; x < B; ++x) Gn[x] = 0.f;
+#pragma unroll
+      for (int x = 0; x < B; ++x) {
+        const float e = expf(Gn[x]);
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb) M[x][bb] *= e;
+      }
+      for (int m = 0; m < n; ++m) {
+        float km[B], um[B], gm[B];
+        loadB<B>(a.bk + (brow + m) * D + i0, km);
+        loadB<B>(a.bu + (brow + m) * D + j0, um);
+        loadB<B>(a.bg + (brow + m) * D + i0, gm);
+#pragma unroll
+        for (int x = 0; x < B; ++x) {
+          const float kf = expf(Gn[x] - gm[x]) * km[x];
+#pragma unroll
+          for (int bb = 0; bb < B; ++bb) M[x][bb] = fmaf(kf, um[bb], M[x][bb]);
+        }
+      }
+    } else {
+      const float Gn = n > 0 ? a.bg[brow + n - 1] : 0.f;
+      const float e = expf(Gn);
+#pragma unroll
+      for (int x = 0; x < B; ++x)
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb) M[x][bb] *= e;
+      for (int m = 0; m < n; ++m) {
+        float km[B], um[B];
+        loadB<B>(a.bk + (brow + m) * D + i0, km);
+        loadB<B>(a.bu + (brow + m) * D + j0, um);
+        const float f = expf(Gn - a.bg[brow + m]);
+#pragma unroll
+        for (int x = 0; x < B; ++x) {
+          const float kf = f * km[x];
+#pragma unroll
+          for (int bb = 0; bb < B; ++bb) M[x][bb] = fmaf(kf, um[bb], M[x][bb]);
+        }
+      }
+    }
+  }
+
+  // ---- compensators: power method with deflation
+  bool live = true;
+  for (int l = 0; l < r; ++l) {
+    float kk[B], w[B], v[B];
+#pragma unroll
+    for (int x = 0; x < B; ++x) kk[x] = w[x] = 0.f;
+    if (live) {
+      float p = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) {
+        v[bb] = start_vec(l, j0 + bb, D);
+        p = fmaf(v[bb], v[bb], p);
+      }
+      p = group_sum<16>(p);
+      const float nv = sqrtf(p);
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) v[bb] = v[bb] / nv;
+      for (int it = 0; it < a.T; ++it) {
+        // kappa = M v  (sum over value columns: DPP across the 16 tj lanes)
+        float kap[B];
+        float pk = 0.f;
+#pragma unroll
+        for (int x = 0; x < B; ++x) {
+          float s = 0.f;
+#pragma unroll
+          for (int bb = 0; bb < B; ++bb) s = fmaf(M[x][bb], v[bb], s);
+          kap[x] = group_sum<16>(s);
+          pk = fmaf(kap[x], kap[x], pk);
+        }
+        if (tj == 0) sh_n[ti] = pk;
+        __syncthreads();
+        float nk2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) nk2 += sh_n[q];
+        if (!(nk2 > 0.f) || !isfinite(nk2)) {  // uniform: every thread read the same sums
+          live = false;
+          break;
+        }
+        const float rk = sqrtf(nk2);
+#pragma unroll
+        for (int x = 0; x < B; ++x) kk[x] = kap[x] / rk;
+        // w = M^T k  (sum over key rows: wave rows, then waves through LDS)
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb) {
+          float s = 0.f;
+#pragma unroll
+          for (int x = 0; x < B; ++x) s = fmaf(M[x][bb], kk[x], s);
+          s = rows_sum(s);
+          if (lane < 16) sh_c[wave][j0 + bb] = s;
+        }
+        __syncthreads();
+        float pw = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb) {
+          const int j = j0 + bb;
+          w[bb] = (sh_c[0][j] + sh_c[1][j]) + (sh_c[2][j] + sh_c[3][j]);
+          pw = fmaf(w[bb], w[bb], pw);
+        }
+        pw = group_sum<16>(pw);
+        if (!(pw > 0.f) || !isfinite(pw)) {
+          live = false;
+          break;
+        }
+        const float rw = sqrtf(pw);
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb) v[bb] = w[bb] / rw;
+      }
+    }
+    __syncthreads();  // sh_n / sh_c are reused after a degenerate early exit
+    if (!live) {
+#pragma unroll
+      for (int x = 0; x < B; ++x) kk[x] = w[x] = 0.f;
+    }
+    if (tj == 0) storeB<B>(a.ck + (size_t(bh) * r + l) * D + i0, kk);
+    if (ti == 0) storeB<B>(a.cu + (size_t(bh) * r + l) * D + j0, w);
+#pragma unroll
+    for (int x = 0; x < B; ++x)
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) M[x][bb] = fmaf(-kk[x], w[bb], M[x][bb]);
+  }
+
+  if (a.dbg) {
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) {
+      float col[B];
+#pragma unroll
+      for (int x = 0; x < B; ++x) col[x] = M[x][bb];
+      storeB<B>(a.dbg + (hD + j0 + bb) * D + i0, col);
+    }
+  }
+
+  // ---- key-row smoothing scales
+  float sa[B];
+#pragma unroll
+  for (int x = 0; x < B; ++x) {
+    float m = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) m = fmaxf(m, fabsf(M[x][bb]));
+    m = group_max<16>(m);
+    sa[x] = (a.smoothing && m > 0.f) ? m : 1.f;
+  }
+#pragma unroll
+  for (int x = 0; x < B; ++x)
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) M[x][bb] = M[x][bb] / sa[x];
+
+  // ---- value-column scales and codes
+#pragma unroll
+  for (int bb = 0; bb < B; ++bb) {
+    float m = 0.f;
+#pragma unroll
+    for (int x = 0; x < B; ++x) m = fmaxf(m, fabsf(M[x][bb]));
+    m = rows_max(m);
+    if (lane < 16) sh_c[wave][j0 + bb] = m;
+  }
+  __syncthreads();
+  float cs[B], inv[B];
+#pragma unroll
+  for (int bb = 0; bb < B; ++bb) {
+    const int j = j0 + bb;
+    const float m = fmaxf(fmaxf(sh_c[0][j], sh_c[1][j]), fmaxf(sh_c[2][j], sh_c[3][j]));
+    cs[bb] = m / float(Q);
+    inv[bb] = m > 0.f ? float(Q) / m : 0.f;
+  }
+  uint8_t* cb = static_cast<uint8_t*>(a.codes) + hD * CB + i0 * BITS / 8;
+#pragma unroll
+  for (int bb = 0; bb < B; ++bb) {
+    int code[B];
+#pragma unroll
+    for (int x = 0; x < B; ++x) {
+      const float qv = fminf(fmaxf(rintf(M[x][bb] * inv[bb]), -float(Q)), float(Q));
+      code[x] = int(qv);
+    }
+    store_codes<B, BITS>(cb + size_t(j0 + bb) * CB, code);
+  }
+  if (tj == 0) storeB<B>(a.s + hD + i0, sa);
+  if (ti == 0) storeB<B>(a.c + hD + j0, cs);
+  if (t == 0) a.blen[bh] = 0;
+}
+
+template <int D, int BITS, bool KDA, bool DENSE>
+hipError_t launch(const CloseArgs& a, int n_blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((close_kernel<D, BITS, KDA, DENSE>), dim3(n_blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int BITS>
+hipError_t launch_b(const lq_dims& d, const CloseArgs& a, int nb, hipStream_t s) {
+  if (a.S) return launch<D, BITS, false, true>(a, nb, s);
+  return d.decay_per_channel ? launch<D, BITS, true, false>(a, nb, s) : launch<D, BITS, false, false>(a, nb, s);
+}
+
+template <int D>
+hipError_t launch_d(const lq_dims& d, const CloseArgs& a, int nb, hipStream_t s) {
+  return d.bits == 8 ? launch_b<D, 8>(d, a, nb, s) : launch_b<D, 4>(d, a, nb, s);
+}
+
+}  // namespace
+
+hipError_t launch_close(const lq_dims& d, const CloseArgs& a, int n_blocks, hipStream_t stream) {
+  switch (d.d_k) {
+    case 32: return launch_d<32>(d, a, n_blocks, stream);
+    case 64: return launch_d<64>(d, a, n_blocks, stream);
+    default: return launch_d<128>(d, a, n_blocks, stream);
+  }
+}
+
+}  // namespace lq

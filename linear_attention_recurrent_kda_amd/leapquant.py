@@ -1,0 +1,202 @@
+"""Python binding of the LeapQuant C ABI (include/leapquant.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libleapquant.so. PyTorch supplies device memory and the stream;
+each call is enqueued on torch's current stream. Importing this module fails
+loudly when the HIP library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libleapquant.so")
+
+LQ_OK = 0
+LQ_ERR_NULL, LQ_ERR_SHAPE, LQ_ERR_BITS, LQ_ERR_CONFIG, LQ_ERR_LAUNCH, LQ_ERR_ALIGN = -1, -2, -3, -4, -5, -6
+LQ_ACT_F32, LQ_ACT_BF16 = 0, 1
+LQ_DEVERR_BUFFER_FULL, LQ_DEVERR_BAD_SEQ, LQ_DEVERR_BAD_LEN = 1, 2, 4
+LQ_STATE_NBUF = 10
+STATE_FIELDS = ("codes", "row_scale", "col_scale", "comp_k", "comp_u", "buf_k", "buf_u", "buf_g",
+                "buf_len", "err")
+
+EXPORTS = ("lq_state_sizes", "leapquant_encode", "leapquant_decode_step", "leapquant_window_close",
+           "gdn_decode_fp32_baseline", "leapquant_dequantize", "lq_close_list", "lq_status_string")
+
+
+class CDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "heads", "d_k", "d_v", "w_max", "n_comp", "bits", "decay_per_channel", "act_dtype",
+        "smoothing", "power_iters")]
+
+
+class CState(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in STATE_FIELDS]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"LeapQuant HIP library not built: {path} is missing "
+                          "(run python -m linear_attention_recurrent_kda_amd.build)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pd, ps = ctypes.POINTER(CDims), ctypes.POINTER(CState)
+    sig = {
+        "lq_state_sizes": (ctypes.c_int, [pd, ctypes.POINTER(SZ)]),
+        "leapquant_encode": (ctypes.c_int, [pd, P, ps, P, P]),
+        "leapquant_decode_step": (ctypes.c_int, [pd, ps, P, P, P, P, P, P, P]),
+        "leapquant_window_close": (ctypes.c_int, [pd, ps, P, I32, P, P]),
+        "gdn_decode_fp32_baseline": (ctypes.c_int, [pd, P, P, P, P, P, P, P, P]),
+        "leapquant_dequantize": (ctypes.c_int, [pd, ps, P, P]),
+        "lq_close_list": (I32, [P, P, I32, I64, P]),
+        "lq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = load_library()
+
+
+class LeapQuantError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return _lib.lq_status_string(int(status)).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != LQ_OK:
+        raise LeapQuantError(fn, rc)
+
+
+@dataclass(frozen=True)
+class Dims:
+    """Problem shape and method parameters (mirrors lq_dims)."""
+
+    batch: int
+    heads: int
+    d: int
+    w_max: int = 16
+    n_comp: int = 4
+    bits: int = 8
+    kda: bool = False
+    bf16: bool = False
+    smoothing: bool = True
+    power_iters: int = 4
+
+    def c(self) -> CDims:
+        return CDims(self.batch, self.heads, self.d, self.d, self.w_max, self.n_comp, self.bits,
+                     int(self.kda), LQ_ACT_BF16 if self.bf16 else LQ_ACT_F32, int(self.smoothing),
+                     self.power_iters)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def state_sizes(dims: Dims) -> Dict[str, int]:
+    out = (ctypes.c_size_t * LQ_STATE_NBUF)()
+    cd = dims.c()
+    _check("lq_state_sizes", _lib.lq_state_sizes(ctypes.byref(cd), out))
+    return dict(zip(STATE_FIELDS, (int(x) for x in out)))
+
+
+def close_list(win_len, win_off, step: int):
+    """Host schedule: sequences whose window ends with token `step`."""
+    import numpy as np
+    wl = np.ascontiguousarray(win_len, np.int32)
+    wo = np.ascontiguousarray(win_off, np.int32)
+    out = np.empty(max(len(wl), 1), np.int32)
+    n = _lib.lq_close_list(wl.ctypes.data, wo.ctypes.data, len(wl), int(step), out.ctypes.data)
+    if n < 0:
+        raise LeapQuantError("lq_close_list", n)
+    return out[:n].copy()
+
+
+class State:
+    """Device buffers of a LeapQuant state (all heads), allocated with torch."""
+
+    def __init__(self, dims: Dims, device="cuda"):
+        self.dims = dims
+        sz = state_sizes(dims)
+        BH, D, W, r = dims.batch * dims.heads, dims.d, dims.w_max, dims.n_comp
+        f32 = dict(dtype=torch.float32, device=device)
+        self.codes = torch.zeros((BH, D, D * dims.bits // 8), dtype=torch.int8, device=device)
+        self.row_scale = torch.ones((BH, D), **f32)
+        self.col_scale = torch.zeros((BH, D), **f32)
+        self.comp_k = torch.zeros((BH, max(r, 0), D), **f32)
+        self.comp_u = torch.zeros((BH, max(r, 0), D), **f32)
+        self.buf_k = torch.zeros((BH, W, D), **f32)
+        self.buf_u = torch.zeros((BH, W, D), **f32)
+        self.buf_g = torch.zeros((BH, W, D) if dims.kda else (BH, W), **f32)
+        self.buf_len = torch.zeros((BH,), dtype=torch.int32, device=device)
+        self.err = torch.zeros((1,), dtype=torch.int32, device=device)
+        for name in STATE_FIELDS:
+            t = getattr(self, name)
+            assert t.numel() * t.element_size() == sz[name], (name, t.shape, sz[name])
+
+    def c(self) -> CState:
+        return CState(*[_ptr(getattr(self, n)) for n in STATE_FIELDS])
+
+    def nbytes(self) -> int:
+        return sum(getattr(self, n).numel() * getattr(self, n).element_size() for n in STATE_FIELDS)
+
+
+def encode(dims: Dims, S: torch.Tensor, st: State, dbg_residual: Optional[torch.Tensor] = None) -> None:
+    """S: fp32 [B*H][d_v][d_k] (transposed dense states)."""
+    cd, cs = dims.c(), st.c()
+    _check("leapquant_encode", _lib.leapquant_encode(ctypes.byref(cd), _ptr(S), ctypes.byref(cs),
+                                                     _ptr(dbg_residual), _stream()))
+
+
+def decode_step(dims: Dims, st: State, q, k, v, g, beta, o) -> None:
+    cd, cs = dims.c(), st.c()
+    _check("leapquant_decode_step", _lib.leapquant_decode_step(
+        ctypes.byref(cd), ctypes.byref(cs), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
+        _stream()))
+
+
+def window_close(dims: Dims, st: State, seq_ids: Optional[torch.Tensor] = None, n_seq: int = 0,
+                 dbg_residual: Optional[torch.Tensor] = None) -> None:
+    """seq_ids: device int32 tensor of sequence ids, or None for every sequence."""
+    cd, cs = dims.c(), st.c()
+    if seq_ids is not None and n_seq == 0:
+        n_seq = seq_ids.numel()
+    _check("leapquant_window_close", _lib.leapquant_window_close(
+        ctypes.byref(cd), ctypes.byref(cs), _ptr(seq_ids), int(n_seq), _ptr(dbg_residual), _stream()))
+
+
+def fp32_baseline_step(dims: Dims, S: torch.Tensor, q, k, v, g, beta, o) -> None:
+    cd = dims.c()
+    _check("gdn_decode_fp32_baseline", _lib.gdn_decode_fp32_baseline(
+        ctypes.byref(cd), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o), _stream()))
+
+
+def dequantize(dims: Dims, st: State, out: torch.Tensor) -> None:
+    cd, cs = dims.c(), st.c()
+    _check("leapquant_dequantize", _lib.leapquant_dequantize(ctypes.byref(cd), ctypes.byref(cs),
+                                                             _ptr(out), _stream()))
+
+
+def raw_call(name: str, *args) -> int:
+    """Call an exported entry point with ctypes arguments; returns its status (tests)."""
+    return getattr(_lib, name)(*args)

@@ -1,0 +1,93 @@
+"""Host-side decode loop over the C ABI: window schedule, close lists, uploads.
+
+A Decoder owns one LeapQuant state (all B*H heads) and advances it one token
+at a time: decode_step for every head, then window_close for the sequences
+whose window ends with that token. Window ends are known on the host in
+advance ((offset + t + 1) % W == 0 per sequence), so the close lists for one
+schedule period are computed once and kept on the device; no step needs a
+device-to-host read.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import leapquant as lqk
+from .workloads import Workload, window_lengths, window_offsets
+
+
+def dims_for(wl: Workload, bits: Optional[int] = None) -> lqk.Dims:
+    return lqk.Dims(batch=wl.batch, heads=wl.heads, d=wl.d_k, w_max=wl.w_max, n_comp=wl.n_comp,
+                    bits=wl.bits if bits is None else bits, kda=wl.kda, bf16=wl.act_bf16,
+                    smoothing=wl.smoothing, power_iters=wl.power_iters)
+
+
+def upload_tokens(tok: Dict[str, np.ndarray], bf16: bool, device="cuda") -> Dict[str, torch.Tensor]:
+    """Token inputs [n][S][H][...] from the workload stream -> contiguous device tensors with a
+    leading step axis (the kernels read [B][H][d] per step)."""
+    out = {}
+    for name in ("q", "k", "v"):
+        if bf16:
+            arr = np.ascontiguousarray(tok[name + "16"]).view(np.int16)
+            out[name] = torch.from_numpy(arr).to(device).view(torch.bfloat16)
+        else:
+            out[name] = torch.from_numpy(np.ascontiguousarray(tok[name])).to(device)
+    out["g"] = torch.from_numpy(np.ascontiguousarray(tok["g"])).to(device)
+    out["beta"] = torch.from_numpy(np.ascontiguousarray(tok["beta"])).to(device)
+    return out
+
+
+def states_to_device(S_math: np.ndarray, device="cuda") -> torch.Tensor:
+    """Math-layout fp32 states [..][d_k][d_v] -> device [B*H][d_v][d_k] (transposed)."""
+    d_k, d_v = S_math.shape[-2:]
+    S = np.ascontiguousarray(np.swapaxes(S_math.reshape(-1, d_k, d_v), 1, 2), dtype=np.float32)
+    return torch.from_numpy(S).to(device)
+
+
+class Decoder:
+    def __init__(self, dims: lqk.Dims, win_len: np.ndarray, win_off: np.ndarray, device="cuda"):
+        self.dims = dims
+        self.state = lqk.State(dims, device)
+        self.win_len = np.asarray(win_len, np.int32)
+        self.win_off = np.asarray(win_off, np.int32)
+        assert len(self.win_len) == dims.batch and np.all(self.win_len <= dims.w_max)
+        self.period = int(np.lcm.reduce(self.win_len)) if dims.batch else 1
+        lists = [lqk.close_list(self.win_len, self.win_off, t) for t in range(self.period)]
+        self._close_n = [len(x) for x in lists]
+        self._close_at = np.cumsum([0] + self._close_n[:-1]).tolist()
+        flat = np.concatenate(lists + [np.zeros(1, np.int32)]).astype(np.int32)
+        self._close_ids = torch.from_numpy(flat).to(device)
+        self._all = all(n == dims.batch for n in self._close_n if n)
+        self.t = 0
+        self.o = torch.empty((dims.batch * dims.heads, dims.d), dtype=torch.float32, device=device)
+
+    def encode(self, S_dev: torch.Tensor, dbg: Optional[torch.Tensor] = None) -> None:
+        lqk.encode(self.dims, S_dev, self.state, dbg)
+        self.t = 0
+
+    def closes_at(self, t: int) -> int:
+        return self._close_n[t % self.period]
+
+    def close_due(self, t: int, dbg: Optional[torch.Tensor] = None) -> int:
+        """Close every sequence whose window ends with token t; returns how many."""
+        p = t % self.period
+        n = self._close_n[p]
+        if n == 0:
+            return 0
+        if n == self.dims.batch and dbg is None:
+            lqk.window_close(self.dims, self.state, None, 0, None)
+        else:
+            ids = self._close_ids[self._close_at[p]:self._close_at[p] + n]
+            lqk.window_close(self.dims, self.state, ids, n, dbg)
+        return n
+
+    def step(self, q, k, v, g, beta, o: Optional[torch.Tensor] = None, close: bool = True) -> torch.Tensor:
+        o = self.o if o is None else o
+        lqk.decode_step(self.dims, self.state, q, k, v, g, beta, o)
+        if close:
+            self.close_due(self.t)
+        self.t += 1
+        return o

@@ -1,0 +1,151 @@
+"""Test-side helpers for GPU-vs-oracle parity: code (un)packing, token
+flattening, and the two runs (HIP path through the C ABI, fp64 oracle) on the
+same seeded inputs. Nothing here computes the method: the oracle does that on
+the CPU and the HIP kernels on the GPU."""
+from __future__ import annotations
+
+from typing import Dict, List, Sequence
+
+import numpy as np
+import torch
+
+from linear_attention_recurrent_kda_amd import leapquant as lqk
+from linear_attention_recurrent_kda_amd import runner
+from linear_attention_recurrent_kda_amd import workloads as wk
+from oracle import leapquant_oracle as lq
+
+
+# ---- code format (include/leapquant.h): [BH][d_v][d_k] int8, or int4 packed
+def unpack_codes(raw: np.ndarray, bits: int, d: int) -> np.ndarray:
+    """Device codes [BH][d_v][d_k*bits/8] (int8 bytes) -> math layout [BH][d_k][d_v] int32."""
+    raw = np.asarray(raw)
+    if bits == 8:
+        C = raw.astype(np.int32).reshape(-1, d, d)
+    else:
+        u = raw.view(np.uint8).reshape(-1, d, d // 2).astype(np.int32)
+        lo, hi = ((u & 0xF) ^ 8) - 8, ((u >> 4) ^ 8) - 8
+        C = np.empty((u.shape[0], d, d), np.int32)
+        C[:, :, 0::2], C[:, :, 1::2] = lo, hi
+    return np.ascontiguousarray(np.swapaxes(C, 1, 2))
+
+
+def pack_codes(C: np.ndarray, bits: int) -> np.ndarray:
+    """Math layout [BH][d_k][d_v] ints -> device bytes [BH][d_v][d_k*bits/8] (int8)."""
+    Ct = np.swapaxes(np.asarray(C, np.int32), 1, 2)
+    if bits == 8:
+        return np.ascontiguousarray(Ct.astype(np.int8))
+    lo, hi = Ct[:, :, 0::2] & 0xF, Ct[:, :, 1::2] & 0xF
+    return np.ascontiguousarray((lo | (hi << 4)).astype(np.uint8).view(np.int8))
+
+
+def T(x: np.ndarray) -> np.ndarray:
+    """[..][a][b] -> [..][b][a]."""
+    return np.ascontiguousarray(np.swapaxes(x, -1, -2))
+
+
+def flat_steps(tok: Dict[str, np.ndarray]) -> List[Dict[str, np.ndarray]]:
+    """Token chunk [n][S][H][...] -> per-step dicts over N = S*H heads, float64."""
+    n = tok["q"].shape[0]
+    out = []
+    for t in range(n):
+        d = {}
+        for key in ("q", "k", "v", "g", "beta"):
+            a = tok[key][t]
+            d[key] = a.reshape((-1,) + a.shape[2:]).astype(np.float64)
+        out.append(d)
+    return out
+
+
+def download_state(st: lqk.State, dims: lqk.Dims) -> Dict[str, np.ndarray]:
+    torch.cuda.synchronize()
+    out = {n: getattr(st, n).cpu().numpy() for n in lqk.STATE_FIELDS}
+    out["C"] = unpack_codes(out["codes"], dims.bits, dims.d)
+    return out
+
+
+def encoded_of(host: Dict[str, np.ndarray]) -> lq.Encoded:
+    """GPU window-start state as the oracle's Encoded (fp32 values exact in fp64)."""
+    f = lambda x: np.asarray(x, np.float64)
+    return lq.Encoded(f(host["comp_k"]), f(host["comp_u"]), f(host["row_scale"]), f(host["col_scale"]),
+                      host["C"], None, True)
+
+
+def upload_state(st: lqk.State, dims: lqk.Dims, enc: lq.Encoded, buf_k=None, buf_u=None, buf_g=None,
+                 n=None) -> None:
+    """Write an oracle-made state into GPU buffers (rounded to fp32)."""
+    def put(dst: torch.Tensor, x):
+        dst.copy_(torch.from_numpy(np.ascontiguousarray(np.asarray(x, np.float32).reshape(dst.shape))))
+    st.codes.copy_(torch.from_numpy(pack_codes(enc.codes, dims.bits)).reshape(st.codes.shape))
+    put(st.row_scale, enc.s)
+    put(st.col_scale, enc.c)
+    if dims.n_comp:
+        put(st.comp_k, enc.comp_k)
+        put(st.comp_u, enc.comp_u)
+    if buf_k is not None:
+        put(st.buf_k, buf_k)
+        put(st.buf_u, buf_u)
+        put(st.buf_g, buf_g)
+        st.buf_len.copy_(torch.from_numpy(np.asarray(n, np.int32)))
+    else:
+        st.buf_len.zero_()
+
+
+def heads_of(seqs: Sequence[int], H: int) -> np.ndarray:
+    return (np.asarray(seqs)[:, None] * H + np.arange(H)[None, :]).reshape(-1)
+
+
+def rel_l2(a, b) -> float:
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def run_gpu(wl: wk.Workload, steps: int, check_seqs: Sequence[int], bits=None, chunk: int = 16):
+    """Free-running HIP path over the full batch; returns outputs of check_seqs [steps][S][H][d]."""
+    dims = runner.dims_for(wl, bits)
+    dec = runner.Decoder(dims, wk.window_lengths(wl), wk.window_offsets(wl))
+    S0 = wk.initial_states(wl, range(wl.batch))
+    dec.encode(runner.states_to_device(S0))
+    del S0
+    stream = wk.TokenStream(wl)
+    sel = torch.as_tensor(np.asarray(check_seqs), device="cuda", dtype=torch.long)
+    outs = torch.empty((steps, len(check_seqs), wl.heads, wl.d_v), dtype=torch.float32, device="cuda")
+    for c0 in range(0, steps, chunk):
+        n = min(chunk, steps - c0)
+        dev = runner.upload_tokens(stream.next(n), wl.act_bf16)
+        for i in range(n):
+            o = dec.step(dev["q"][i], dev["k"][i], dev["v"][i], dev["g"][i], dev["beta"][i])
+            outs[c0 + i] = o.view(wl.batch, wl.heads, wl.d_v).index_select(0, sel)
+        del dev
+    torch.cuda.synchronize()
+    err = int(dec.state.err.item())
+    return outs.cpu().numpy(), dec, err
+
+
+def run_oracle(wl: wk.Workload, steps: int, seqs: Sequence[int], bits=None, record=False):
+    """fp64 plain definition on the listed sequences (same per-sequence inputs)."""
+    S0 = wk.initial_states(wl, seqs).reshape(-1, wl.d_k, wl.d_v).astype(np.float64)
+    toks = flat_steps(wk.TokenStream(wl, seqs).next(steps))
+    H = wl.heads
+    win_len = np.repeat(wk.window_lengths(wl)[list(seqs)], H)
+    win_off = np.repeat(wk.window_offsets(wl)[list(seqs)], H)
+    res = lq.run_dense(S0, toks, win_len, win_off, r=wl.n_comp, T=wl.power_iters,
+                       bits=wl.bits if bits is None else bits, smoothing=wl.smoothing, record=record)
+    res["o"] = res["o"].reshape(steps, len(seqs), H, wl.d_v)
+    return res
+
+
+def g1_check(R_gpu_math: np.ndarray, host: Dict[str, np.ndarray], bits: int, smoothing: bool,
+             heads=None):
+    """Staged code gate: oracle E3-E4 in fp64 on the GPU's own fp32 residual."""
+    idx = slice(None) if heads is None else heads
+    s, c, C = lq.smooth_quantize(R_gpu_math.astype(np.float64), bits, smoothing)
+    Cg = host["C"][idx]
+    same = float(np.mean(Cg == C))
+    max_diff = int(np.max(np.abs(Cg - C)))
+    s_gpu = host["row_scale"][idx]
+    c_gpu = host["col_scale"][idx]
+    s_exact = bool(np.array_equal(s_gpu, s.astype(np.float32)))
+    c_ref = c.astype(np.float32)
+    ulp = np.spacing(np.maximum(np.abs(c_ref), np.float32(1e-38)).astype(np.float32))
+    c_ulps = float(np.max(np.abs(c_gpu.astype(np.float64) - c_ref.astype(np.float64)) / ulp))
+    return dict(same=same, max_diff=max_diff, s_exact=s_exact, c_ulps=c_ulps)

@@ -1,0 +1,147 @@
+"""C ABI host tests (CPU only): the library loads and exports every function
+include/leapquant.h declares; argument validation returns the documented codes
+before anything reaches the GPU; the host helpers compute sizes and close
+lists. No call here passes validation, so no kernel is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from linear_attention_recurrent_kda_amd import leapquant as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "leapquant.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def dims(**kw):
+    base = dict(batch=2, heads=3, d_k=128, d_v=128, w_max=16, n_comp=4, bits=8, decay_per_channel=0,
+                act_dtype=0, smoothing=1, power_iters=4)
+    base.update(kw)
+    return L.CDims(**base)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def state(**kw):
+    p = {n: FAKE + 0x1000 * i for i, n in enumerate(L.STATE_FIELDS)}
+    p.update(kw)
+    return L.CState(**p)
+
+
+def step(d, st, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE):
+    return L.raw_call("leapquant_decode_step", ctypes.byref(d), ctypes.byref(st), q, k, v, g, beta, o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_k=96, d_v=96), L.LQ_ERR_SHAPE),
+    (dict(d_k=128, d_v=64), L.LQ_ERR_SHAPE),
+    (dict(batch=-1), L.LQ_ERR_SHAPE),
+    (dict(bits=6), L.LQ_ERR_BITS),
+    (dict(w_max=0), L.LQ_ERR_CONFIG),
+    (dict(w_max=65), L.LQ_ERR_CONFIG),
+    (dict(n_comp=9), L.LQ_ERR_CONFIG),
+    (dict(power_iters=0), L.LQ_ERR_CONFIG),
+    (dict(act_dtype=2), L.LQ_ERR_CONFIG),
+    (dict(decay_per_channel=2), L.LQ_ERR_CONFIG),
+    (dict(smoothing=3), L.LQ_ERR_CONFIG),
+])
+def test_dims_validation(kw, code):
+    d = dims(**kw)
+    st = state()
+    assert step(d, st) == code
+    assert L.raw_call("leapquant_window_close", ctypes.byref(d), ctypes.byref(st), None, 0, None, None) == code
+    assert L.raw_call("leapquant_encode", ctypes.byref(d), FAKE, ctypes.byref(st), None, None) == code
+    sizes = (ctypes.c_size_t * L.LQ_STATE_NBUF)()
+    assert L.raw_call("lq_state_sizes", ctypes.byref(d), sizes) == code
+
+
+def test_null_and_alignment_validation():
+    d = dims()
+    assert L.raw_call("leapquant_decode_step", None, None, None, None, None, None, None, None, None) == L.LQ_ERR_NULL
+    assert step(d, state(codes=None)) == L.LQ_ERR_NULL
+    assert step(d, state(buf_k=None)) == L.LQ_ERR_NULL
+    assert step(d, state(), q=None) == L.LQ_ERR_NULL
+    assert step(d, state(comp_k=None)) == L.LQ_ERR_NULL
+    assert step(d, state(codes=FAKE + 4)) == L.LQ_ERR_ALIGN
+    assert step(d, state(buf_g=FAKE + 8)) == L.LQ_ERR_ALIGN
+    assert step(d, state(), q=FAKE + 2) == L.LQ_ERR_ALIGN
+    db = dims(act_dtype=1)
+    assert step(db, state(), q=FAKE + 1) == L.LQ_ERR_ALIGN
+    # r == 0 does not need compensator buffers, but a misaligned buffer is still rejected
+    assert step(dims(n_comp=0), state(comp_k=None, comp_u=None, buf_u=FAKE + 4)) == L.LQ_ERR_ALIGN
+    assert L.raw_call("gdn_decode_fp32_baseline", ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                      None) == L.LQ_ERR_NULL
+    assert L.raw_call("gdn_decode_fp32_baseline", ctypes.byref(d), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE,
+                      FAKE, None) == L.LQ_ERR_ALIGN
+    assert L.raw_call("leapquant_encode", ctypes.byref(d), None, ctypes.byref(state()), None, None) == L.LQ_ERR_NULL
+    assert L.raw_call("leapquant_encode", ctypes.byref(d), FAKE, ctypes.byref(state()), FAKE + 4,
+                      None) == L.LQ_ERR_ALIGN
+    assert L.raw_call("leapquant_dequantize", ctypes.byref(d), ctypes.byref(state()), None, None) == L.LQ_ERR_NULL
+
+
+def test_close_list_argument_validation():
+    d = dims()
+    st = state()
+    close = lambda ids, n: L.raw_call("leapquant_window_close", ctypes.byref(d), ctypes.byref(st), ids, n,
+                                      None, None)
+    assert close(FAKE, 3) == L.LQ_ERR_CONFIG       # more ids than sequences
+    assert close(FAKE, -1) == L.LQ_ERR_CONFIG
+    assert close(FAKE, 0) == L.LQ_OK               # empty list: nothing to do
+    assert close(FAKE + 2, 1) == L.LQ_ERR_ALIGN
+
+
+def test_empty_batch_is_a_no_op():
+    for kw in (dict(batch=0), dict(heads=0)):
+        d = dims(**kw)
+        empty = L.CState()
+        assert step(d, empty, None, None, None, None, None, None) == L.LQ_OK
+        assert L.raw_call("leapquant_encode", ctypes.byref(d), None, ctypes.byref(empty), None, None) == L.LQ_OK
+        assert L.raw_call("leapquant_window_close", ctypes.byref(d), ctypes.byref(empty), None, 0, None,
+                          None) == L.LQ_OK
+        assert L.raw_call("gdn_decode_fp32_baseline", ctypes.byref(d), None, None, None, None, None, None, None,
+                          None) == L.LQ_OK
+
+
+def test_state_sizes():
+    s = L.state_sizes(L.Dims(64, 32, 128, w_max=16, n_comp=4, bits=8))
+    BH = 64 * 32
+    assert s["codes"] == BH * 128 * 128 and s["buf_g"] == BH * 16 * 4 and s["err"] == 4
+    assert s["comp_k"] == s["comp_u"] == BH * 4 * 128 * 4
+    s4 = L.state_sizes(L.Dims(128, 32, 128, w_max=16, n_comp=4, bits=4, kda=True))
+    assert s4["codes"] == 128 * 32 * 128 * 64 and s4["buf_g"] == 128 * 32 * 16 * 128 * 4
+
+
+def test_close_list_matches_schedule():
+    rng = np.random.default_rng(0)
+    W = np.where(np.arange(40) % 2 == 0, 16, 32).astype(np.int32)
+    off = rng.integers(0, 16, 40).astype(np.int32)
+    for t in range(70):
+        want = [b for b in range(40) if (off[b] + t + 1) % W[b] == 0]
+        assert list(L.close_list(W, off, t)) == want
+    with pytest.raises(L.LeapQuantError):
+        L.close_list(np.array([16], np.int32), np.array([16], np.int32), 0)  # offset outside the window
+    with pytest.raises(L.LeapQuantError):
+        L.close_list(np.array([0], np.int32), np.array([0], np.int32), 0)
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.status_string(code) != "unknown status"
+    assert L.status_string(-99) == "unknown status"

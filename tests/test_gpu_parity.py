@@ -1,0 +1,290 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Protocol (tolerances are the ones the method's target states):
+  G1 codes, staged: the oracle smooths and quantises (fp64) the GPU's own
+     pre-quantisation residual; codes >= 99.99% identical and all within one
+     LSB, key-row scales bit-identical, value-column scales within 2 ulp.
+  G2 decomposition: the GPU's compensators plus residual rebuild the dense
+     state (the initial state, or the oracle's fold of the GPU's pre-close
+     buffers) to <= 1e-6 relative Frobenius.
+  G3 free-running outputs: for every token, relative L2 of o over all heads
+     <= 1e-3 against the oracle's plain definition from the same inputs.
+  G4 single step from an oracle-made state uploaded bit-exactly: o_t and u_t
+     <= 1e-5 relative.
+Full-size workloads run the whole batch on the GPU; the oracle checks all
+heads of the listed sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_recurrent_kda_amd import leapquant as lqk
+from linear_attention_recurrent_kda_amd import runner
+from linear_attention_recurrent_kda_amd import workloads as wk
+from oracle import leapquant_oracle as lq
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+W = wk.WORKLOADS
+
+
+def _subset(wl):
+    B = wl.batch
+    return sorted({0, 1, 2, 3, B - 2, B - 1} & set(range(B)))
+
+
+def _encode_case(wl, bits):
+    dims = runner.dims_for(wl, bits)
+    st = lqk.State(dims)
+    S0 = wk.initial_states(wl, range(wl.batch))
+    dbg = torch.empty((wl.batch * wl.heads, wl.d_v, wl.d_k), dtype=torch.float32, device="cuda")
+    lqk.encode(dims, runner.states_to_device(S0), st, dbg)
+    host = gh.download_state(st, dims)
+    R = gh.T(dbg.cpu().numpy())
+    return dims, S0.reshape(-1, wl.d_k, wl.d_v), host, R
+
+
+@pytest.mark.parametrize("name,bits", [("tiny_gdn", 8), ("qwen_gdn", 8), ("kda_int4", 4), ("kda_int4", 8)])
+def test_encode_codes_and_decomposition(name, bits):
+    wl = W[name]
+    if name == "kda_int4":
+        wl = wl.replace(batch=16)
+    dims, S0, host, R = _encode_case(wl, bits)
+    g1 = gh.g1_check(R, host, bits, wl.smoothing)
+    print(name, bits, g1)
+    assert g1["same"] >= 0.9999 and g1["max_diff"] <= 1
+    assert g1["s_exact"] and g1["c_ulps"] <= 2.0
+    # G2: compensators + residual rebuild the initial state
+    rebuilt = np.einsum("nli,nlj->nij", host["comp_k"].astype(np.float64), host["comp_u"]) + R
+    err = np.linalg.norm(rebuilt - S0, axis=(1, 2)) / np.linalg.norm(S0, axis=(1, 2))
+    assert err.max() <= 1e-6, err.max()
+    assert np.all(host["buf_len"] == 0)
+    # the compensators follow the oracle's power method (same start vectors)
+    ref = lq.encode(S0.astype(np.float64), wl.n_comp, wl.power_iters, bits, wl.smoothing)
+    cos = np.abs(np.einsum("nli,nli->nl", host["comp_k"].astype(np.float64), ref.comp_k))
+    assert cos.min() >= 1 - 1e-4, cos.min()
+    # end-to-end code agreement is reported, not gated
+    print("end-to-end code agreement", float(np.mean(host["C"] == ref.codes)))
+
+
+@pytest.mark.parametrize("name,bits", [("tiny_gdn", 8), ("kda_int4", 4)])
+def test_dequantize_matches_oracle_decode(name, bits):
+    wl = W[name].replace(batch=min(W[name].batch, 4))
+    dims, S0, host, R = _encode_case(wl, bits)
+    out = torch.empty((wl.batch * wl.heads, wl.d_v, wl.d_k), dtype=torch.float32, device="cuda")
+    lqk.dequantize(dims, lqk_state_from_host(dims, host), out)
+    ref = lq.decode(gh.encoded_of(host))
+    assert gh.rel_l2(gh.T(out.cpu().numpy()), ref) <= 1e-6
+
+
+def lqk_state_from_host(dims, host):
+    st = lqk.State(dims)
+    for n in lqk.STATE_FIELDS:
+        getattr(st, n).copy_(torch.from_numpy(host[n]))
+    return st
+
+
+@pytest.mark.parametrize("name,bits,n_pre", [("tiny_gdn", 8, 5), ("qwen_gdn", 8, 7), ("kda_int4", 4, 9),
+                                              ("kda_int4", 8, 0), ("prefix_mix", 8, 20)])
+def test_single_step_from_uploaded_state(name, bits, n_pre):
+    """G4: oracle state after n_pre buffered tokens, rounded to fp32 and uploaded."""
+    wl = W[name]
+    seqs = list(range(min(wl.batch, 4)))
+    wl = wl.replace(batch=len(seqs))
+    H, d = wl.heads, wl.d_k
+    dims = runner.dims_for(wl, bits)
+    S0 = wk.initial_states(wl, seqs).reshape(-1, d, d).astype(np.float64)
+    stream = wk.TokenStream(wl, seqs)
+    toks = gh.flat_steps(stream.next(n_pre + 1))
+    N = len(seqs) * H
+    bo = lq.BufferedOracle(S0, np.full(N, 10 ** 6), np.zeros(N), w_max=wl.w_max, r=wl.n_comp,
+                           T=wl.power_iters, bits=bits, smoothing=wl.smoothing, kda=wl.kda)
+    for t in toks[:n_pre]:
+        bo.step(t["q"], t["k"], t["v"], t["g"], t["beta"])
+    # round the whole state to fp32, as it will sit on the GPU
+    r32 = lambda x: np.asarray(x, np.float32).astype(np.float64)
+    for f in ("comp_k", "comp_u", "s", "c"):
+        setattr(bo.base, f, r32(getattr(bo.base, f)))
+    bo.buf_k, bo.buf_u, bo.buf_G = r32(bo.buf_k), r32(bo.buf_u), r32(bo.buf_G)
+    st = lqk.State(dims)
+    gh.upload_state(st, dims, bo.base, bo.buf_k, bo.buf_u, bo.buf_G, bo.n)
+    last = toks[n_pre]
+    o_ref, u_ref = bo.step(last["q"], last["k"], last["v"], last["g"], last["beta"])
+    raw = wk.TokenStream(wl, seqs).next(n_pre + 1)
+    dev = runner.upload_tokens({k: v[n_pre:] for k, v in raw.items()}, wl.act_bf16)
+    o = torch.empty((N, d), dtype=torch.float32, device="cuda")
+    lqk.decode_step(dims, st, dev["q"][0], dev["k"][0], dev["v"][0], dev["g"][0], dev["beta"][0], o)
+    host = gh.download_state(st, dims)
+    u_gpu = host["buf_u"][np.arange(N), n_pre]
+    print(name, bits, gh.rel_l2(o.cpu().numpy(), o_ref), gh.rel_l2(u_gpu, u_ref))
+    assert gh.rel_l2(o.cpu().numpy(), o_ref) <= 1e-5
+    assert gh.rel_l2(u_gpu, u_ref) <= 1e-5
+    assert np.all(host["buf_len"] == n_pre + 1)
+    assert np.array_equal(host["buf_k"][np.arange(N), n_pre], np.asarray(last["k"], np.float32))
+
+
+@pytest.mark.parametrize("name,bits,steps", [
+    ("tiny_gdn", 8, 64),
+    ("qwen_gdn", 8, 256),
+    ("serving_gdn", 8, 48),
+    ("kda_int4", 4, 48),
+    ("kda_int4", 8, 48),
+    ("prefix_mix", 8, 64),
+])
+def test_free_running_outputs(name, bits, steps):
+    """G3 at the full batch of each workload (oracle on a subset of sequences)."""
+    wl = W[name]
+    seqs = list(range(wl.batch)) if wl.batch * wl.heads <= 256 else _subset(wl)
+    o_gpu, dec, err = gh.run_gpu(wl, steps, seqs, bits)
+    assert err == 0
+    ref = gh.run_oracle(wl, steps, seqs, bits)
+    per_step = [gh.rel_l2(o_gpu[t], ref["o"][t]) for t in range(steps)]
+    worst = int(np.argmax(per_step))
+    print(name, bits, "max rel L2", per_step[worst], "at step", worst)
+    assert max(per_step) <= 1e-3
+
+
+def test_close_codes_and_decomposition():
+    """G1 + G2 at a window close: the GPU's pre-close buffers folded by the oracle."""
+    for name, bits in (("qwen_gdn", 8), ("kda_int4", 4)):
+        wl = W[name].replace(batch=8)
+        dims = runner.dims_for(wl, bits)
+        dec = runner.Decoder(dims, wk.window_lengths(wl), wk.window_offsets(wl))
+        dec.encode(runner.states_to_device(wk.initial_states(wl, range(wl.batch))))
+        dev = runner.upload_tokens(wk.TokenStream(wl).next(wl.window), wl.act_bf16)
+        for i in range(wl.window):
+            dec.step(dev["q"][i], dev["k"][i], dev["v"][i], dev["g"][i], dev["beta"][i], close=False)
+        pre = gh.download_state(dec.state, dims)
+        assert np.all(pre["buf_len"] == wl.window)
+        F = lq.fold_window(lq.decode(gh.encoded_of(pre)), pre["buf_k"], pre["buf_u"], pre["buf_g"],
+                           pre["buf_len"], wl.kda)
+        dbg = torch.zeros((wl.batch * wl.heads, wl.d_v, wl.d_k), dtype=torch.float32, device="cuda")
+        assert dec.close_due(wl.window - 1, dbg) == wl.batch
+        post = gh.download_state(dec.state, dims)
+        R = gh.T(dbg.cpu().numpy())
+        rebuilt = np.einsum("nli,nlj->nij", post["comp_k"].astype(np.float64), post["comp_u"]) + R
+        err = np.linalg.norm(rebuilt - F, axis=(1, 2)) / np.linalg.norm(F, axis=(1, 2))
+        assert err.max() <= 1e-6, (name, err.max())
+        g1 = gh.g1_check(R, post, bits, wl.smoothing)
+        print(name, bits, g1)
+        assert g1["same"] >= 0.9999 and g1["max_diff"] <= 1 and g1["s_exact"] and g1["c_ulps"] <= 2.0
+        assert np.all(post["buf_len"] == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny_gdn", "qwen_gdn", "kda_int4"])
+def test_fp32_baseline_matches_exact_recurrence(name):
+    wl = W[name].replace(batch=min(W[name].batch, 8))
+    dims = runner.dims_for(wl)
+    S0 = wk.initial_states(wl, range(wl.batch))
+    S = runner.states_to_device(S0)
+    steps = 24
+    raw = wk.TokenStream(wl).next(steps)
+    dev = runner.upload_tokens(raw, wl.act_bf16)
+    toks = gh.flat_steps(raw)
+    Sref = S0.reshape(-1, wl.d_k, wl.d_v).astype(np.float64)
+    o = torch.empty((wl.batch * wl.heads, wl.d_v), dtype=torch.float32, device="cuda")
+    for t in range(steps):
+        lqk.fp32_baseline_step(dims, S, dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], o)
+        Sref, oref, _ = lq.exact_step(Sref, toks[t]["q"], toks[t]["k"], toks[t]["v"], toks[t]["g"],
+                                      toks[t]["beta"])
+        assert gh.rel_l2(o.cpu().numpy(), oref) <= 1e-5
+    assert gh.rel_l2(gh.T(S.cpu().numpy()), Sref) <= 1e-5
+
+
+def test_deterministic():
+    wl = W["qwen_gdn"].replace(batch=8)
+    a, dec_a, _ = gh.run_gpu(wl, 40, list(range(8)))
+    b, dec_b, _ = gh.run_gpu(wl, 40, list(range(8)))
+    assert np.array_equal(a, b)
+    for n in lqk.STATE_FIELDS:
+        assert torch.equal(getattr(dec_a.state, n), getattr(dec_b.state, n)), n
+
+
+def test_power_of_two_scaling_is_exact():
+    wl = W["qwen_gdn"].replace(batch=4)
+    dims = runner.dims_for(wl)
+    S0 = wk.initial_states(wl, range(4))
+    outs = []
+    for p in (0, 5):
+        st = lqk.State(dims)
+        lqk.encode(dims, runner.states_to_device(S0 * np.float32(2.0 ** p)), st)
+        outs.append(gh.download_state(st, dims))
+    a, b = outs
+    assert np.array_equal(a["codes"], b["codes"])
+    assert np.array_equal(a["row_scale"] * np.float32(32.0), b["row_scale"])
+    assert np.array_equal(a["col_scale"], b["col_scale"])
+    assert np.array_equal(a["comp_k"], b["comp_k"])
+    assert np.array_equal(a["comp_u"] * np.float32(32.0), b["comp_u"])
+
+
+def test_max_window_and_compensators():
+    """w_max = 64 with r = 8: more key rows than one pass of the row groups."""
+    wl = W["tiny_gdn"].replace(batch=2, heads=3, d_k=128, d_v=128, window=64, n_comp=8, steps=70)
+    steps = 70
+    o_gpu, _, err = gh.run_gpu(wl, steps, [0, 1])
+    assert err == 0
+    ref = gh.run_oracle(wl, steps, [0, 1])
+    worst = max(gh.rel_l2(o_gpu[t], ref["o"][t]) for t in range(steps))
+    assert worst <= 1e-3, worst
+
+
+@pytest.mark.parametrize("d,kda", [(64, False), (64, True), (32, True)])
+def test_other_head_dims(d, kda):
+    wl = W["tiny_gdn"].replace(batch=3, heads=2, d_k=d, d_v=d, kda=kda, steps=40)
+    o_gpu, _, err = gh.run_gpu(wl, 40, [0, 1, 2])
+    ref = gh.run_oracle(wl, 40, [0, 1, 2])
+    assert err == 0
+    assert max(gh.rel_l2(o_gpu[t], ref["o"][t]) for t in range(40)) <= 1e-3
+
+
+def test_partial_window_close_and_window_one():
+    """A close after 5 of 16 tokens (partial window) and W = 1, r = 0 (per-token requantisation)."""
+    wl = W["tiny_gdn"].replace(batch=2, heads=2)
+    dims = runner.dims_for(wl)
+    st_dec = runner.Decoder(dims, np.full(2, 16), np.zeros(2))
+    S0 = wk.initial_states(wl, [0, 1])
+    st_dec.encode(runner.states_to_device(S0))
+    raw = wk.TokenStream(wl).next(8)
+    dev = runner.upload_tokens(raw, False)
+    for i in range(5):
+        st_dec.step(dev["q"][i], dev["k"][i], dev["v"][i], dev["g"][i], dev["beta"][i], close=False)
+    lqk.window_close(dims, st_dec.state, torch.tensor([1], dtype=torch.int32, device="cuda"))
+    host = gh.download_state(st_dec.state, dims)
+    assert list(host["buf_len"]) == [5, 5, 0, 0]
+    # oracle: sequence 1 closes after its 5th token
+    toks = gh.flat_steps(raw)
+    ref = lq.run_dense(S0.reshape(-1, 32, 32).astype(np.float64), toks[:5], np.array([99, 99, 5, 5]),
+                       np.zeros(4), r=2)
+    dense = lq.decode(gh.encoded_of({k: v[2:] for k, v in host.items()}))
+    assert gh.rel_l2(dense, ref["S"][2:]) <= 1e-2  # both are quantised states (1 LSB level)
+    # W = 1, r = 0
+    wl1 = wl.replace(window=1, n_comp=0)
+    o_gpu, _, err = gh.run_gpu(wl1, 20, [0, 1])
+    ref1 = gh.run_oracle(wl1, 20, [0, 1])
+    assert err == 0 and max(gh.rel_l2(o_gpu[t], ref1["o"][t]) for t in range(20)) <= 1e-3
+
+
+def test_device_error_flags_and_empty_call():
+    wl = W["tiny_gdn"].replace(batch=2, heads=2, window=4)
+    dims = runner.dims_for(wl)
+    st = lqk.State(dims)
+    lqk.encode(dims, runner.states_to_device(wk.initial_states(wl, [0, 1])), st)
+    st.buf_len[1] = dims.w_max  # host forces the buffer-full precondition on head 1
+    before = {n: getattr(st, n).clone() for n in ("buf_k", "buf_u", "buf_g")}
+    dev = runner.upload_tokens(wk.TokenStream(wl).next(1), False)
+    o = torch.full((4, 32), 7.0, device="cuda")
+    lqk.decode_step(dims, st, dev["q"][0], dev["k"][0], dev["v"][0], dev["g"][0], dev["beta"][0], o)
+    torch.cuda.synchronize()
+    assert int(st.err.item()) & lqk.LQ_DEVERR_BUFFER_FULL
+    assert torch.all(o[1] == 7.0) and not torch.all(o[0] == 7.0)
+    assert int(st.buf_len[1]) == dims.w_max and int(st.buf_len[0]) == 1
+    for n, t in before.items():
+        assert torch.equal(getattr(st, n)[1], t[1])
+    st.err.zero_()
+    lqk.window_close(dims, st, torch.tensor([5], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(st.err.item()) & lqk.LQ_DEVERR_BAD_SEQ
+    # empty batch: accepted, nothing enqueued
+    lqk.decode_step(runner.dims_for(wl.replace(batch=0)), lqk.State(runner.dims_for(wl.replace(batch=0))),
+                    dev["q"][0], dev["k"][0], dev["v"][0], dev["g"][0], dev["beta"][0], o)
