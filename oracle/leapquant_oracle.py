@@ -184,8 +184,9 @@ class Encoded:
     quantized: bool
 
     def take(self, idx) -> "Encoded":
+        resid = None if self.resid is None else self.resid[idx]
         return Encoded(self.comp_k[idx], self.comp_u[idx], self.s[idx], self.c[idx],
-                       self.codes[idx], self.resid[idx], self.quantized)
+                       self.codes[idx], resid, self.quantized)
 
 
 def encode(S, r: int, T: int, bits: int, smoothing: bool = True, quantize: bool = True) -> Encoded:
@@ -223,7 +224,7 @@ class CloseEvent:
 
 def run_dense(S_init, tokens: Iterable[Dict[str, np.ndarray]], win_len, win_off, *, r: int,
               T: int = 4, bits: int = 8, smoothing: bool = True, quantize: bool = True,
-              record: bool = False):
+              record: bool = False, rounding_noise: float = 0.0, noise_seed: int = 0):
     """Run LeapQuant decoding as its plain definition.
 
     S <- Dec(Enc(S_init)); for each token: S <- exact step; when the head's
@@ -232,11 +233,23 @@ def run_dense(S_init, tokens: Iterable[Dict[str, np.ndarray]], win_len, win_off,
     o_W uses the unquantised state); window position starts at the head's
     offset with nothing buffered; every head of a sequence shares its window.
 
+    rounding_noise > 0 is not part of the method: every state entering Enc is
+    first multiplied entrywise by (1 + rounding_noise * N(0,1)). With a noise
+    of fp32 rounding size this measures how well the plain definition's
+    outputs are determined by its inputs (rounding decisions near ties).
+
     S_init [N][d_k][d_v]; tokens yields per-step dicts with q, k [N][d_k],
     v [N][d_v], g [N] or [N][d_k], beta [N]; win_len, win_off [N].
     Returns dict(o [T][N][d_v], u [T][N][d_v], S final, enc0, closes).
     """
-    enc0 = encode(S_init, r, T, bits, smoothing, quantize)
+    rng = np.random.default_rng(noise_seed)
+
+    def enc(X):
+        if rounding_noise:
+            X = X * (1.0 + rounding_noise * rng.standard_normal(X.shape))
+        return encode(X, r, T, bits, smoothing, quantize)
+
+    enc0 = enc(_f64(S_init))
     S = decode(enc0)
     pos = np.array(win_off, np.int64).copy()
     W = np.array(win_len, np.int64)
@@ -248,7 +261,7 @@ def run_dense(S_init, tokens: Iterable[Dict[str, np.ndarray]], win_len, win_off,
         pos += 1
         idx = np.nonzero(pos == W)[0]
         if idx.size:
-            e = encode(S[idx], r, T, bits, smoothing, quantize)
+            e = enc(S[idx])
             if record:
                 closes.append(CloseEvent(t, idx, S[idx].copy(), e))
             S[idx] = decode(e)

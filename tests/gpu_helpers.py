@@ -13,6 +13,7 @@ from linear_attention_recurrent_kda_amd import leapquant as lqk
 from linear_attention_recurrent_kda_amd import runner
 from linear_attention_recurrent_kda_amd import workloads as wk
 from oracle import leapquant_oracle as lq
+from tests.oracle_inputs import flat_steps, rel_l2  # noqa: F401
 
 
 # ---- code format (include/leapquant.h): [BH][d_v][d_k] int8, or int4 packed
@@ -41,19 +42,6 @@ def pack_codes(C: np.ndarray, bits: int) -> np.ndarray:
 def T(x: np.ndarray) -> np.ndarray:
     """[..][a][b] -> [..][b][a]."""
     return np.ascontiguousarray(np.swapaxes(x, -1, -2))
-
-
-def flat_steps(tok: Dict[str, np.ndarray]) -> List[Dict[str, np.ndarray]]:
-    """Token chunk [n][S][H][...] -> per-step dicts over N = S*H heads, float64."""
-    n = tok["q"].shape[0]
-    out = []
-    for t in range(n):
-        d = {}
-        for key in ("q", "k", "v", "g", "beta"):
-            a = tok[key][t]
-            d[key] = a.reshape((-1,) + a.shape[2:]).astype(np.float64)
-        out.append(d)
-    return out
 
 
 def download_state(st: lqk.State, dims: lqk.Dims) -> Dict[str, np.ndarray]:
@@ -94,18 +82,37 @@ def heads_of(seqs: Sequence[int], H: int) -> np.ndarray:
     return (np.asarray(seqs)[:, None] * H + np.arange(H)[None, :]).reshape(-1)
 
 
-def rel_l2(a, b) -> float:
-    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
-    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+def overwrite_heads(st: lqk.State, dims: lqk.Dims, gpu_heads, enc: lq.Encoded) -> None:
+    """Replace the window-start state of some heads by an oracle encoding (fp32)."""
+    idx = torch.as_tensor(np.asarray(gpu_heads), device="cuda", dtype=torch.long)
+    dev = lambda x, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+    st.codes[idx] = dev(pack_codes(enc.codes, dims.bits), torch.int8)
+    st.row_scale[idx] = dev(np.asarray(enc.s, np.float32))
+    st.col_scale[idx] = dev(np.asarray(enc.c, np.float32))
+    if dims.n_comp:
+        st.comp_k[idx] = dev(np.asarray(enc.comp_k, np.float32))
+        st.comp_u[idx] = dev(np.asarray(enc.comp_u, np.float32))
 
 
-def run_gpu(wl: wk.Workload, steps: int, check_seqs: Sequence[int], bits=None, chunk: int = 16):
-    """Free-running HIP path over the full batch; returns outputs of check_seqs [steps][S][H][d]."""
+def run_gpu(wl: wk.Workload, steps: int, check_seqs: Sequence[int], bits=None, chunk: int = 16,
+            force=None):
+    """HIP path over the full batch; returns outputs of check_seqs [steps][S][H][d].
+
+    force: an oracle result of run_oracle(..., record=True) on check_seqs. The
+    checked heads then start every window from the oracle's encoding (teacher
+    forcing): after the GPU closes a window, those heads are overwritten with
+    the oracle's Enc of the same window, so each window's outputs test the
+    kernels' arithmetic without the history of earlier rounding decisions."""
     dims = runner.dims_for(wl, bits)
     dec = runner.Decoder(dims, wk.window_lengths(wl), wk.window_offsets(wl))
     S0 = wk.initial_states(wl, range(wl.batch))
     dec.encode(runner.states_to_device(S0))
     del S0
+    gheads = heads_of(check_seqs, wl.heads)
+    closes = {}
+    if force is not None:
+        overwrite_heads(dec.state, dims, gheads, force["enc0"])
+        closes = {ev.step: ev for ev in force["closes"]}
     stream = wk.TokenStream(wl)
     sel = torch.as_tensor(np.asarray(check_seqs), device="cuda", dtype=torch.long)
     outs = torch.empty((steps, len(check_seqs), wl.heads, wl.d_v), dtype=torch.float32, device="cuda")
@@ -113,15 +120,19 @@ def run_gpu(wl: wk.Workload, steps: int, check_seqs: Sequence[int], bits=None, c
         n = min(chunk, steps - c0)
         dev = runner.upload_tokens(stream.next(n), wl.act_bf16)
         for i in range(n):
+            t = c0 + i
             o = dec.step(dev["q"][i], dev["k"][i], dev["v"][i], dev["g"][i], dev["beta"][i])
-            outs[c0 + i] = o.view(wl.batch, wl.heads, wl.d_v).index_select(0, sel)
+            outs[t] = o.view(wl.batch, wl.heads, wl.d_v).index_select(0, sel)
+            if t in closes:
+                overwrite_heads(dec.state, dims, gheads[closes[t].heads], closes[t].enc)
         del dev
     torch.cuda.synchronize()
     err = int(dec.state.err.item())
     return outs.cpu().numpy(), dec, err
 
 
-def run_oracle(wl: wk.Workload, steps: int, seqs: Sequence[int], bits=None, record=False):
+def run_oracle(wl: wk.Workload, steps: int, seqs: Sequence[int], bits=None, record=False,
+               rounding_noise: float = 0.0, noise_seed: int = 1):
     """fp64 plain definition on the listed sequences (same per-sequence inputs)."""
     S0 = wk.initial_states(wl, seqs).reshape(-1, wl.d_k, wl.d_v).astype(np.float64)
     toks = flat_steps(wk.TokenStream(wl, seqs).next(steps))
@@ -129,7 +140,8 @@ def run_oracle(wl: wk.Workload, steps: int, seqs: Sequence[int], bits=None, reco
     win_len = np.repeat(wk.window_lengths(wl)[list(seqs)], H)
     win_off = np.repeat(wk.window_offsets(wl)[list(seqs)], H)
     res = lq.run_dense(S0, toks, win_len, win_off, r=wl.n_comp, T=wl.power_iters,
-                       bits=wl.bits if bits is None else bits, smoothing=wl.smoothing, record=record)
+                       bits=wl.bits if bits is None else bits, smoothing=wl.smoothing, record=record,
+                       rounding_noise=rounding_noise, noise_seed=noise_seed)
     res["o"] = res["o"].reshape(steps, len(seqs), H, wl.d_v)
     return res
 

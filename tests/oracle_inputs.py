@@ -26,3 +26,22 @@ def planted_state(rng, N, dk, dv, sigma=0.1, rows=2, rmul=50.0, cols=1, cmul=20.
         S[n, rng.choice(dk, rows, replace=False), :] *= rmul
         S[n, :, rng.choice(dv, cols, replace=False)] *= cmul
     return S
+
+
+def flat_steps(tok):
+    """Token chunk [n][S][H][...] from the workload stream -> per-step dicts over
+    N = S*H heads, float64."""
+    n = tok["q"].shape[0]
+    out = []
+    for t in range(n):
+        d = {}
+        for key in ("q", "k", "v", "g", "beta"):
+            a = tok[key][t]
+            d[key] = a.reshape((-1,) + a.shape[2:]).astype(np.float64)
+        out.append(d)
+    return out
+
+
+def rel_l2(a, b) -> float:
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))

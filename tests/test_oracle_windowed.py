@@ -127,3 +127,26 @@ def test_per_window_error_is_smaller_than_per_token():
     naive = lq.run_dense(S0, toks, np.ones(N), np.zeros(N), r=0, smoothing=False)
     e_lq, e_naive = _rel(lqo["o"], ref), _rel(naive["o"], ref)
     assert e_lq < 0.5 * e_naive, (e_lq, e_naive)
+
+
+def test_rounding_noise_option_and_free_running_sensitivity():
+    """The plain definition is only as well determined as its rounding
+    decisions: a relative perturbation of fp32 rounding size at every window
+    close moves the free-running outputs of a window-of-one run by more than
+    1e-3 within a dozen tokens (an entry lands within ~1e-5 LSB of a tie),
+    while a window of two stays at rounding level. This is why GPU parity is
+    gated teacher-forced per window, and free-running runs are held to this
+    envelope once it exceeds the 1e-3 target."""
+    from linear_attention_recurrent_kda_amd import workloads as wk
+    from tests.oracle_inputs import flat_steps, rel_l2
+    for W, expect_big in ((1, True), (2, False)):
+        wl = wk.WORKLOADS["tiny_gdn"].replace(batch=2, heads=2, window=W, n_comp=0)
+        S0 = wk.initial_states(wl, [0, 1]).reshape(-1, 32, 32).astype(np.float64)
+        toks = flat_steps(wk.TokenStream(wl, [0, 1]).next(12))
+        args = dict(r=0, bits=8)
+        a = lq.run_dense(S0, toks, np.full(4, W), np.zeros(4), **args)
+        a0 = lq.run_dense(S0, toks, np.full(4, W), np.zeros(4), rounding_noise=0.0, **args)
+        assert np.array_equal(a["o"], a0["o"])
+        b = lq.run_dense(S0, toks, np.full(4, W), np.zeros(4), rounding_noise=2.0 ** -24, noise_seed=1, **args)
+        env = max(rel_l2(b["o"][t], a["o"][t]) for t in range(12))
+        assert (env > 1e-3) == expect_big, (W, env)
