@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Decode throughput of LeapQuant on one MI355X: the int8 decode step plus its
+window closes, against the FP32-state baseline on identical inputs.
+
+Default workload: Qwen-style GDN decode, 64 sequences x 32 heads,
+d_k = d_v = 128, window W = 16, r = 4 compensators, int8 residual with
+per-key-row smoothing and per-value-column scales, bf16 q/k/v (synthetic,
+seeded). L = 8 independent state sets, one per linear-attention layer of a
+model, are advanced in turn, so each launch reads its state from HBM and not
+from the 256 MB Infinity Cache.
+
+One step = one decode token for every head of every layer, plus the window
+closes that fall on that token. The timed region replays HIP graphs: the
+decode launches between two close points form one graph, the closes due at a
+point another; HIP events on the replay stream bracket every graph, which
+gives the average duration of each kernel. The whole region is bracketed by
+device synchronisation on both sides.
+
+Prints one JSON line. The roofline object describes the decode-step kernel:
+achieved = algorithmic bytes per launch / average launch duration.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--layers", type=int, default=8)
+    p.add_argument("--workload", default="qwen_gdn")
+    p.add_argument("--bits", type=int, default=None)
+    p.add_argument("--no-fp32", action="store_true", help="skip the FP32-state baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    p.add_argument("--cpu-sample", default="8x128", help="oracle sample: sequences x steps")
+    return p.parse_args()
+
+
+def schedule(win_len, win_off, total):
+    """Per step: list of sequences whose window closes after it; per step and
+    sequence the number of tokens already buffered (n)."""
+    import numpy as np
+    B = len(win_len)
+    n = np.zeros(B, np.int64)
+    closes, ns = [], []
+    for t in range(total):
+        ns.append(n.copy())
+        n += 1
+        due = np.nonzero((win_off.astype(np.int64) + t + 1) % win_len == 0)[0]
+        closes.append(due)
+        n[due] = 0
+    return closes, ns
+
+
+def segments(closes, t0, t1):
+    """Split steps [t0, t1) after every step with a close."""
+    segs, start = [], t0
+    for t in range(t0, t1):
+        if len(closes[t]) or t == t1 - 1:
+            segs.append((start, t + 1))
+            start = t + 1
+    return segs
+
+
+def run_gpu(args, wl, bits):
+    import numpy as np
+    import torch
+
+    from linear_attention_recurrent_kda_amd import bytes_model as bm
+    from linear_attention_recurrent_kda_amd import leapquant as lqk
+    from linear_attention_recurrent_kda_amd import runner
+    from linear_attention_recurrent_kda_amd import workloads as wk
+
+    torch.cuda.set_device(0)
+    L, K, Wu = args.layers, args.steps, args.warmup
+    total = Wu + K
+    dims = runner.dims_for(wl, bits)
+    BH, D = wl.batch * wl.heads, wl.d_k
+    win_len, win_off = wk.window_lengths(wl), wk.window_offsets(wl)
+    closes, ns = schedule(win_len, win_off, total)
+
+    # inputs resident in HBM before anything is timed
+    S_init = runner.states_to_device(wk.initial_states(wl, range(wl.batch)))
+    toks = [wk.device_tokens(wl, total, seed=l) for l in range(L)]
+    states = [lqk.State(dims) for _ in range(L)]
+    for st in states:
+        lqk.encode(dims, S_init, st)
+    outs = [torch.empty((BH, D), dtype=torch.float32, device="cuda") for _ in range(L)]
+    close_ids = {}  # distinct close lists, uploaded once
+
+    def ids_for(t):
+        key = tuple(int(b) for b in closes[t])
+        if key not in close_ids:
+            close_ids[key] = torch.tensor(key, dtype=torch.int32, device="cuda")
+        return close_ids[key]
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def dec_graph(a, b):
+        def body():
+            for t in range(a, b):
+                for l in range(L):
+                    x = toks[l]
+                    lqk.decode_step(dims, states[l], x["q"][t], x["k"][t], x["v"][t], x["g"][t],
+                                    x["beta"][t], outs[l])
+        return capture(body)
+
+    def close_graph(t):
+        ids = ids_for(t)
+        all_seqs = len(closes[t]) == wl.batch
+
+        def body():
+            for l in range(L):
+                if all_seqs:
+                    lqk.window_close(dims, states[l], None, 0)
+                else:
+                    lqk.window_close(dims, states[l], ids, len(closes[t]))
+        return capture(body)
+
+    torch.cuda.synchronize()
+    # capture: one decode graph per segment, one close graph per distinct close list
+    plan = []
+    cgraphs = {}
+    for (a, b) in segments(closes, 0, total):
+        g_dec = dec_graph(a, b)
+        key = tuple(int(x) for x in closes[b - 1])
+        if key and key not in cgraphs:
+            cgraphs[key] = close_graph(b - 1)
+        plan.append((a, b, g_dec, cgraphs.get(key) if key else None))
+    torch.cuda.synchronize()
+    # capture ran nothing; start from freshly encoded states
+    for st in states:
+        lqk.encode(dims, S_init, st)
+    torch.cuda.synchronize()
+
+    def replay(lo, hi, timed):
+        evs = []
+        for (a, b, g_dec, g_close) in plan:
+            if a < lo or a >= hi:
+                continue
+            if timed:
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record()
+            g_dec.replay()
+            if timed:
+                e1.record()
+            if g_close is not None:
+                g_close.replay()
+            if timed:
+                e2.record()
+                evs.append((a, b, e0, e1, e2, g_close is not None))
+        return evs
+
+    replay(0, Wu, timed=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = replay(Wu, total, timed=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    err = int(sum(int(st.err.item()) for st in states))
+    assert err == 0, f"device error word {err}"
+
+    # per-kernel averages from the events and algorithmic bytes from the schedule
+    dec_us = close_us = 0.0
+    n_dec = n_close = 0
+    dec_bytes = close_bytes = 0
+    H = wl.heads
+    for (a, b, e0, e1, e2, has_close) in evs:
+        dec_us += e0.elapsed_time(e1) * 1e3
+        n_dec += (b - a) * L
+        for t in range(a, b):
+            dec_bytes += L * H * sum(bm.step_bytes(D, wl.n_comp, dims.bits, wl.kda, wl.act_bf16, int(n))
+                                     for n in ns[t])
+        if has_close:
+            close_us += e1.elapsed_time(e2) * 1e3
+            n_close += L
+            t = b - 1
+            close_bytes += L * H * sum(bm.close_bytes(D, wl.n_comp, dims.bits, wl.kda, wl.act_bf16,
+                                                      int(ns[t][s]) + 1) for s in closes[t])
+    res = dict(wall=wall, dec_us=dec_us / max(n_dec, 1), close_us=close_us / max(n_close, 1),
+               n_dec=n_dec, n_close=n_close, dec_bytes=dec_bytes, close_bytes=close_bytes,
+               dec_gbs=dec_bytes / (dec_us * 1e-6) / 1e9 if dec_us else 0.0,
+               head_tokens=K * L * BH, state_mb=states[0].nbytes() / 1e6)
+
+    # FP32-state baseline on identical inputs and the same protocol
+    if not args.no_fp32:
+        del states
+        Sf = [S_init.clone() for _ in range(L)]
+
+        def fp_graph(a, b):
+            def body():
+                for t in range(a, b):
+                    for l in range(L):
+                        x = toks[l]
+                        lqk.fp32_baseline_step(dims, Sf[l], x["q"][t], x["k"][t], x["v"][t], x["g"][t],
+                                               x["beta"][t], outs[l])
+            return capture(body)
+        fplan = [(a, b, fp_graph(a, b)) for (a, b) in segments(closes, 0, total)]
+        for l in range(L):
+            Sf[l].copy_(S_init)
+        for (a, b, g) in fplan:
+            if a < Wu:
+                g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fevs = []
+        for (a, b, g) in fplan:
+            if a >= Wu:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.replay()
+                e1.record()
+                fevs.append((a, b, e0, e1))
+        torch.cuda.synchronize()
+        fwall = time.perf_counter() - t0
+        fus = sum(e0.elapsed_time(e1) * 1e3 for (_, _, e0, e1) in fevs)
+        fn = sum((b - a) * L for (a, b, _, _) in fevs)
+        fbytes = fn * BH * bm.fp32_step_bytes(D, wl.kda, wl.act_bf16)
+        res.update(fp32_wall=fwall, fp32_us=fus / fn, fp32_gbs=fbytes / (fus * 1e-6) / 1e9)
+    return res
+
+
+def cpu_baseline(wl, bits, sample):
+    """The fp64 oracle (plain definition) on a bounded sample of the same workload."""
+    import numpy as np
+
+    from linear_attention_recurrent_kda_amd import workloads as wk
+    from oracle import leapquant_oracle as lq
+
+    n_seq, n_steps = (int(x) for x in sample.split("x"))
+    seqs = list(range(n_seq))
+    raw = wk.TokenStream(wl, seqs).next(n_steps)
+    toks = [{k: raw[k][t].reshape((-1,) + raw[k].shape[3:]).astype(np.float64)
+             for k in ("q", "k", "v", "g", "beta")} for t in range(n_steps)]
+    S0 = wk.initial_states(wl, seqs).reshape(-1, wl.d_k, wl.d_v).astype(np.float64)
+    N = S0.shape[0]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    t0 = time.perf_counter()
+    lq.run_dense(S0, toks, np.repeat(wk.window_lengths(wl)[seqs], wl.heads),
+                 np.repeat(wk.window_offsets(wl)[seqs], wl.heads), r=wl.n_comp, T=wl.power_iters,
+                 bits=bits, smoothing=wl.smoothing)
+    dt = time.perf_counter() - t0
+    return dict(value=N * n_steps / dt, unit="head-tokens/s", cores=threads, kind="oracle",
+                sample=f"{n_seq} sequences x {wl.heads} heads x {n_steps} tokens of the same workload "
+                       f"(initial encode + {n_steps // wl.window} window closes), numpy fp64, "
+                       f"{dt:.1f} s; BLAS threads {threads}, {len(os.sched_getaffinity(0))} cores visible")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the decode path has no cross-GPU exchange (heads and "
+              f"sequences shard with no communication), so --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        sys.exit(2)
+    from linear_attention_recurrent_kda_amd import workloads as wk
+
+    wl = wk.WORKLOADS[args.workload]
+    bits = wl.bits if args.bits is None else args.bits
+    r = run_gpu(args, wl, bits)
+    value = r["head_tokens"] / r["wall"]
+    line = {
+        "metric": "decode head-tokens/s + achieved HBM GB/s (int8 LeapQuant vs FP32 state)",
+        "value": round(value, 1),
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall"] * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {'KDA' if wl.kda else 'GDN'} decode, {wl.batch} sequences x "
+                        f"{wl.heads} heads, d_k=d_v={wl.d_k}, W={wl.window if not wl.mixed_window else '16/32'}, "
+                        f"r={wl.n_comp}, int{bits} state, {'bf16' if wl.act_bf16 else 'fp32'} q/k/v; "
+                        f"{args.layers} layers' state sets advanced per step",
+            "batch": wl.batch, "heads": wl.heads, "d_k": wl.d_k, "d_v": wl.d_v, "window": wl.window,
+            "n_comp": wl.n_comp, "state_bits": bits, "layers": args.layers,
+            "state_mb_per_layer": round(r["state_mb"], 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(r["dec_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["dec_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "decode_step_kernel",
+            "avg_launch_us": round(r["dec_us"], 3),
+            "bytes_per_launch": round(r["dec_bytes"] / max(r["n_dec"], 1)),
+        },
+        "window_close": {"avg_launch_us": round(r["close_us"], 3), "launches": r["n_close"],
+                         "bytes_per_launch": round(r["close_bytes"] / max(r["n_close"], 1))},
+        "hbm_gbs_all_in": round((r["dec_bytes"] + r["close_bytes"]) / r["wall"] / 1e9, 1),
+    }
+    if "fp32_us" in r:
+        fval = r["head_tokens"] / r["fp32_wall"]
+        line["fp32_baseline"] = {"value": round(fval, 1), "unit": "head-tokens/s",
+                                 "avg_launch_us": round(r["fp32_us"], 3),
+                                 "achieved_gbs": round(r["fp32_gbs"], 1)}
+        line["speedup_vs_fp32"] = round(value / fval, 3)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, bits, args.cpu_sample)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -225,3 +225,36 @@ class TokenStream:
         self.t += n
         return out
 
+
+
+def device_tokens(wl: Workload, steps: int, seed: int = 0, device="cuda"):
+    """Token inputs for throughput runs, drawn on the device with torch's seeded
+    generator: the same distributions as TokenStream (a different random
+    stream), laid out [steps][B*H][...] exactly as the decode kernels read one
+    step. Values are never compared with the oracle; parity runs use
+    TokenStream."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1_000_003 * wl.config_id + seed)
+    BH, dk, dv = wl.batch * wl.heads, wl.d_k, wl.d_v
+    f32 = dict(device=device, dtype=torch.float32, generator=gen)
+
+    def unit(x):
+        return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+
+    q = unit(torch.randn((steps, BH, dk), **f32))
+    k = unit(torch.randn((steps, BH, dk), **f32))
+    v = torch.randn((steps, BH, dv), **f32)
+    if wl.kda:
+        lam = torch.from_numpy(kda_lambda(wl)).to(device)               # [H][d_k]
+        lam = lam.repeat(wl.batch, 1)                                    # [B*H][d_k]
+        g = -torch.nn.functional.softplus(torch.randn((steps, BH, dk), **f32)) * lam
+    elif wl.decay == "uniform":
+        g = torch.log(0.9 + 0.1 * torch.rand((steps, BH), **f32))
+    else:
+        g = -torch.nn.functional.softplus(torch.randn((steps, BH), **f32)) * wl.decay_scale
+    beta = torch.sigmoid(torch.randn((steps, BH), **f32))
+    if wl.act_bf16:
+        q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), g=g.contiguous(), beta=beta.contiguous())
