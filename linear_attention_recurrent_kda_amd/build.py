@@ -54,6 +54,12 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    # every kernel launch stub must resolve: a host pass that silently drops a
+    # kernel instantiation leaves an undefined symbol that only dlopen reports
+    undefined = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+    stubs = [ln for ln in undefined.splitlines() if "__device_stub__" in ln]
+    if stubs:
+        raise RuntimeError("kernel launch stubs missing from the host pass:\n" + "\n".join(stubs))
     os.replace(tmp, LIB)
     if verbose:
         if res.stderr.strip():
