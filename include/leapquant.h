@@ -12,11 +12,14 @@
  *
  * Per (sequence b, head h) -- a "head" below -- the recurrent state
  * S in R^{d_k x d_v} (row i = key channel, column j = value channel) is held as
- *   S_hat_0 = sum_l comp_k[l] comp_u[l]^T + diag(s) C diag(c)
- * (r fp32 rank-one compensators plus a symmetric int8/int4 residual C with
+ * a window-start residual diag(s) C diag(c) (symmetric int8/int4 codes C with
  * per-key-row smoothing scales s and per-value-column scales c), fixed for a
- * window, plus an fp32 buffer of the window's token updates (k_m, u_m, G_m),
- * G_m = cumulative log-decay since the window start.
+ * window, plus a list of fp32 rank-one entries (k_e, u_e, G_e):
+ *   S = exp(G) (.) diag(s) C diag(c) + sum_e exp(G - G_e) (.) k_e u_e^T
+ * where G is the cumulative log-decay since the window start and (.) scales
+ * key rows. The first r entries are the compensator tokens (unit keys, G_e = 0:
+ * they sit at window position 0 and share the update path of real tokens);
+ * the next n are the window's buffered tokens, G_e = G at that token.
  *
  * Conventions for every entry point:
  *  - Every pointer is a DEVICE pointer unless marked (host). The caller
@@ -31,8 +34,9 @@
  *  - batch * heads == 0 is a valid empty call: it returns LQ_OK and enqueues
  *    nothing.
  *  - Layouts are dense and row-major in the order written; "head index"
- *    bh = b * heads + h. Every float buffer must be 16-byte aligned, codes
- *    16-byte aligned (LQ_ERR_ALIGN otherwise).
+ *    bh = b * heads + h. State buffers, dense states and o must be 16-byte
+ *    aligned; q, k, v 16-byte (fp32) or 8-byte (bf16); g, beta, buf_len, err
+ *    and close lists 4-byte (LQ_ERR_ALIGN otherwise).
  *  - Supported shapes (build-time limit): d_k == d_v in {32, 64, 128}.
  */
 #ifndef LEAPQUANT_H
@@ -77,7 +81,9 @@ typedef struct lq_dims {
   int32_t power_iters;       /* T power iterations per compensator, 1..64 */
 } lq_dims;
 
-/* The LeapQuant state of all B*H heads (device buffers owned by the caller). */
+/* The LeapQuant state of all B*H heads (device buffers owned by the caller).
+   Entry arrays hold r + w_max entries per head: entries 0..r-1 are the
+   compensators, entries r..r+n-1 the buffered tokens (n = buf_len). */
 typedef struct lq_state {
   void* codes;       /* int8 [B*H][d_v][d_k] two's complement, or int4 packed
                         [B*H][d_v][d_k/2] with key channel 2m in the low nibble
@@ -85,20 +91,18 @@ typedef struct lq_state {
                         Q = 127 (int8) or 7 (int4) */
   float* row_scale;  /* s [B*H][d_k] key-row smoothing scales */
   float* col_scale;  /* c [B*H][d_v] value-column scales */
-  float* comp_k;     /* [B*H][r][d_k] unit compensator keys (may be NULL if r == 0) */
-  float* comp_u;     /* [B*H][r][d_v] compensator values (may be NULL if r == 0) */
-  float* buf_k;      /* [B*H][w_max][d_k] buffered keys of the current window */
-  float* buf_u;      /* [B*H][w_max][d_v] buffered deltas u_m */
-  float* buf_g;      /* [B*H][w_max] (GDN) or [B*H][w_max][d_k] (KDA): cumulative
-                        log-decay G_m since the window start */
-  int32_t* buf_len;  /* [B*H] entries buffered per head */
+  float* ent_k;      /* [B*H][r + w_max][d_k] entry keys (compensator keys are unit vectors) */
+  float* ent_u;      /* [B*H][r + w_max][d_v] entry values u_e */
+  float* ent_g;      /* [B*H][r + w_max] (GDN) or [B*H][r + w_max][d_k] (KDA): G_e, the
+                        cumulative log-decay since the window start (0 for compensators) */
+  int32_t* buf_len;  /* [B*H] buffered tokens n per head */
   int32_t* err;      /* [1] device error word (LQ_DEVERR_* bits), may be NULL */
 } lq_state;
 
 /* Number of device buffers in lq_state whose sizes lq_state_sizes reports,
-   in the field order above: codes, row_scale, col_scale, comp_k, comp_u,
-   buf_k, buf_u, buf_g, buf_len, err. */
-#define LQ_STATE_NBUF 10
+   in the field order above: codes, row_scale, col_scale, ent_k, ent_u,
+   ent_g, buf_len, err. */
+#define LQ_STATE_NBUF 8
 
 /* Host-only helper: bytes needed for each lq_state buffer (err: 4 bytes).
    bytes_out (host) receives LQ_STATE_NBUF sizes. Validates dims. */
@@ -106,9 +110,9 @@ int lq_state_sizes(const lq_dims* dims, size_t* bytes_out);
 
 /* Encode fp32 dense states into LeapQuant form: compensator extraction by a
    T-step power method with deflation (start vectors from SplitMix64), key-row
-   smoothing, symmetric quantisation with per-value-column scales; empties
-   every buffer (buf_len = 0). Same arithmetic as a window close on an empty
-   buffer. Sources: LeapQuant abstract (compensator tokens, smoothing) and the
+   smoothing, symmetric quantisation with per-value-column scales; writes the
+   compensators as entries 0..r-1 and empties every buffer (buf_len = 0).
+   Same arithmetic as a window close with no entries. Sources: LeapQuant abstract (compensator tokens, smoothing) and the
    wink.run article's compensator and smoothing paragraphs.
    S: fp32 [B*H][d_v][d_k] (element (j, i) = S[i][j], i.e. S transposed).
    dbg_residual: NULL, or fp32 [B*H][d_v][d_k] receiving the residual after
@@ -118,10 +122,11 @@ int leapquant_encode(const lq_dims* dims, const float* S, const lq_state* st,
 
 /* One decode token for every head (per-window quantization: the low-bit state
    stays fixed and the token's update is buffered in fp32). Per head, with
-   G_t = G_{t-1} + g_t (G_{t-1} from the last buffered entry, 0 if empty):
-     y^x = Shat_0^T (exp(G_t) (.) x) + sum_m u_m (k_m . (exp(G_t - G_m) (.) x)),
+   G_t = G_{t-1} + g_t (G_{t-1} = G of the last entry, 0 if there is none):
+     y^x = c (.) C^T (s (.) exp(G_t) (.) x) + sum_e u_e (k_e . (exp(G_t - G_e) (.) x)),
      u_t = beta_t (v_t - y^k),  o_t = y^q + (k_t . q_t) u_t,
-   then appends (k_t, u_t, G_t) to the buffer and increments buf_len.
+   with entries e = 0..r+n-1 of the head (compensators included), then appends
+   (k_t, u_t, G_t) as entry r+n and increments buf_len.
    q, k: [B][H][d_k]; v: [B][H][d_v] (fp32 or bf16 per act_dtype);
    g: fp32 [B][H] (GDN) or [B][H][d_k] (KDA), the log-decay (alpha = exp(g));
    beta: fp32 [B][H]; o: fp32 [B][H][d_v] (output).
@@ -132,9 +137,10 @@ int leapquant_decode_step(const lq_dims* dims, const lq_state* st, const void* q
                           const void* v, const float* g, const float* beta, float* o,
                           void* stream);
 
-/* Window close for a list of sequences (all heads of each): fold the buffer
-   into the dense state S = exp(G_n) (.) Shat_0 + sum_m exp(G_n - G_m) (.) k_m u_m^T,
-   re-extract the compensators, re-smooth, requantise, and empty the buffer.
+/* Window close for a list of sequences (all heads of each): fold the entries
+   into the dense state S = exp(G_n) (.) diag(s) C diag(c) + sum_e exp(G_n - G_e) (.) k_e u_e^T
+   (G_n = G of the last entry), re-extract the compensators into entries
+   0..r-1, re-smooth, requantise, and empty the buffer (buf_len = 0).
    A partly filled buffer is legal (a partial window). Sources: LeapQuant
    abstract (quantize once at the window end; compensators and smoothing).
    seq_ids: int32 [n_seq] distinct sequence ids in [0, B), or NULL for all B
@@ -155,8 +161,9 @@ int gdn_decode_fp32_baseline(const lq_dims* dims, float* S, const void* q, const
                              const void* v, const float* g, const float* beta, float* o,
                              void* stream);
 
-/* Dense window-start state Shat_0 = sum_l comp_k comp_u^T + diag(s) C diag(c)
-   of every head into S_out: fp32 [B*H][d_v][d_k] (transposed). Test helper. */
+/* Dense window-start state Shat_0 = sum_{e<r} k_e u_e^T + diag(s) C diag(c)
+   (compensators plus residual) of every head into S_out: fp32
+   [B*H][d_v][d_k] (transposed). Test helper. */
 int leapquant_dequantize(const lq_dims* dims, const lq_state* st, float* S_out, void* stream);
 
 /* Host-only: sequences whose window ends with decode token `step` (0-based),

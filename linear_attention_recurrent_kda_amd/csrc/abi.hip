@@ -30,17 +30,15 @@ int check_dims(const lq_dims* d, bool method) {
   return LQ_OK;
 }
 
-// buffers: 0 = codes/scales/compensators only, 1 = + buf_len, 2 = + whole buffer
+// buffers: 0 = codes/scales/entries, 1 = + buf_len
 int check_state(const lq_dims* d, const lq_state* st, int buffers) {
   if (!st) return LQ_ERR_NULL;
   if (!st->codes || !st->row_scale || !st->col_scale) return LQ_ERR_NULL;
-  if (d->n_comp > 0 && (!st->comp_k || !st->comp_u)) return LQ_ERR_NULL;
+  if (!st->ent_k || !st->ent_u || !st->ent_g) return LQ_ERR_NULL;
   if (buffers >= 1 && !st->buf_len) return LQ_ERR_NULL;
-  if (buffers >= 2 && (!st->buf_k || !st->buf_u || !st->buf_g)) return LQ_ERR_NULL;
-  const void* a16[] = {st->codes, st->row_scale, st->col_scale, st->comp_k, st->comp_u,
-                       st->buf_k, st->buf_u, st->buf_g};
+  const void* a16[] = {st->codes, st->row_scale, st->col_scale, st->ent_k, st->ent_u, st->ent_g};
   for (const void* p : a16)
-    if (p && !aligned(p, 16)) return LQ_ERR_ALIGN;
+    if (!aligned(p, 16)) return LQ_ERR_ALIGN;
   if ((st->buf_len && !aligned(st->buf_len, 4)) || (st->err && !aligned(st->err, 4))) return LQ_ERR_ALIGN;
   return LQ_OK;
 }
@@ -48,9 +46,10 @@ int check_state(const lq_dims* d, const lq_state* st, int buffers) {
 int check_acts(const lq_dims* d, const void* q, const void* k, const void* v, const float* g,
                const float* beta, const float* o) {
   if (!q || !k || !v || !g || !beta || !o) return LQ_ERR_NULL;
-  const uintptr_t ea = d->act_dtype == LQ_ACT_BF16 ? 2 : 4;
+  // value rows and outputs move four channels per access
+  const uintptr_t ea = d->act_dtype == LQ_ACT_BF16 ? 8 : 16;
   if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, ea)) return LQ_ERR_ALIGN;
-  if (!aligned(g, 4) || !aligned(beta, 4) || !aligned(o, 4)) return LQ_ERR_ALIGN;
+  if (!aligned(g, 4) || !aligned(beta, 4) || !aligned(o, 16)) return LQ_ERR_ALIGN;
   return LQ_OK;
 }
 
@@ -61,11 +60,9 @@ lq::StepArgs step_args(const lq_dims* d, const lq_state* st) {
   a.codes = st->codes;
   a.s = st->row_scale;
   a.c = st->col_scale;
-  a.ck = st->comp_k;
-  a.cu = st->comp_u;
-  a.bk = st->buf_k;
-  a.bu = st->buf_u;
-  a.bg = st->buf_g;
+  a.ek = st->ent_k;
+  a.eu = st->ent_u;
+  a.eg = st->ent_g;
   a.blen = st->buf_len;
   a.err = st->err;
   a.r = d->n_comp;
@@ -78,11 +75,9 @@ lq::CloseArgs close_args(const lq_dims* d, const lq_state* st) {
   a.codes = st->codes;
   a.s = st->row_scale;
   a.c = st->col_scale;
-  a.ck = st->comp_k;
-  a.cu = st->comp_u;
-  a.bk = st->buf_k;
-  a.bu = st->buf_u;
-  a.bg = st->buf_g;
+  a.ek = st->ent_k;
+  a.eu = st->ent_u;
+  a.eg = st->ent_g;
   a.blen = st->buf_len;
   a.err = st->err;
   a.batch = d->batch;
@@ -105,17 +100,15 @@ int lq_state_sizes(const lq_dims* d, size_t* out) {
   if (rc) return rc;
   if (!out) return LQ_ERR_NULL;
   const size_t BH = size_t(d->batch) * size_t(d->heads), D = size_t(d->d_k);
-  const size_t W = size_t(d->w_max), r = size_t(d->n_comp);
+  const size_t NE = size_t(d->w_max) + size_t(d->n_comp);  // entries per head
   out[0] = BH * D * D * size_t(d->bits) / 8;
   out[1] = BH * D * 4;
   out[2] = BH * D * 4;
-  out[3] = BH * r * D * 4;
-  out[4] = BH * r * D * 4;
-  out[5] = BH * W * D * 4;
-  out[6] = BH * W * D * 4;
-  out[7] = BH * W * (d->decay_per_channel ? D : 1) * 4;
-  out[8] = BH * 4;
-  out[9] = 4;
+  out[3] = BH * NE * D * 4;
+  out[4] = BH * NE * D * 4;
+  out[5] = BH * NE * (d->decay_per_channel ? D : 1) * 4;
+  out[6] = BH * 4;
+  out[7] = 4;
   return LQ_OK;
 }
 
@@ -137,7 +130,7 @@ int leapquant_decode_step(const lq_dims* d, const lq_state* st, const void* q, c
   int rc = check_dims(d, true);
   if (rc) return rc;
   if (empty(d)) return LQ_OK;
-  if ((rc = check_state(d, st, 2))) return rc;
+  if ((rc = check_state(d, st, 1))) return rc;
   if ((rc = check_acts(d, q, k, v, g, beta, o))) return rc;
   lq::StepArgs a = step_args(d, st);
   a.q = q;
@@ -155,7 +148,7 @@ int leapquant_window_close(const lq_dims* d, const lq_state* st, const int32_t* 
   if (rc) return rc;
   if (seq_ids && (n_seq < 0 || n_seq > d->batch)) return LQ_ERR_CONFIG;
   if (empty(d) || (seq_ids && n_seq == 0)) return LQ_OK;
-  if ((rc = check_state(d, st, 2))) return rc;
+  if ((rc = check_state(d, st, 1))) return rc;
   if (dbg && !aligned(dbg, 16)) return LQ_ERR_ALIGN;
   if (seq_ids && !aligned(seq_ids, 4)) return LQ_ERR_ALIGN;
   lq::CloseArgs a = close_args(d, st);
@@ -183,7 +176,7 @@ int leapquant_dequantize(const lq_dims* d, const lq_state* st, float* S_out, voi
   if (empty(d)) return LQ_OK;
   if ((rc = check_state(d, st, 0))) return rc;
   if (!S_out) return LQ_ERR_NULL;
-  if (!aligned(S_out, 4)) return LQ_ERR_ALIGN;
+  if (!aligned(S_out, 16)) return LQ_ERR_ALIGN;
   return launched(lq::launch_dequantize(*d, *st, S_out, static_cast<hipStream_t>(stream)));
 }
 

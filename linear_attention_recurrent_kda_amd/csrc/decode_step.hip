@@ -32,14 +32,19 @@ constexpr int MAX_COMP = 8;
 constexpr int MAX_WMAX = 64;
 constexpr int MAX_ROWS = MAX_COMP + MAX_WMAX + 1;  // compensators, buffer entries, the k.q row
 
-__device__ __forceinline__ void lds16(const float* p, float (&x)[16]) {
+// N consecutive fp32 values (N in 2, 4, 8) from a 4N-byte aligned address
+// (global or LDS).
+template <int N>
+__device__ __forceinline__ void loadN(const float* p, float (&x)[N]) {
+  if constexpr (N == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    x[0] = t.x, x[1] = t.y;
+  } else {
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float4 t = reinterpret_cast<const float4*>(p)[w];
-    x[4 * w] = t.x;
-    x[4 * w + 1] = t.y;
-    x[4 * w + 2] = t.z;
-    x[4 * w + 3] = t.w;
+    for (int w = 0; w < N / 4; ++w) {
+      const float4 t = reinterpret_cast<const float4*>(p)[w];
+      x[4 * w] = t.x, x[4 * w + 1] = t.y, x[4 * w + 2] = t.z, x[4 * w + 3] = t.w;
+    }
   }
 }
 
@@ -52,11 +57,13 @@ struct StepShape {
   static constexpr int RB = D / 16;               // 16-column MFMA row blocks of the code matrix
   static constexpr int RBW = RB / NW;             // row blocks per wave
   static constexpr int KB = (D + 63) / 64;        // 64-channel MFMA k blocks
-  static constexpr int LPC = D / 16;              // lanes per key row in the key-side dots
-  static constexpr int NG = NT / LPC;             // key-row lane groups
-  static constexpr int NH = NT / D;               // threads sharing one value column's sums
-  static constexpr int KPF = KDA ? 1 : 2;         // key rows per group prefetched into registers
-  static constexpr int PF = 24 / NH;              // value-row entries loaded per thread
+  static constexpr int CPL = D / 16;              // key channels per lane in the key-side dots
+  static constexpr int NG = NT / 16;              // key-row lane groups (16 lanes per row)
+  static constexpr int NQ = D / 4;                // value-column quads (value sums, outputs)
+  static constexpr int EP = NT / NQ;              // entry phases sharing one quad
+  static constexpr int PRE = 24;                  // entries whose rows are prefetched into registers
+  static constexpr int KPF = PRE / NG;            // key rows per lane group prefetched
+  static constexpr int PFE = PRE / EP;            // value rows per thread prefetched
 };
 
 // Code bytes one lane feeds to one MFMA: 16 key channels of one value column.
@@ -86,102 +93,107 @@ __device__ __forceinline__ int chan_pos(int c) {
   else return (c & 1) ? 8 + (c >> 1) : (c >> 1);
 }
 
+template <bool BF16>
+__device__ __forceinline__ float4 load_act4(const void* p, size_t idx) {  // idx multiple of 4
+  if constexpr (BF16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + idx);
+    return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+  } else {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
+  }
+}
+
 template <int D, int BITS, bool KDA, bool BF16>
 __global__ void __launch_bounds__((StepShape<D, KDA>::NT)) decode_step_kernel(StepArgs a) {
   using SS = StepShape<D, KDA>;
-  constexpr int NT = SS::NT, NW = SS::NW, RBW = SS::RBW, KB = SS::KB, LPC = SS::LPC, NG = SS::NG;
-  constexpr int NH = SS::NH, KPF = SS::KPF, PF = SS::PF;
+  constexpr int NT = SS::NT, NW = SS::NW, RBW = SS::RBW, KB = SS::KB, CPL = SS::CPL, NG = SS::NG;
+  constexpr int KPF = SS::KPF, NQ = SS::NQ, EP = SS::EP, PFE = SS::PFE;
   constexpr int CB = D * BITS / 8;  // code bytes per value column
+  constexpr float L2E = 1.4426950408889634f;
   using CL = CodeLoad<BITS>;
   using CT = typename CL::T;
 
-  __shared__ __align__(16) float s_x[2][D];                // x for x = k, q
-  __shared__ __align__(16) float s_G[KDA ? D : 4];         // KDA: G_t per key channel
-  __shared__ __align__(16) int8_t s_B[KB][16][64];         // MFMA B operand: z limbs
-  __shared__ float s_c[D];                                 // value-column scales
-  __shared__ float s_y[2][D];                              // code readout
-  __shared__ float s_p[NH > 1 ? 2 : 1][D];                 // value-side partials of the other part
-  __shared__ float s_kap[2][MAX_ROWS];                     // kappa^k, kappa^q per entry
-  __shared__ float s_red[3][NW];                           // per-wave k.q and max |z^x|
+  __shared__ __align__(16) float s_x[2][D];         // x for x = k, q
+  __shared__ __align__(16) float s_G[KDA ? D : 4];  // KDA: G_t per key channel
+  __shared__ __align__(16) int8_t s_B[KB][16][64];  // MFMA B operand: z limbs
+  __shared__ __align__(16) float s_c[D];            // value-column scales
+  __shared__ __align__(16) float s_y[2][D];         // code readout
+  __shared__ __align__(16) float s_vs[EP][2][D];    // value-side partial sums per entry phase
+  __shared__ float s_kap[2][MAX_ROWS];              // kappa^k, kappa^q per entry
+  __shared__ float s_red[3][NW];                    // per-wave k.q and max |z^x| (bits)
 
   const int bh = blockIdx.x;
+  const int n = a.blen[bh];  // first: every entry address depends on it
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int grp = t / LPC, li = t % LPC, i0 = li * 16;
-  const int r = a.r, w_max = a.w_max;
+  const int grp = t / 16, li = t % 16, i0 = li * CPL;
+  const int q4 = t % NQ, ph = t / NQ;  // value-column quad and entry phase
+  const bool chan = NT == D || t < D;  // thread owns key channel t
+  const int tc = chan ? t : 0;
+  const int r = a.r, NE = r + a.w_max;
   const size_t hD = size_t(bh) * D;
-  const size_t brow = size_t(bh) * w_max;  // first buffer row of this head
+  // this head's entry rows (per-lane offsets below stay 32-bit)
+  float* const ekh = a.ek + size_t(bh) * NE * D;
+  float* const euh = a.eu + size_t(bh) * NE * D;
+  float* const egh = a.eg + size_t(bh) * NE * (KDA ? D : 1);
 
-  const int n = a.blen[bh];
-  if (n >= w_max || n < 0) {  // precondition violated: leave the head untouched
-    if (t == 0 && a.err) atomicOr(a.err, n < 0 ? LQ_DEVERR_BAD_LEN : LQ_DEVERR_BUFFER_FULL);
-    return;
-  }
-  // entries e = 0..E-1: r compensators (window position 0, G = 0), then the
-  // n buffered tokens (G = G_m)
-  const int E = r + n;
-  auto key_row = [&](int e) -> const float* {
-    return e < r ? a.ck + (size_t(bh) * r + e) * D : a.bk + (brow + (e - r)) * D;
-  };
-
-  // (1) issue the head's loads in the order they are consumed: this group's
-  // key rows, per-channel inputs, residual codes. Loads return in order, so the
-  // key-side dots do not wait for the codes.
-  float kr[KPF][16], gr[KPF][16];
-#pragma unroll
-  for (int q = 0; q < KPF; ++q) {
-    const int e = grp + NG * q;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) kr[q][x] = gr[q][x] = 0.f;
-    if (e < E) {
-      load16(key_row(e) + i0, kr[q]);
-      if constexpr (KDA)
-        if (e >= r) load16(a.bg + (brow + (e - r)) * D + i0, gr[q]);
-    }
-  }
-  float Gm[KPF];
-#pragma unroll
-  for (int q = 0; q < KPF; ++q) {
-    const int e = grp + NG * q;
-    Gm[q] = (!KDA && e >= r && e < E) ? a.bg[brow + (e - r)] : 0.f;
-  }
-  float kx = 0.f, qx = 0.f, si = 0.f, vj = 0.f, gi = 0.f, Gp = 0.f, cc = 0.f;
-  if (t < D) {
-    kx = load_act<BF16>(a.k, hD + t);
-    qx = load_act<BF16>(a.q, hD + t);
-    si = a.s[hD + t];
-    vj = load_act<BF16>(a.v, hD + t);
-    cc = a.c[hD + t];
-    if constexpr (KDA) {
-      gi = a.g[hD + t];
-      Gp = n > 0 ? a.bg[(brow + n - 1) * D + t] : 0.f;
-    }
-  }
-  float G = 0.f;  // GDN: cumulative log-decay of this token since the window start
-  if constexpr (!KDA) G = (n > 0 ? a.bg[brow + n - 1] : 0.f) + a.g[bh];
-  const float beta = a.beta[bh];
-  // residual codes in MFMA A-operand order: lane -> value column 16*rb + lane%16,
-  // key channels 64*kb + 16*(lane/16) .. +16
+  // (1) loads that do not depend on the buffer length: residual codes in MFMA
+  // A-operand order (lane -> value column 16*rb + lane%16, key channels
+  // 64*kb + 16*(lane/16) .. +16), per-channel inputs, this thread's v quad
   CT cw[RBW][KB];
   {
     const int jl = lane & 15, il = 16 * (lane >> 4);
+    const uint8_t* base = static_cast<const uint8_t*>(a.codes) + hD * CB;
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int j = 16 * (wave * RBW + rb) + jl, i = 64 * kb + il;
-        if (i < D) cw[rb][kb] = *reinterpret_cast<const CT*>(static_cast<const uint8_t*>(a.codes) + hD * CB +
-                                                           size_t(j) * CB + i * BITS / 8);
+        if (i < D) cw[rb][kb] = *reinterpret_cast<const CT*>(base + j * CB + i * BITS / 8);
         else cw[rb][kb] = CT{};
       }
   }
+  float kx = load_act<BF16>(a.k, hD + tc), qx = load_act<BF16>(a.q, hD + tc);
+  const float si = a.s[hD + tc], cc = a.c[hD + tc];
+  float gi = 0.f;
+  if constexpr (KDA) gi = a.g[hD + tc];
+  if (!chan) kx = qx = 0.f;
+  const float4 v4 = load_act4<BF16>(a.v, hD + 4 * q4);
+  const float beta = a.beta[bh];
 
-  // (2) per key channel: z^x = s (.) exp(G_t) (.) x, the block max |z^x|, k_t . q_t
-  float zk = 0.f, zq = 0.f, Gi = 0.f;
-  if (t < D) {
-    Gi = KDA ? Gp + gi : G;
-    const float e = expf(Gi);
-    zk = si * (e * kx);
-    zq = si * (e * qx);
+  if (n >= a.w_max || n < 0) {  // precondition violated: leave the head untouched
+    if (t == 0 && a.err) atomicOr(a.err, n < 0 ? LQ_DEVERR_BAD_LEN : LQ_DEVERR_BUFFER_FULL);
+    return;
+  }
+  // entries e = 0..E-1: r compensators (window position 0, G = 0), then the n
+  // buffered tokens; loads of entries past E are clamped to entry E-1 (or 0)
+  const int E = r + n, elast = E > 0 ? E - 1 : 0;
+
+  // (2) entry loads: this group's key rows (and their G), this thread's value rows
+  float kr[KPF][CPL], gr[KDA ? KPF : 1][CPL], Gm[KPF];
+#pragma unroll
+  for (int k = 0; k < KPF; ++k) {
+    const int e = grp + NG * k, ec = e < elast ? e : elast;
+    loadN(ekh + ec * D + i0, kr[k]);
+    if constexpr (KDA) loadN(egh + ec * D + i0, gr[k]);  // zero rows for compensators
+    else Gm[k] = egh[ec];
+  }
+  float4 uv[PFE];
+#pragma unroll
+  for (int k = 0; k < PFE; ++k) {
+    const int e = ph + EP * k, ec = e < elast ? e : elast;
+    uv[k] = *reinterpret_cast<const float4*>(euh + ec * D + 4 * q4);
+  }
+  // G_{t-1}: G of the last entry (compensators carry 0), 0 with no entries
+  float Gp = 0.f;
+  if constexpr (KDA) Gp = E > 0 ? egh[(E - 1) * D + tc] : 0.f;
+  else Gp = E > 0 ? egh[E - 1] : 0.f;
+  const float G = KDA ? 0.f : Gp + a.g[bh];  // GDN: G_t
+
+  // (3) per key channel: z^x = s (.) exp(G_t) (.) x, block max |z^x|, k_t . q_t
+  const float Gi = KDA ? Gp + gi : G;
+  const float eG = exp_fast(Gi);
+  const float zk = si * (eG * kx), zq = si * (eG * qx);
+  if (chan) {
     s_x[0][t] = kx;
     s_x[1][t] = qx;
     if constexpr (KDA) s_G[t] = Gi;
@@ -189,28 +201,28 @@ __global__ void __launch_bounds__((StepShape<D, KDA>::NT)) decode_step_kernel(St
   }
   {
     const float kq = rows_sum(group_sum<16>(kx * qx));
-    const float mk = rows_max(group_max<16>(fabsf(zk)));
-    const float mq = rows_max(group_max<16>(fabsf(zq)));
+    const uint32_t mk = rows_umax(group_umax<16>(as_u(fabsf(zk))));
+    const uint32_t mq = rows_umax(group_umax<16>(as_u(fabsf(zq))));
     if (lane == 0) {
       s_red[0][wave] = kq;
-      s_red[1][wave] = mk;
-      s_red[2][wave] = mq;
+      s_red[1][wave] = as_f(mk);
+      s_red[2][wave] = as_f(mq);
     }
   }
   __syncthreads();
 
-  // (3) z^x as a 30-bit fixed-point integer with a power-of-two block scale,
+  // (4) z^x as a 30-bit fixed-point integer with a power-of-two block scale,
   // split into four signed 8-bit limbs: the MFMA B operand (columns 4x+l)
   float zscale[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    float m = 0.f;
+    uint32_t mb = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) m = fmaxf(m, s_red[1 + x][w]);
+    for (int w = 0; w < NW; ++w) mb = max(mb, as_u(s_red[1 + x][w]));
     int ex = 0;
-    frexpf(m, &ex);                 // m < 2^ex
+    frexpf(as_f(mb), &ex);             // max |z| < 2^ex
     zscale[x] = ldexpf(1.f, ex - 30);  // z = Z * zscale, |Z| < 2^30
-    if (t < D) {
+    if (chan) {
       const int Z = int(rintf(ldexpf(x == 0 ? zk : zq, 30 - ex)));
       const int l0 = int(int8_t(Z & 0xFF));
       const int z1 = (Z - l0) >> 8;
@@ -225,77 +237,62 @@ __global__ void __launch_bounds__((StepShape<D, KDA>::NT)) decode_step_kernel(St
       s_B[kb][4 * x + 3][pos] = int8_t(l3);
     }
   }
-  if constexpr (D < 64) {  // the upper half of the single k block is padding
-    for (int idx = t; idx < 16 * 64; idx += NT)
-      if ((idx & 63) >= D) s_B[0][idx >> 6][idx & 63] = 0;
-  }
+  // (D = 32: the A operand is zero past channel D, so the B operand's unwritten
+  // padding bytes never contribute)
 
-  // (4) key-side dots while the codes are still arriving:
-  //   kappa^x_e = sum_i k_e,i exp(G_t,i - G_e,i) x_i
+  // (5) key-side dots: kappa^x_e = sum_i k_e,i exp(G_t,i - G_e,i) x_i
   // (GDN: the decay ratio is one scalar exp(G_t - G_e) applied after the sum)
   {
-    float xk[16], xq[16], Gt[16];
-    lds16(&s_x[0][i0], xk);
-    lds16(&s_x[1][i0], xq);
-    if constexpr (KDA) lds16(&s_G[i0], Gt);
+    float xk[CPL], xq[CPL], Gt[CPL];
+    loadN(&s_x[0][i0], xk);
+    loadN(&s_x[1][i0], xq);
+    if constexpr (KDA) {
+      loadN(&s_G[i0], Gt);
+#pragma unroll
+      for (int x = 0; x < CPL; ++x) Gt[x] *= L2E;
+    }
     for (int e0 = 0; e0 < E; e0 += NG * KPF) {
 #pragma unroll
-      for (int q = 0; q < KPF; ++q) {
-        const int e = e0 + grp + NG * q;
-        float row[16], gm[16];
+      for (int k = 0; k < KPF; ++k) {
+        const int e = e0 + grp + NG * k;
+        float row[CPL], gm[CPL], gsc = Gm[k];
         if (e0 == 0) {
 #pragma unroll
-          for (int x = 0; x < 16; ++x) row[x] = kr[q][x], gm[x] = gr[q][x];
-        } else {
-#pragma unroll
-          for (int x = 0; x < 16; ++x) row[x] = gm[x] = 0.f;
-          if (e < E) {
-            load16(key_row(e) + i0, row);
-            if constexpr (KDA)
-              if (e >= r) load16(a.bg + (brow + (e - r)) * D + i0, gm);
+          for (int x = 0; x < CPL; ++x) {
+            row[x] = kr[k][x];
+            if constexpr (KDA) gm[x] = gr[k][x];
           }
+        } else {  // entries beyond the prefetched ones (long windows)
+          const int ec = e < elast ? e : elast;
+          loadN(ekh + ec * D + i0, row);
+          if constexpr (KDA) loadN(egh + ec * D + i0, gm);
+          else gsc = egh[ec];
         }
         float dk = 0.f, dq = 0.f;
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
+        for (int x = 0; x < CPL; ++x) {
           float f = row[x];
-          if constexpr (KDA) f *= expf(Gt[x] - gm[x]);
+          if constexpr (KDA) f *= __builtin_amdgcn_exp2f(fmaf(gm[x], -L2E, Gt[x]));
           dk = fmaf(f, xk[x], dk);
           dq = fmaf(f, xq[x], dq);
         }
-        dk = group_sum<LPC>(dk);
-        dq = group_sum<LPC>(dq);
+        dk = group_sum<16>(dk);
+        dq = group_sum<16>(dq);
+        if constexpr (!KDA) {
+          const float f = exp_fast(G - gsc);
+          dk *= f;
+          dq *= f;
+        }
         if (li == 0 && e < E) {
-          if constexpr (!KDA) {
-            const float gme = e0 == 0 ? Gm[q] : (e >= r ? a.bg[brow + (e - r)] : 0.f);
-            const float f = expf(G - gme);
-            dk *= f;
-            dq *= f;
-          }
           s_kap[0][e] = dk;
           s_kap[1][e] = dq;
         }
       }
     }
   }
-
-  // value rows for the sums after the readout (clamped, so every load is valid)
-  const int j = t % D, part = t / D;
-  auto val_row = [&](int e) -> float {  // entry e in 0..E-1
-    return e < r ? a.cu[(size_t(bh) * r + e) * D + j] : a.bu[(brow + (e - r)) * D + j];
-  };
-  float uv[PF];
-  {
-    const int elast = E > 0 ? E - 1 : 0;
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int e = part + NH * p;
-      uv[p] = E > 0 ? val_row(e < elast ? e : elast) : 0.f;
-    }
-  }
   __syncthreads();
 
-  // (5) residual readout on the matrix cores: for every value column j and
+  // (6) residual readout on the matrix cores: for every value column j and
   // x in {k, q}, sum_i C_ij Z^x_i exactly in int32, limb by limb; then
   // y^x_j = c_j * zscale_x * sum_l 256^l D[j][4x+l]
   {
@@ -321,51 +318,58 @@ __global__ void __launch_bounds__((StepShape<D, KDA>::NT)) decode_step_kernel(St
       }
     }
   }
+
+  // (7) value-side sums: sum_e u_e[j] kappa^x_e for this thread's four value
+  // columns over the entries of its phase (e = ph, ph + EP, ...)
+  {
+    float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+#pragma unroll
+    for (int k = 0; k < PFE; ++k) {
+      const int e = ph + EP * k;
+      if (e < E) {
+        const float ak = s_kap[0][e], aq = s_kap[1][e];
+        pk.x = fmaf(uv[k].x, ak, pk.x), pk.y = fmaf(uv[k].y, ak, pk.y);
+        pk.z = fmaf(uv[k].z, ak, pk.z), pk.w = fmaf(uv[k].w, ak, pk.w);
+        pq.x = fmaf(uv[k].x, aq, pq.x), pq.y = fmaf(uv[k].y, aq, pq.y);
+        pq.z = fmaf(uv[k].z, aq, pq.z), pq.w = fmaf(uv[k].w, aq, pq.w);
+      }
+    }
+    for (int e = ph + EP * PFE; e < E; e += EP) {
+      const float4 u = *reinterpret_cast<const float4*>(euh + e * D + 4 * q4);
+      const float ak = s_kap[0][e], aq = s_kap[1][e];
+      pk.x = fmaf(u.x, ak, pk.x), pk.y = fmaf(u.y, ak, pk.y), pk.z = fmaf(u.z, ak, pk.z), pk.w = fmaf(u.w, ak, pk.w);
+      pq.x = fmaf(u.x, aq, pq.x), pq.y = fmaf(u.y, aq, pq.y), pq.z = fmaf(u.z, aq, pq.z), pq.w = fmaf(u.w, aq, pq.w);
+    }
+    *reinterpret_cast<float4*>(&s_vs[ph][0][4 * q4]) = pk;
+    *reinterpret_cast<float4*>(&s_vs[ph][1][4 * q4]) = pq;
+  }
   __syncthreads();
 
-  // (6) value-side sums: y^x_j += sum_e U_e[j] kappa^x_e (entries split over
-  // the NH threads of a column)
-  float pk = 0.f, pq = 0.f;
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    const int e = part + NH * p;
-    if (e < E) {
-      pk = fmaf(uv[p], s_kap[0][e], pk);
-      pq = fmaf(uv[p], s_kap[1][e], pq);
-    }
-  }
-  for (int e = part + NH * PF; e < E; e += NH) {
-    const float u = val_row(e);
-    pk = fmaf(u, s_kap[0][e], pk);
-    pq = fmaf(u, s_kap[1][e], pq);
-  }
-  if constexpr (NH > 1) {
-    if (part == 1) {
-      s_p[0][j] = pk;
-      s_p[1][j] = pq;
-    }
-    __syncthreads();
-    if (part == 0) {
-      pk += s_p[0][j];
-      pq += s_p[1][j];
-    }
-  }
-
-  // (7) delta, output, append (k_t, u_t, G_t) to the window buffer
-  if (part == 0) {
+  // (8) delta, output, append (k_t, u_t, G_t) as entry E: one thread per
+  // value-column quad
+  if (t < NQ) {
     float kqs = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) kqs += s_red[0][w];
-    const float yk = s_y[0][j] + pk;
-    const float yq = s_y[1][j] + pq;
-    const float u = beta * (vj - yk);
-    const size_t slot = brow + n;
-    a.o[hD + j] = yq + kqs * u;
-    a.bu[slot * D + j] = u;
-    a.bk[slot * D + j] = s_x[0][j];
-    if constexpr (KDA) a.bg[slot * D + j] = s_G[j];
+    float4 yk = *reinterpret_cast<const float4*>(&s_y[0][4 * q4]);
+    float4 yq = *reinterpret_cast<const float4*>(&s_y[1][4 * q4]);
+#pragma unroll
+    for (int p = 0; p < EP; ++p) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&s_vs[p][0][4 * q4]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&s_vs[p][1][4 * q4]);
+      yk.x += a4.x, yk.y += a4.y, yk.z += a4.z, yk.w += a4.w;
+      yq.x += b4.x, yq.y += b4.y, yq.z += b4.z, yq.w += b4.w;
+    }
+    float4 u, o;
+    u.x = beta * (v4.x - yk.x), u.y = beta * (v4.y - yk.y), u.z = beta * (v4.z - yk.z), u.w = beta * (v4.w - yk.w);
+    o.x = fmaf(kqs, u.x, yq.x), o.y = fmaf(kqs, u.y, yq.y), o.z = fmaf(kqs, u.z, yq.z), o.w = fmaf(kqs, u.w, yq.w);
+    *reinterpret_cast<float4*>(a.o + hD + 4 * q4) = o;
+    *reinterpret_cast<float4*>(euh + E * D + 4 * q4) = u;
+    *reinterpret_cast<float4*>(ekh + E * D + 4 * q4) = *reinterpret_cast<const float4*>(&s_x[0][4 * q4]);
+    if constexpr (KDA)
+      *reinterpret_cast<float4*>(egh + E * D + 4 * q4) = *reinterpret_cast<const float4*>(&s_G[4 * q4]);
     if (t == 0) {
-      if constexpr (!KDA) a.bg[slot] = G;
+      if constexpr (!KDA) egh[E] = G;
       a.blen[bh] = n + 1;
     }
   }

@@ -86,11 +86,12 @@ __global__ void __launch_bounds__(2 * D) baseline_kernel(BaselineArgs a) {
   }
 }
 
-// Shat_0 = sum_l comp_k[l] comp_u[l]^T + diag(s) C diag(c), written [d_v][d_k].
+// Shat_0 = sum_{l<r} k_l u_l^T + diag(s) C diag(c) (compensator entries plus
+// residual), written [d_v][d_k].
 template <int D, int BITS>
-__global__ void __launch_bounds__(256) dequant_kernel(lq_state st, int r, float* out) {
+__global__ void __launch_bounds__(256) dequant_kernel(lq_state st, int r, int n_ent, float* out) {
   const int bh = blockIdx.x;
-  const size_t hD = size_t(bh) * D;
+  const size_t hD = size_t(bh) * D, erow = size_t(bh) * n_ent;
   for (int idx = threadIdx.x; idx < D * D; idx += 256) {
     const int j = idx / D, i = idx % D;
     int code;
@@ -102,8 +103,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(lq_state st, int r, float*
       code = int(nib ^ 0x8u) - 8;
     }
     float val = (st.row_scale[hD + i] * float(code)) * st.col_scale[hD + j];
-    for (int l = 0; l < r; ++l)
-      val = fmaf(st.comp_k[(size_t(bh) * r + l) * D + i], st.comp_u[(size_t(bh) * r + l) * D + j], val);
+    for (int l = 0; l < r; ++l) val = fmaf(st.ent_k[(erow + l) * D + i], st.ent_u[(erow + l) * D + j], val);
     out[(hD + j) * D + i] = val;
   }
 }
@@ -124,7 +124,7 @@ hipError_t launch_d(const lq_dims& d, const BaselineArgs& a, hipStream_t s) {
 template <int D, int BITS>
 hipError_t launch_dq(const lq_dims& d, const lq_state& st, float* out, hipStream_t stream) {
   hipLaunchKernelGGL((dequant_kernel<D, BITS>), dim3(d.batch * d.heads), dim3(256), 0, stream, st,
-                     d.n_comp, out);
+                     d.n_comp, d.n_comp + d.w_max, out);
   return hipGetLastError();
 }
 

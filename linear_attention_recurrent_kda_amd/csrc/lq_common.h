@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lq {
 
 __device__ __forceinline__ float as_f(uint32_t x) { return __uint_as_float(x); }
@@ -44,6 +46,31 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 16) x = fmaxf(x, dpp<DPP_MIRROR>(x));
   return x;
 }
+
+// Max over aligned groups of N lanes of a non-negative float's bit pattern
+// (for x >= 0 the fp32 order is the unsigned order of the bits).
+template <int N>
+__device__ __forceinline__ uint32_t group_umax(uint32_t x) {
+  auto d = [](uint32_t v, auto ctrl) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  if constexpr (N >= 2) x = max(x, d(x, std::integral_constant<int, DPP_QUAD_XOR1>{}));
+  if constexpr (N >= 4) x = max(x, d(x, std::integral_constant<int, DPP_QUAD_XOR2>{}));
+  if constexpr (N >= 8) x = max(x, d(x, std::integral_constant<int, DPP_HALF_MIRROR>{}));
+  if constexpr (N >= 16) x = max(x, d(x, std::integral_constant<int, DPP_MIRROR>{}));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t rows_umax(uint32_t x) {
+  auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(uint32_t(p[0]), uint32_t(p[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(uint32_t(q[0]), uint32_t(q[1]));
+}
+
+// exp(x) as 2^(x log2 e) on the transcendental unit (about 1 ulp of exp2,
+// plus the rounding of the product: relative error ~ |x| 2^-24).
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 // Sum / max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
 // with the gfx950 row-swap instructions. Every lane ends with the same value.

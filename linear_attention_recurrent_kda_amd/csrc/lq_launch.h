@@ -14,11 +14,9 @@ struct StepArgs {
   const void* codes;
   const float* s;
   const float* c;
-  const float* ck;
-  const float* cu;
-  float* bk;
-  float* bu;
-  float* bg;
+  float* ek;  // entry keys   [BH][r + w_max][D]
+  float* eu;  // entry values [BH][r + w_max][D]
+  float* eg;  // entry G      [BH][r + w_max] or [BH][r + w_max][D]
   int32_t* blen;
   int32_t* err;
   const void* q;
@@ -36,11 +34,9 @@ struct CloseArgs {
   void* codes;
   float* s;
   float* c;
-  float* ck;
-  float* cu;
-  const float* bk;
-  const float* bu;
-  const float* bg;
+  float* ek;
+  float* eu;
+  float* eg;
   int32_t* blen;
   int32_t* err;
   const int32_t* seq_ids;  // NULL: all sequences

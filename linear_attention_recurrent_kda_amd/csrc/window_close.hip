@@ -113,6 +113,7 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
   const size_t hD = size_t(bh) * D;
   const int i0 = ti * B, j0 = tj * B;
   const int r = a.r;
+  const size_t erow = size_t(bh) * (r + a.w_max);  // first entry row of this head
 
   // ---- the dense state block M[a][bb] = S[i0 + a][j0 + bb]
   float M[B][B];
@@ -125,13 +126,15 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
       for (int x = 0; x < B; ++x) M[x][bb] = col[x];
     }
   } else {
-    // fold: S = exp(G_n) (.) Shat_0 + sum_m exp(G_n - G_m) (.) k_m u_m^T
+    // fold: S = exp(G_n) (.) diag(s) C diag(c) + sum_e exp(G_n - G_e) (.) k_e u_e^T
+    // over the entries e < r + n (compensators carry G_e = 0); G_n is the G of
+    // the last entry (0 when there is none)
     const int n = a.blen[bh];
     if (n < 0 || n > a.w_max) {  // corrupted buffer length: leave the head untouched
       if (t == 0 && a.err) atomicOr(a.err, LQ_DEVERR_BAD_LEN);
       return;
     }
-    const size_t brow = size_t(bh) * a.w_max;
+    const int E = r + n;
     float si[B], cj[B];
     loadB<B>(a.s + hD + i0, si);
     loadB<B>(a.c + hD + j0, cj);
@@ -143,18 +146,9 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
 #pragma unroll
       for (int x = 0; x < B; ++x) M[x][bb] = (si[x] * float(code[x])) * cj[bb];
     }
-    for (int l = 0; l < r; ++l) {
-      float kh[B], uh[B];
-      loadB<B>(a.ck + (size_t(bh) * r + l) * D + i0, kh);
-      loadB<B>(a.cu + (size_t(bh) * r + l) * D + j0, uh);
-#pragma unroll
-      for (int x = 0; x < B; ++x)
-#pragma unroll
-        for (int bb = 0; bb < B; ++bb) M[x][bb] = fmaf(kh[x], uh[bb], M[x][bb]);
-    }
     if constexpr (KDA) {
       float Gn[B];
-      if (n > 0) loadB<B>(a.bg + (brow + n - 1) * D + i0, Gn);
+      if (E > 0) loadB<B>(a.eg + (erow + E - 1) * D + i0, Gn);
       else
 #pragma unroll
         for (int x = 0; x < B; ++x) Gn[x] = 0.f;
@@ -164,11 +158,11 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
 #pragma unroll
         for (int bb = 0; bb < B; ++bb) M[x][bb] *= e;
       }
-      for (int m = 0; m < n; ++m) {
+      for (int m = 0; m < E; ++m) {
         float km[B], um[B], gm[B];
-        loadB<B>(a.bk + (brow + m) * D + i0, km);
-        loadB<B>(a.bu + (brow + m) * D + j0, um);
-        loadB<B>(a.bg + (brow + m) * D + i0, gm);
+        loadB<B>(a.ek + (erow + m) * D + i0, km);
+        loadB<B>(a.eu + (erow + m) * D + j0, um);
+        loadB<B>(a.eg + (erow + m) * D + i0, gm);
 #pragma unroll
         for (int x = 0; x < B; ++x) {
           const float kf = expf(Gn[x] - gm[x]) * km[x];
@@ -177,17 +171,17 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
         }
       }
     } else {
-      const float Gn = n > 0 ? a.bg[brow + n - 1] : 0.f;
+      const float Gn = E > 0 ? a.eg[erow + E - 1] : 0.f;
       const float e = expf(Gn);
 #pragma unroll
       for (int x = 0; x < B; ++x)
 #pragma unroll
         for (int bb = 0; bb < B; ++bb) M[x][bb] *= e;
-      for (int m = 0; m < n; ++m) {
+      for (int m = 0; m < E; ++m) {
         float km[B], um[B];
-        loadB<B>(a.bk + (brow + m) * D + i0, km);
-        loadB<B>(a.bu + (brow + m) * D + j0, um);
-        const float f = expf(Gn - a.bg[brow + m]);
+        loadB<B>(a.ek + (erow + m) * D + i0, km);
+        loadB<B>(a.eu + (erow + m) * D + j0, um);
+        const float f = expf(Gn - a.eg[erow + m]);
 #pragma unroll
         for (int x = 0; x < B; ++x) {
           const float kf = f * km[x];
@@ -271,8 +265,19 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
 #pragma unroll
       for (int x = 0; x < B; ++x) kk[x] = w[x] = 0.f;
     }
-    if (tj == 0) storeB<B>(a.ck + (size_t(bh) * r + l) * D + i0, kk);
-    if (ti == 0) storeB<B>(a.cu + (size_t(bh) * r + l) * D + j0, w);
+    // compensator l is entry l: a unit key, its value, and G = 0 (window position 0)
+    if (tj == 0) storeB<B>(a.ek + (erow + l) * D + i0, kk);
+    if (ti == 0) storeB<B>(a.eu + (erow + l) * D + j0, w);
+    if constexpr (KDA) {
+      if (tj == 0) {
+        float z[B];
+#pragma unroll
+        for (int x = 0; x < B; ++x) z[x] = 0.f;
+        storeB<B>(a.eg + (erow + l) * D + i0, z);
+      }
+    } else if (t == 0) {
+      a.eg[erow + l] = 0.f;
+    }
 #pragma unroll
     for (int x = 0; x < B; ++x)
 #pragma unroll
@@ -346,7 +351,8 @@ hipError_t launch(const CloseArgs& a, int n_blocks, hipStream_t stream) {
 
 template <int D, int BITS>
 hipError_t launch_b(const lq_dims& d, const CloseArgs& a, int nb, hipStream_t s) {
-  if (a.S) return launch<D, BITS, false, true>(a, nb, s);
+  if (a.S)
+    return d.decay_per_channel ? launch<D, BITS, true, true>(a, nb, s) : launch<D, BITS, false, true>(a, nb, s);
   return d.decay_per_channel ? launch<D, BITS, true, false>(a, nb, s) : launch<D, BITS, false, false>(a, nb, s);
 }
 

@@ -21,9 +21,8 @@ LQ_OK = 0
 LQ_ERR_NULL, LQ_ERR_SHAPE, LQ_ERR_BITS, LQ_ERR_CONFIG, LQ_ERR_LAUNCH, LQ_ERR_ALIGN = -1, -2, -3, -4, -5, -6
 LQ_ACT_F32, LQ_ACT_BF16 = 0, 1
 LQ_DEVERR_BUFFER_FULL, LQ_DEVERR_BAD_SEQ, LQ_DEVERR_BAD_LEN = 1, 2, 4
-LQ_STATE_NBUF = 10
-STATE_FIELDS = ("codes", "row_scale", "col_scale", "comp_k", "comp_u", "buf_k", "buf_u", "buf_g",
-                "buf_len", "err")
+LQ_STATE_NBUF = 8
+STATE_FIELDS = ("codes", "row_scale", "col_scale", "ent_k", "ent_u", "ent_g", "buf_len", "err")
 
 EXPORTS = ("lq_state_sizes", "leapquant_encode", "leapquant_decode_step", "leapquant_window_close",
            "gdn_decode_fp32_baseline", "leapquant_dequantize", "lq_close_list", "lq_status_string")
@@ -143,11 +142,10 @@ class State:
         self.codes = torch.zeros((BH, D, D * dims.bits // 8), dtype=torch.int8, device=device)
         self.row_scale = torch.ones((BH, D), **f32)
         self.col_scale = torch.zeros((BH, D), **f32)
-        self.comp_k = torch.zeros((BH, max(r, 0), D), **f32)
-        self.comp_u = torch.zeros((BH, max(r, 0), D), **f32)
-        self.buf_k = torch.zeros((BH, W, D), **f32)
-        self.buf_u = torch.zeros((BH, W, D), **f32)
-        self.buf_g = torch.zeros((BH, W, D) if dims.kda else (BH, W), **f32)
+        # entries 0..r-1: compensators; r..r+W-1: buffered tokens
+        self.ent_k = torch.zeros((BH, r + W, D), **f32)
+        self.ent_u = torch.zeros((BH, r + W, D), **f32)
+        self.ent_g = torch.zeros((BH, r + W, D) if dims.kda else (BH, r + W), **f32)
         self.buf_len = torch.zeros((BH,), dtype=torch.int32, device=device)
         self.err = torch.zeros((1,), dtype=torch.int32, device=device)
         for name in STATE_FIELDS:
@@ -156,6 +154,27 @@ class State:
 
     def c(self) -> CState:
         return CState(*[_ptr(getattr(self, n)) for n in STATE_FIELDS])
+
+    # views of the entry arrays
+    @property
+    def comp_k(self) -> torch.Tensor:
+        return self.ent_k[:, :self.dims.n_comp]
+
+    @property
+    def comp_u(self) -> torch.Tensor:
+        return self.ent_u[:, :self.dims.n_comp]
+
+    @property
+    def buf_k(self) -> torch.Tensor:
+        return self.ent_k[:, self.dims.n_comp:]
+
+    @property
+    def buf_u(self) -> torch.Tensor:
+        return self.ent_u[:, self.dims.n_comp:]
+
+    @property
+    def buf_g(self) -> torch.Tensor:
+        return self.ent_g[:, self.dims.n_comp:]
 
     def nbytes(self) -> int:
         return sum(getattr(self, n).numel() * getattr(self, n).element_size() for n in STATE_FIELDS)

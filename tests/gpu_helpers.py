@@ -48,6 +48,9 @@ def download_state(st: lqk.State, dims: lqk.Dims) -> Dict[str, np.ndarray]:
     torch.cuda.synchronize()
     out = {n: getattr(st, n).cpu().numpy() for n in lqk.STATE_FIELDS}
     out["C"] = unpack_codes(out["codes"], dims.bits, dims.d)
+    r = dims.n_comp  # entries 0..r-1 are the compensators, the rest the token buffer
+    out["comp_k"], out["comp_u"], out["comp_g"] = out["ent_k"][:, :r], out["ent_u"][:, :r], out["ent_g"][:, :r]
+    out["buf_k"], out["buf_u"], out["buf_g"] = out["ent_k"][:, r:], out["ent_u"][:, r:], out["ent_g"][:, r:]
     return out
 
 
@@ -69,6 +72,7 @@ def upload_state(st: lqk.State, dims: lqk.Dims, enc: lq.Encoded, buf_k=None, buf
     if dims.n_comp:
         put(st.comp_k, enc.comp_k)
         put(st.comp_u, enc.comp_u)
+        st.ent_g[:, :dims.n_comp] = 0.0  # compensators sit at window position 0
     if buf_k is not None:
         put(st.buf_k, buf_k)
         put(st.buf_u, buf_u)
@@ -90,8 +94,8 @@ def overwrite_heads(st: lqk.State, dims: lqk.Dims, gpu_heads, enc: lq.Encoded) -
     st.row_scale[idx] = dev(np.asarray(enc.s, np.float32))
     st.col_scale[idx] = dev(np.asarray(enc.c, np.float32))
     if dims.n_comp:
-        st.comp_k[idx] = dev(np.asarray(enc.comp_k, np.float32))
-        st.comp_u[idx] = dev(np.asarray(enc.comp_u, np.float32))
+        st.ent_k[idx, :dims.n_comp] = dev(np.asarray(enc.comp_k, np.float32))
+        st.ent_u[idx, :dims.n_comp] = dev(np.asarray(enc.comp_u, np.float32))
 
 
 def run_gpu(wl: wk.Workload, steps: int, check_seqs: Sequence[int], bits=None, chunk: int = 16,

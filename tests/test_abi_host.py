@@ -76,16 +76,23 @@ def test_null_and_alignment_validation():
     d = dims()
     assert L.raw_call("leapquant_decode_step", None, None, None, None, None, None, None, None, None) == L.LQ_ERR_NULL
     assert step(d, state(codes=None)) == L.LQ_ERR_NULL
-    assert step(d, state(buf_k=None)) == L.LQ_ERR_NULL
+    for f in ("ent_k", "ent_u", "ent_g", "buf_len", "row_scale"):
+        assert step(d, state(**{f: None})) == L.LQ_ERR_NULL, f
     assert step(d, state(), q=None) == L.LQ_ERR_NULL
-    assert step(d, state(comp_k=None)) == L.LQ_ERR_NULL
     assert step(d, state(codes=FAKE + 4)) == L.LQ_ERR_ALIGN
-    assert step(d, state(buf_g=FAKE + 8)) == L.LQ_ERR_ALIGN
+    assert step(d, state(ent_g=FAKE + 8)) == L.LQ_ERR_ALIGN
+    assert step(d, state(ent_u=FAKE + 4)) == L.LQ_ERR_ALIGN
+    assert step(d, state(err=FAKE + 2)) == L.LQ_ERR_ALIGN
     assert step(d, state(), q=FAKE + 2) == L.LQ_ERR_ALIGN
+    assert step(d, state(), v=FAKE + 8) == L.LQ_ERR_ALIGN   # fp32 rows move in 16-byte pieces
+    assert step(d, state(), o=FAKE + 4) == L.LQ_ERR_ALIGN
+    assert step(d, state(), g=FAKE + 2) == L.LQ_ERR_ALIGN
     db = dims(act_dtype=1)
     assert step(db, state(), q=FAKE + 1) == L.LQ_ERR_ALIGN
-    # r == 0 does not need compensator buffers, but a misaligned buffer is still rejected
-    assert step(dims(n_comp=0), state(comp_k=None, comp_u=None, buf_u=FAKE + 4)) == L.LQ_ERR_ALIGN
+    assert step(db, state(), v=FAKE + 4) == L.LQ_ERR_ALIGN  # bf16 rows move in 8-byte pieces
+    # r == 0: the entry arrays hold only the token buffer, still required and aligned
+    assert step(dims(n_comp=0), state(ent_k=None)) == L.LQ_ERR_NULL
+    assert step(dims(n_comp=0), state(ent_u=FAKE + 4)) == L.LQ_ERR_ALIGN
     assert L.raw_call("gdn_decode_fp32_baseline", ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                       None) == L.LQ_ERR_NULL
     assert L.raw_call("gdn_decode_fp32_baseline", ctypes.byref(d), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE,
@@ -122,10 +129,13 @@ def test_empty_batch_is_a_no_op():
 def test_state_sizes():
     s = L.state_sizes(L.Dims(64, 32, 128, w_max=16, n_comp=4, bits=8))
     BH = 64 * 32
-    assert s["codes"] == BH * 128 * 128 and s["buf_g"] == BH * 16 * 4 and s["err"] == 4
-    assert s["comp_k"] == s["comp_u"] == BH * 4 * 128 * 4
+    assert s["codes"] == BH * 128 * 128 and s["ent_g"] == BH * (4 + 16) * 4 and s["err"] == 4
+    assert s["ent_k"] == s["ent_u"] == BH * (4 + 16) * 128 * 4
+    assert s["row_scale"] == s["col_scale"] == BH * 128 * 4 and s["buf_len"] == BH * 4
     s4 = L.state_sizes(L.Dims(128, 32, 128, w_max=16, n_comp=4, bits=4, kda=True))
-    assert s4["codes"] == 128 * 32 * 128 * 64 and s4["buf_g"] == 128 * 32 * 16 * 128 * 4
+    assert s4["codes"] == 128 * 32 * 128 * 64 and s4["ent_g"] == 128 * 32 * (4 + 16) * 128 * 4
+    s0 = L.state_sizes(L.Dims(2, 3, 32, w_max=1, n_comp=0))
+    assert s0["ent_k"] == 6 * 1 * 32 * 4
 
 
 def test_close_list_matches_schedule():

@@ -218,8 +218,10 @@ def test_close_codes_and_decomposition(name, bits, n_tok, close_seqs):
     closed[heads] = True
     assert np.all(post["buf_len"][closed] == 0) and np.all(post["buf_len"][~closed] == n_tok)
     # heads that were not closed are untouched
-    for f in ("codes", "row_scale", "col_scale", "comp_k", "comp_u", "buf_k", "buf_u", "buf_g"):
+    for f in ("codes", "row_scale", "col_scale", "ent_k", "ent_u", "ent_g"):
         assert np.array_equal(post[f][~closed], pre[f][~closed]), f
+    # compensators sit at window position 0 (G = 0)
+    assert np.all(post["comp_g"][heads] == 0)
 
 
 @pytest.mark.parametrize("name", ["tiny_gdn", "qwen_gdn", "kda_int4"])
