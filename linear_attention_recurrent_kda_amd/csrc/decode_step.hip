@@ -49,6 +49,46 @@ __device__ __forceinline__ void loadN(const float* p, float (&x)[N]) {
 }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Cache policies of the state loads: the codes (the bulk of the state, read
+// once per step) stream with the non-temporal hint; the entry rows keep the
+// default policy (the non-temporal hint measured slower for them).
+constexpr int CODES_POLICY = 2;
+constexpr int ENTRY_POLICY = 0;
+
+// Raw buffer resource over [base, base + bytes): a load at or past `bytes`
+// returns zeros and moves no data (gfx9 descriptor word 3: 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// N consecutive fp32 values (N in 2, 4, 8) at byte offset off of a buffer.
+template <int N>
+__device__ __forceinline__ void buf_loadN(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[N]) {
+  if constexpr (N == 2) {
+    const v2u t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, ENTRY_POLICY);
+    x[0] = __uint_as_float(t[0]), x[1] = __uint_as_float(t[1]);
+  } else {
+#pragma unroll
+    for (int w = 0; w < N / 4; ++w) {
+      const v4u t = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * w, 0, ENTRY_POLICY);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[4 * w + c] = __uint_as_float(t[c]);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_nt4(float* p, float4 v) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(p));
+}
+
+__device__ __forceinline__ float4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4u t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, ENTRY_POLICY);
+  return make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]), __uint_as_float(t[3]));
+}
 
 template <int D, bool KDA>
 struct StepShape {
@@ -79,7 +119,7 @@ struct CodeLoad<4> {
   using T = uint2;
   // Nibble n (two's complement) masked into a byte's high half is the int8
   // 16*n, exactly. Even channels (low nibbles) go first, then odd ones; the
-  // MFMA's B operand is written in the same channel order.
+  // z-limb operand is written in the same channel order.
   __device__ static v4i operand(const T& w) {
     return v4i{int((w.x << 4) & 0xF0F0F0F0u), int((w.y << 4) & 0xF0F0F0F0u), int(w.x & 0xF0F0F0F0u),
                int(w.y & 0xF0F0F0F0u)};
@@ -103,276 +143,343 @@ __device__ __forceinline__ float4 load_act4(const void* p, size_t idx) {  // idx
   }
 }
 
+// One head's decode step, split into the loads (all issued first, into
+// registers) and the arithmetic that consumes them.
 template <int D, int BITS, bool KDA, bool BF16>
-__global__ void __launch_bounds__((StepShape<D, KDA>::NT)) decode_step_kernel(StepArgs a) {
+struct HeadStep {
   using SS = StepShape<D, KDA>;
-  constexpr int NT = SS::NT, NW = SS::NW, RBW = SS::RBW, KB = SS::KB, CPL = SS::CPL, NG = SS::NG;
-  constexpr int KPF = SS::KPF, NQ = SS::NQ, EP = SS::EP, PFE = SS::PFE;
-  constexpr int CB = D * BITS / 8;  // code bytes per value column
-  constexpr float L2E = 1.4426950408889634f;
+  static constexpr int NT = SS::NT, NW = SS::NW, RBW = SS::RBW, KB = SS::KB, CPL = SS::CPL, NG = SS::NG;
+  static constexpr int KPF = SS::KPF, NQ = SS::NQ, EP = SS::EP, PFE = SS::PFE;
+  static constexpr int CB = D * BITS / 8;  // code bytes per value column
+  static constexpr float L2E = 1.4426950408889634f;
   using CL = CodeLoad<BITS>;
   using CT = typename CL::T;
 
-  __shared__ __align__(16) float s_x[2][D];         // x for x = k, q
-  __shared__ __align__(16) float s_G[KDA ? D : 4];  // KDA: G_t per key channel
-  __shared__ __align__(16) int8_t s_B[KB][16][64];  // MFMA B operand: z limbs
-  __shared__ __align__(16) float s_c[D];            // value-column scales
-  __shared__ __align__(16) float s_y[2][D];         // code readout
-  __shared__ __align__(16) float s_vs[EP][2][D];    // value-side partial sums per entry phase
-  __shared__ float s_kap[2][MAX_ROWS];              // kappa^k, kappa^q per entry
-  __shared__ float s_red[3][NW];                    // per-wave k.q and max |z^x| (bits)
+  struct Smem {
+    __align__(16) float x[2][D];         // x for x = k, q
+    __align__(16) float G[KDA ? D : 4];  // KDA: G_t per key channel
+    __align__(16) int8_t B[KB][16][64];  // z limbs (MFMA A operand)
+    __align__(16) float c[D];            // value-column scales
+    __align__(16) float y[2][D];         // code readout
+    __align__(16) float vs[EP][2][D];    // value-side partial sums per entry phase
+    float kap[2][MAX_ROWS];              // kappa^k, kappa^q per entry
+    float red[3][NW];                    // per-wave k.q and max |z^x| (bits)
+  };
 
-  const int bh = blockIdx.x;
-  const int n = a.blen[bh];  // first: every entry address depends on it
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int grp = t / 16, li = t % 16, i0 = li * CPL;
-  const int q4 = t % NQ, ph = t / NQ;  // value-column quad and entry phase
-  const bool chan = NT == D || t < D;  // thread owns key channel t
-  const int tc = chan ? t : 0;
-  const int r = a.r, NE = r + a.w_max;
-  const size_t hD = size_t(bh) * D;
-  // this head's entry rows (per-lane offsets below stay 32-bit)
-  float* const ekh = a.ek + size_t(bh) * NE * D;
-  float* const euh = a.eu + size_t(bh) * NE * D;
-  float* const egh = a.eg + size_t(bh) * NE * (KDA ? D : 1);
+  // Inputs of one head in registers.
+  struct In {
+    CT cw[RBW][KB];  // residual codes, MFMA operand order
+    float kx, qx, si, cc, gi, beta, gs, Gp;
+    float4 v4;
+    float kr[KPF][CPL], gr[KDA ? KPF : 1][CPL], Gm[KPF];
+    float4 uv[PFE];
+  };
 
-  // (1) loads that do not depend on the buffer length: residual codes in MFMA
-  // A-operand order (lane -> value column 16*rb + lane%16, key channels
-  // 64*kb + 16*(lane/16) .. +16), per-channel inputs, this thread's v quad
-  CT cw[RBW][KB];
-  {
-    const int jl = lane & 15, il = 16 * (lane >> 4);
-    const uint8_t* base = static_cast<const uint8_t*>(a.codes) + hD * CB;
+  struct Ptr {  // this head's rows (per-lane offsets stay 32-bit)
+    size_t hD;
+    float *ek, *eu, *eg;
+  };
+
+  __device__ static __forceinline__ Ptr ptr(const StepArgs& a, int bh) {
+    const int NE = a.r + a.w_max;
+    return Ptr{size_t(bh) * D, a.ek + size_t(bh) * NE * D, a.eu + size_t(bh) * NE * D,
+               a.eg + size_t(bh) * NE * (KDA ? D : 1)};
+  }
+
+  // Issue every load of head bh with n buffered tokens (0 <= n < w_max).
+  __device__ static __forceinline__ void load(const StepArgs& a, int bh, int n, In& h) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int grp = t / 16, li = t % 16, i0 = li * CPL;
+    const int q4 = t % NQ, ph = t / NQ;
+    const bool chan = NT == D || t < D;
+    const int tc = chan ? t : 0;
+    const Ptr P = ptr(a, bh);
+    // residual codes in MFMA operand order: lane -> value column
+    // 16*rb + lane%16, key channels 64*kb + 16*(lane/16) .. +16
+    {
+      const int jl = lane & 15, il = 16 * (lane >> 4);
+      const auto rc = buf_rsrc(static_cast<const uint8_t*>(a.codes) + P.hD * CB, D * CB);
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
+      for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int j = 16 * (wave * RBW + rb) + jl, i = 64 * kb + il;
-        if (i < D) cw[rb][kb] = *reinterpret_cast<const CT*>(base + j * CB + i * BITS / 8);
-        else cw[rb][kb] = CT{};
-      }
-  }
-  float kx = load_act<BF16>(a.k, hD + tc), qx = load_act<BF16>(a.q, hD + tc);
-  const float si = a.s[hD + tc], cc = a.c[hD + tc];
-  float gi = 0.f;
-  if constexpr (KDA) gi = a.g[hD + tc];
-  if (!chan) kx = qx = 0.f;
-  const float4 v4 = load_act4<BF16>(a.v, hD + 4 * q4);
-  const float beta = a.beta[bh];
-
-  if (n >= a.w_max || n < 0) {  // precondition violated: leave the head untouched
-    if (t == 0 && a.err) atomicOr(a.err, n < 0 ? LQ_DEVERR_BAD_LEN : LQ_DEVERR_BUFFER_FULL);
-    return;
-  }
-  // entries e = 0..E-1: r compensators (window position 0, G = 0), then the n
-  // buffered tokens; loads of entries past E are clamped to entry E-1 (or 0)
-  const int E = r + n, elast = E > 0 ? E - 1 : 0;
-
-  // (2) entry loads: this group's key rows (and their G), this thread's value rows
-  float kr[KPF][CPL], gr[KDA ? KPF : 1][CPL], Gm[KPF];
-#pragma unroll
-  for (int k = 0; k < KPF; ++k) {
-    const int e = grp + NG * k, ec = e < elast ? e : elast;
-    loadN(ekh + ec * D + i0, kr[k]);
-    if constexpr (KDA) loadN(egh + ec * D + i0, gr[k]);  // zero rows for compensators
-    else Gm[k] = egh[ec];
-  }
-  float4 uv[PFE];
-#pragma unroll
-  for (int k = 0; k < PFE; ++k) {
-    const int e = ph + EP * k, ec = e < elast ? e : elast;
-    uv[k] = *reinterpret_cast<const float4*>(euh + ec * D + 4 * q4);
-  }
-  // G_{t-1}: G of the last entry (compensators carry 0), 0 with no entries
-  float Gp = 0.f;
-  if constexpr (KDA) Gp = E > 0 ? egh[(E - 1) * D + tc] : 0.f;
-  else Gp = E > 0 ? egh[E - 1] : 0.f;
-  const float G = KDA ? 0.f : Gp + a.g[bh];  // GDN: G_t
-
-  // (3) per key channel: z^x = s (.) exp(G_t) (.) x, block max |z^x|, k_t . q_t
-  const float Gi = KDA ? Gp + gi : G;
-  const float eG = exp_fast(Gi);
-  const float zk = si * (eG * kx), zq = si * (eG * qx);
-  if (chan) {
-    s_x[0][t] = kx;
-    s_x[1][t] = qx;
-    if constexpr (KDA) s_G[t] = Gi;
-    s_c[t] = cc;
-  }
-  {
-    const float kq = rows_sum(group_sum<16>(kx * qx));
-    const uint32_t mk = rows_umax(group_umax<16>(as_u(fabsf(zk))));
-    const uint32_t mq = rows_umax(group_umax<16>(as_u(fabsf(zq))));
-    if (lane == 0) {
-      s_red[0][wave] = kq;
-      s_red[1][wave] = as_f(mk);
-      s_red[2][wave] = as_f(mq);
+        for (int kb = 0; kb < KB; ++kb) {
+          const int j = 16 * (wave * RBW + rb) + jl, i = 64 * kb + il;
+          const uint32_t off = j * CB + i * BITS / 8;
+          if (D >= 64 || i < D) {
+            if constexpr (BITS == 8) {
+              const v4u w = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, CODES_POLICY);
+              h.cw[rb][kb] = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+              const v2u w = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, CODES_POLICY);
+              h.cw[rb][kb] = make_uint2(w[0], w[1]);
+            }
+          } else {
+            h.cw[rb][kb] = CT{};
+          }
+        }
     }
+    h.kx = load_act<BF16>(a.k, P.hD + tc);
+    h.qx = load_act<BF16>(a.q, P.hD + tc);
+    h.si = a.s[P.hD + tc];
+    h.cc = a.c[P.hD + tc];
+    h.gi = KDA ? a.g[P.hD + tc] : 0.f;
+    h.gs = KDA ? 0.f : a.g[bh];
+    h.v4 = load_act4<BF16>(a.v, P.hD + 4 * q4);
+    h.beta = a.beta[bh];
+    // entries e = 0..E-1: r compensators (window position 0, G = 0), then the
+    // n buffered tokens. The entry buffers end at entry E, so rows past the
+    // last entry read as zeros and cost no memory traffic.
+    const int E = a.r + n;
+    const auto rk = buf_rsrc(P.ek, uint32_t(E) * D * 4), ru = buf_rsrc(P.eu, uint32_t(E) * D * 4);
+    const auto rg = buf_rsrc(P.eg, uint32_t(E) * (KDA ? D : 1) * 4);
+#pragma unroll
+    for (int k = 0; k < KPF; ++k) {
+      const int e = grp + NG * k;
+      buf_loadN(rk, uint32_t(e * D + i0) * 4, h.kr[k]);
+      if constexpr (KDA) buf_loadN(rg, uint32_t(e * D + i0) * 4, h.gr[k]);  // zero rows for compensators
+      else h.Gm[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, uint32_t(e) * 4, 0, ENTRY_POLICY));
+    }
+#pragma unroll
+    for (int k = 0; k < PFE; ++k) h.uv[k] = buf_load4(ru, uint32_t((ph + EP * k) * D + 4 * q4) * 4);
+    // G_{t-1}: G of the last entry (compensators carry 0), 0 with no entries
+    if constexpr (KDA) h.Gp = E > 0 ? P.eg[(E - 1) * D + tc] : 0.f;
+    else h.Gp = E > 0 ? P.eg[E - 1] : 0.f;
+    if (!chan) h.kx = h.qx = 0.f;
   }
-  __syncthreads();
 
-  // (4) z^x as a 30-bit fixed-point integer with a power-of-two block scale,
-  // split into four signed 8-bit limbs: the MFMA B operand (columns 4x+l)
-  float zscale[2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    uint32_t mb = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mb = max(mb, as_u(s_red[1 + x][w]));
-    int ex = 0;
-    frexpf(as_f(mb), &ex);             // max |z| < 2^ex
-    zscale[x] = ldexpf(1.f, ex - 30);  // z = Z * zscale, |Z| < 2^30
+  // The step of head bh from its loaded inputs; writes o, appends entry E.
+  __device__ static __forceinline__ void compute(const StepArgs& a, int bh, int n, const In& h, Smem& sm) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int grp = t / 16, li = t % 16, i0 = li * CPL;
+    const int q4 = t % NQ, ph = t / NQ;
+    const bool chan = NT == D || t < D;
+    const Ptr P = ptr(a, bh);
+    const int E = a.r + n;
+    const float G = KDA ? 0.f : h.Gp + h.gs;  // GDN: G_t
+
+    // (1) per key channel: z^x = s (.) exp(G_t) (.) x, block max |z^x|, k_t . q_t
+    const float Gi = KDA ? h.Gp + h.gi : G;
+    const float eG = exp_fast(Gi);
+    const float zk = h.si * (eG * h.kx), zq = h.si * (eG * h.qx);
     if (chan) {
-      const int Z = int(rintf(ldexpf(x == 0 ? zk : zq, 30 - ex)));
-      const int l0 = int(int8_t(Z & 0xFF));
-      const int z1 = (Z - l0) >> 8;
-      const int l1 = int(int8_t(z1 & 0xFF));
-      const int z2 = (z1 - l1) >> 8;
-      const int l2 = int(int8_t(z2 & 0xFF));
-      const int l3 = (z2 - l2) >> 8;
-      const int kb = t >> 6, pos = (t & 48) | chan_pos<BITS>(t & 15);
-      s_B[kb][4 * x + 0][pos] = int8_t(l0);
-      s_B[kb][4 * x + 1][pos] = int8_t(l1);
-      s_B[kb][4 * x + 2][pos] = int8_t(l2);
-      s_B[kb][4 * x + 3][pos] = int8_t(l3);
+      sm.x[0][t] = h.kx;
+      sm.x[1][t] = h.qx;
+      if constexpr (KDA) sm.G[t] = Gi;
+      sm.c[t] = h.cc;
     }
-  }
-  // (D = 32: the A operand is zero past channel D, so the B operand's unwritten
-  // padding bytes never contribute)
+    {
+      const float kq = rows_sum(group_sum<16>(h.kx * h.qx));
+      const uint32_t mk = rows_umax(group_umax<16>(as_u(fabsf(zk))));
+      const uint32_t mq = rows_umax(group_umax<16>(as_u(fabsf(zq))));
+      if (lane == 0) {
+        sm.red[0][wave] = kq;
+        sm.red[1][wave] = as_f(mk);
+        sm.red[2][wave] = as_f(mq);
+      }
+    }
+    __syncthreads();
 
-  // (5) key-side dots: kappa^x_e = sum_i k_e,i exp(G_t,i - G_e,i) x_i
-  // (GDN: the decay ratio is one scalar exp(G_t - G_e) applied after the sum)
-  {
-    float xk[CPL], xq[CPL], Gt[CPL];
-    loadN(&s_x[0][i0], xk);
-    loadN(&s_x[1][i0], xq);
-    if constexpr (KDA) {
-      loadN(&s_G[i0], Gt);
+    // (2) z^x as a 30-bit fixed-point integer with a power-of-two block scale,
+    // split into four signed 8-bit limbs (rows 4x+l of the MFMA A operand)
+    float zscale[2];
 #pragma unroll
-      for (int x = 0; x < CPL; ++x) Gt[x] *= L2E;
+    for (int x = 0; x < 2; ++x) {
+      uint32_t mb = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mb = max(mb, as_u(sm.red[1 + x][w]));
+      int ex = 0;
+      frexpf(as_f(mb), &ex);             // max |z| < 2^ex
+      zscale[x] = ldexpf(1.f, ex - 30);  // z = Z * zscale, |Z| < 2^30
+      if (chan) {
+        const int Z = int(rintf(ldexpf(x == 0 ? zk : zq, 30 - ex)));
+        const int l0 = int(int8_t(Z & 0xFF));
+        const int z1 = (Z - l0) >> 8;
+        const int l1 = int(int8_t(z1 & 0xFF));
+        const int z2 = (z1 - l1) >> 8;
+        const int l2 = int(int8_t(z2 & 0xFF));
+        const int l3 = (z2 - l2) >> 8;
+        const int kb = t >> 6, pos = (t & 48) | chan_pos<BITS>(t & 15);
+        sm.B[kb][4 * x + 0][pos] = int8_t(l0);
+        sm.B[kb][4 * x + 1][pos] = int8_t(l1);
+        sm.B[kb][4 * x + 2][pos] = int8_t(l2);
+        sm.B[kb][4 * x + 3][pos] = int8_t(l3);
+      }
     }
-    for (int e0 = 0; e0 < E; e0 += NG * KPF) {
+    // (D = 32: the code operand is zero past channel D, so the limb operand's
+    // unwritten padding bytes never contribute)
+
+    // (3) key-side dots: kappa^x_e = sum_i k_e,i exp(G_t,i - G_e,i) x_i
+    // (GDN: the decay ratio is one scalar exp(G_t - G_e) applied after the sum)
+    {
+      float xk[CPL], xq[CPL], Gt[CPL];
+      loadN(&sm.x[0][i0], xk);
+      loadN(&sm.x[1][i0], xq);
+      if constexpr (KDA) {
+        loadN(&sm.G[i0], Gt);
 #pragma unroll
-      for (int k = 0; k < KPF; ++k) {
-        const int e = e0 + grp + NG * k;
-        float row[CPL], gm[CPL], gsc = Gm[k];
-        if (e0 == 0) {
+        for (int x = 0; x < CPL; ++x) Gt[x] *= L2E;
+      }
+      const auto rk = buf_rsrc(P.ek, uint32_t(E) * D * 4);
+      const auto rg = buf_rsrc(P.eg, uint32_t(E) * (KDA ? D : 1) * 4);
+      int e0 = 0;
+      do {  // at least one pass, so that kappa of the prefetched rows is always written
+#pragma unroll
+        for (int k = 0; k < KPF; ++k) {
+          const int e = e0 + grp + NG * k;
+          // a 16-lane row group shares e: skipped groups leave whole rows idle
+          if (e >= E && e0 + NG * k > 0) {
+            if (li == 0) sm.kap[0][e] = sm.kap[1][e] = 0.f;
+            continue;
+          }
+          float row[CPL], gm[CPL], gsc = h.Gm[k];
+          if (e0 == 0) {
+#pragma unroll
+            for (int x = 0; x < CPL; ++x) {
+              row[x] = h.kr[k][x];
+              if constexpr (KDA) gm[x] = h.gr[k][x];
+            }
+          } else {  // entries beyond the prefetched ones (long windows)
+            buf_loadN(rk, uint32_t(e * D + i0) * 4, row);
+            if constexpr (KDA) buf_loadN(rg, uint32_t(e * D + i0) * 4, gm);
+            else gsc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, uint32_t(e) * 4, 0, ENTRY_POLICY));
+          }
+          float dk = 0.f, dq = 0.f;
 #pragma unroll
           for (int x = 0; x < CPL; ++x) {
-            row[x] = kr[k][x];
-            if constexpr (KDA) gm[x] = gr[k][x];
+            float f = row[x];
+            if constexpr (KDA) f *= __builtin_amdgcn_exp2f(fmaf(gm[x], -L2E, Gt[x]));
+            dk = fmaf(f, xk[x], dk);
+            dq = fmaf(f, xq[x], dq);
           }
-        } else {  // entries beyond the prefetched ones (long windows)
-          const int ec = e < elast ? e : elast;
-          loadN(ekh + ec * D + i0, row);
-          if constexpr (KDA) loadN(egh + ec * D + i0, gm);
-          else gsc = egh[ec];
+          dk = group_sum<16>(dk);
+          dq = group_sum<16>(dq);
+          if constexpr (!KDA) {
+            const float f = exp_fast(G - gsc);
+            dk *= f;
+            dq *= f;
+          }
+          // rows past the last entry read as zeros: kappa = 0 there
+          if (li == 0) {
+            sm.kap[0][e] = dk;
+            sm.kap[1][e] = dq;
+          }
         }
-        float dk = 0.f, dq = 0.f;
-#pragma unroll
-        for (int x = 0; x < CPL; ++x) {
-          float f = row[x];
-          if constexpr (KDA) f *= __builtin_amdgcn_exp2f(fmaf(gm[x], -L2E, Gt[x]));
-          dk = fmaf(f, xk[x], dk);
-          dq = fmaf(f, xq[x], dq);
-        }
-        dk = group_sum<16>(dk);
-        dq = group_sum<16>(dq);
-        if constexpr (!KDA) {
-          const float f = exp_fast(G - gsc);
-          dk *= f;
-          dq *= f;
-        }
-        if (li == 0 && e < E) {
-          s_kap[0][e] = dk;
-          s_kap[1][e] = dq;
-        }
-      }
+        e0 += NG * KPF;
+      } while (e0 < E);
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // (6) residual readout on the matrix cores: for every value column j and
-  // x in {k, q}, sum_i C_ij Z^x_i exactly in int32, limb by limb; then
-  // y^x_j = c_j * zscale_x * sum_l 256^l D[j][4x+l]
-  {
-    v4i bop[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      bop[kb] = *reinterpret_cast<const v4i*>(&s_B[kb][lane & 15][16 * (lane >> 4)]);
-    const int col = lane & 15, limb = lane & 3, xs = col >> 2;
-    const float lw = float(1 << (8 * limb)) * (BITS == 4 ? 0.0625f : 1.f) * (xs == 0 ? zscale[0] : zscale[1]);
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      v4i acc = {0, 0, 0, 0};
+    // (4) residual readout on the matrix cores: for every value column j and
+    // x in {k, q}, sum_i Z^x_i C_ij exactly in int32, limb by limb (A = limbs,
+    // rows 4x+l; B = codes, columns j). Lane l of row block rb then holds the
+    // four limb sums of x = l/16 for column j = 16 rb + l%16 and combines them:
+    // y^x_j / c_j = zscale_x * sum_l 256^l D[4x+l][j].
+    {
+      v4i aop[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(CL::operand(cw[rb][kb]), bop[kb], acc, 0, 0, 0);
+        aop[kb] = *reinterpret_cast<const v4i*>(&sm.B[kb][lane & 15][16 * (lane >> 4)]);
+      v4i acc[RBW];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float f = float(acc[v]) * lw;
-        f += dpp<DPP_QUAD_XOR1>(f);
-        f += dpp<DPP_QUAD_XOR2>(f);
-        const int jj = 16 * (wave * RBW + rb) + 4 * (lane >> 4) + v;
-        if (limb == 0 && col < 8) s_y[xs][jj] = s_c[jj] * f;
+      for (int rb = 0; rb < RBW; ++rb) {
+        acc[rb] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          acc[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[kb], CL::operand(h.cw[rb][kb]), acc[rb], 0, 0, 0);
+      }
+      const int xs = lane >> 4;
+      const float zs = (xs == 0 ? zscale[0] : zscale[1]) * (BITS == 4 ? 0.0625f : 1.f);
+      if (xs < 2) {
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+          float f = fmaf(float(acc[rb][3]), 16777216.f, float(acc[rb][2]) * 65536.f);
+          f = fmaf(float(acc[rb][1]), 256.f, f) + float(acc[rb][0]);
+          sm.y[xs][16 * (wave * RBW + rb) + (lane & 15)] = f * zs;
+        }
+      }
+    }
+
+    // (5) value-side sums: sum_e u_e[j] kappa^x_e for this thread's four value
+    // columns over the entries of its phase (e = ph, ph + EP, ...)
+    {
+      float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+#pragma unroll
+      for (int k = 0; k < PFE; ++k) {
+        const int e = ph + EP * k;
+        if (e >= E && k > 0) continue;  // (past the last entry u = 0 and kappa = 0)
+        const float ak = sm.kap[0][e], aq = sm.kap[1][e];
+        pk.x = fmaf(h.uv[k].x, ak, pk.x), pk.y = fmaf(h.uv[k].y, ak, pk.y);
+        pk.z = fmaf(h.uv[k].z, ak, pk.z), pk.w = fmaf(h.uv[k].w, ak, pk.w);
+        pq.x = fmaf(h.uv[k].x, aq, pq.x), pq.y = fmaf(h.uv[k].y, aq, pq.y);
+        pq.z = fmaf(h.uv[k].z, aq, pq.z), pq.w = fmaf(h.uv[k].w, aq, pq.w);
+      }
+      const auto ru = buf_rsrc(P.eu, uint32_t(E) * D * 4);
+      for (int e = ph + EP * PFE; e < E; e += EP) {
+        const float4 u = buf_load4(ru, uint32_t(e * D + 4 * q4) * 4);
+        const float ak = sm.kap[0][e], aq = sm.kap[1][e];
+        pk.x = fmaf(u.x, ak, pk.x), pk.y = fmaf(u.y, ak, pk.y), pk.z = fmaf(u.z, ak, pk.z), pk.w = fmaf(u.w, ak, pk.w);
+        pq.x = fmaf(u.x, aq, pq.x), pq.y = fmaf(u.y, aq, pq.y), pq.z = fmaf(u.z, aq, pq.z), pq.w = fmaf(u.w, aq, pq.w);
+      }
+      *reinterpret_cast<float4*>(&sm.vs[ph][0][4 * q4]) = pk;
+      *reinterpret_cast<float4*>(&sm.vs[ph][1][4 * q4]) = pq;
+    }
+    __syncthreads();
+
+    // (6) delta, output, append (k_t, u_t, G_t) as entry E: one thread per
+    // value-column quad
+    if (t < NQ) {
+      float kqs = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) kqs += sm.red[0][w];
+      const float4 c4 = *reinterpret_cast<const float4*>(&sm.c[4 * q4]);
+      float4 yk = *reinterpret_cast<const float4*>(&sm.y[0][4 * q4]);
+      float4 yq = *reinterpret_cast<const float4*>(&sm.y[1][4 * q4]);
+      yk.x *= c4.x, yk.y *= c4.y, yk.z *= c4.z, yk.w *= c4.w;
+      yq.x *= c4.x, yq.y *= c4.y, yq.z *= c4.z, yq.w *= c4.w;
+#pragma unroll
+      for (int p = 0; p < EP; ++p) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&sm.vs[p][0][4 * q4]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&sm.vs[p][1][4 * q4]);
+        yk.x += a4.x, yk.y += a4.y, yk.z += a4.z, yk.w += a4.w;
+        yq.x += b4.x, yq.y += b4.y, yq.z += b4.z, yq.w += b4.w;
+      }
+      const float4 v4 = h.v4;
+      const float beta = h.beta;
+      float4 u, o;
+      u.x = beta * (v4.x - yk.x), u.y = beta * (v4.y - yk.y), u.z = beta * (v4.z - yk.z), u.w = beta * (v4.w - yk.w);
+      o.x = fmaf(kqs, u.x, yq.x), o.y = fmaf(kqs, u.y, yq.y), o.z = fmaf(kqs, u.z, yq.z), o.w = fmaf(kqs, u.w, yq.w);
+      *reinterpret_cast<float4*>(a.o + P.hD + 4 * q4) = o;
+      // the appended entry is read again one step later, after the rest of
+      // the step's state has streamed through: non-temporal stores
+      store_nt4(P.eu + E * D + 4 * q4, u);
+      store_nt4(P.ek + E * D + 4 * q4, *reinterpret_cast<const float4*>(&sm.x[0][4 * q4]));
+      if constexpr (KDA) store_nt4(P.eg + E * D + 4 * q4, *reinterpret_cast<const float4*>(&sm.G[4 * q4]));
+      if (t == 0) {
+        if constexpr (!KDA) P.eg[E] = G;
+        a.blen[bh] = n + 1;
       }
     }
   }
+};
 
-  // (7) value-side sums: sum_e u_e[j] kappa^x_e for this thread's four value
-  // columns over the entries of its phase (e = ph, ph + EP, ...)
-  {
-    float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
-#pragma unroll
-    for (int k = 0; k < PFE; ++k) {
-      const int e = ph + EP * k;
-      if (e < E) {
-        const float ak = s_kap[0][e], aq = s_kap[1][e];
-        pk.x = fmaf(uv[k].x, ak, pk.x), pk.y = fmaf(uv[k].y, ak, pk.y);
-        pk.z = fmaf(uv[k].z, ak, pk.z), pk.w = fmaf(uv[k].w, ak, pk.w);
-        pq.x = fmaf(uv[k].x, aq, pq.x), pq.y = fmaf(uv[k].y, aq, pq.y);
-        pq.z = fmaf(uv[k].z, aq, pq.z), pq.w = fmaf(uv[k].w, aq, pq.w);
-      }
-    }
-    for (int e = ph + EP * PFE; e < E; e += EP) {
-      const float4 u = *reinterpret_cast<const float4*>(euh + e * D + 4 * q4);
-      const float ak = s_kap[0][e], aq = s_kap[1][e];
-      pk.x = fmaf(u.x, ak, pk.x), pk.y = fmaf(u.y, ak, pk.y), pk.z = fmaf(u.z, ak, pk.z), pk.w = fmaf(u.w, ak, pk.w);
-      pq.x = fmaf(u.x, aq, pq.x), pq.y = fmaf(u.y, aq, pq.y), pq.z = fmaf(u.z, aq, pq.z), pq.w = fmaf(u.w, aq, pq.w);
-    }
-    *reinterpret_cast<float4*>(&s_vs[ph][0][4 * q4]) = pk;
-    *reinterpret_cast<float4*>(&s_vs[ph][1][4 * q4]) = pq;
+// One workgroup per head: a batch of a few thousand heads is resident on the
+// chip at once, every head's loads are in flight from the start, and no
+// workgroup waits for another. (Several heads per workgroup with the next
+// head's loads overlapping the current head's arithmetic measured slower.)
+template <int D, int BITS, bool KDA, bool BF16>
+__global__ void __launch_bounds__((StepShape<D, KDA>::NT)) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 4)))
+decode_step_kernel(StepArgs a) {
+  using HS = HeadStep<D, BITS, KDA, BF16>;
+  __shared__ typename HS::Smem sm;
+  const int bh = blockIdx.x;
+  const int n = __builtin_amdgcn_readfirstlane(a.blen[bh]);  // every entry address depends on it
+  if (n < 0 || n >= a.w_max) {  // precondition violated: the head is left untouched
+    if (threadIdx.x == 0 && a.err) atomicOr(a.err, n < 0 ? LQ_DEVERR_BAD_LEN : LQ_DEVERR_BUFFER_FULL);
+    return;
   }
-  __syncthreads();
-
-  // (8) delta, output, append (k_t, u_t, G_t) as entry E: one thread per
-  // value-column quad
-  if (t < NQ) {
-    float kqs = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) kqs += s_red[0][w];
-    float4 yk = *reinterpret_cast<const float4*>(&s_y[0][4 * q4]);
-    float4 yq = *reinterpret_cast<const float4*>(&s_y[1][4 * q4]);
-#pragma unroll
-    for (int p = 0; p < EP; ++p) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&s_vs[p][0][4 * q4]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&s_vs[p][1][4 * q4]);
-      yk.x += a4.x, yk.y += a4.y, yk.z += a4.z, yk.w += a4.w;
-      yq.x += b4.x, yq.y += b4.y, yq.z += b4.z, yq.w += b4.w;
-    }
-    float4 u, o;
-    u.x = beta * (v4.x - yk.x), u.y = beta * (v4.y - yk.y), u.z = beta * (v4.z - yk.z), u.w = beta * (v4.w - yk.w);
-    o.x = fmaf(kqs, u.x, yq.x), o.y = fmaf(kqs, u.y, yq.y), o.z = fmaf(kqs, u.z, yq.z), o.w = fmaf(kqs, u.w, yq.w);
-    *reinterpret_cast<float4*>(a.o + hD + 4 * q4) = o;
-    *reinterpret_cast<float4*>(euh + E * D + 4 * q4) = u;
-    *reinterpret_cast<float4*>(ekh + E * D + 4 * q4) = *reinterpret_cast<const float4*>(&s_x[0][4 * q4]);
-    if constexpr (KDA)
-      *reinterpret_cast<float4*>(egh + E * D + 4 * q4) = *reinterpret_cast<const float4*>(&s_G[4 * q4]);
-    if (t == 0) {
-      if constexpr (!KDA) egh[E] = G;
-      a.blen[bh] = n + 1;
-    }
-  }
+  typename HS::In in;
+  HS::load(a, bh, n, in);
+  HS::compute(a, bh, n, in, sm);
 }
 
 template <int D, int BITS, bool KDA, bool BF16>
