@@ -17,7 +17,10 @@ gives the average duration of each kernel. The whole region is bracketed by
 device synchronisation on both sides.
 
 Prints one JSON line. The roofline object describes the decode-step kernel:
-achieved = algorithmic bytes per launch / average launch duration.
+achieved = algorithmic bytes per launch / average launch duration; traffic =
+HBM bytes per launch read by the FETCH_SIZE and WRITE_SIZE counters (scaled by
+their reading on a plain copy of known size), taken from the committed counter
+profile while the kernel sources are unchanged since, else null.
 """
 import argparse
 import json
@@ -43,7 +46,25 @@ def parse():
     p.add_argument("--no-fp32", action="store_true", help="skip the FP32-state baseline")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--cpu-sample", default="8x128", help="oracle sample: sequences x steps")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device copy three times (the reference dispatch "
+                        "for scaling hardware byte counters), then exit")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: a counter profile of these dispatches gives
+    the factor between what the HBM byte counters read and the bytes moved."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_dispatch": n, "bytes_written_per_dispatch": n,
+                                           "dispatches": 3}}), flush=True)
 
 
 def schedule(win_len, win_off, total):
@@ -70,6 +91,31 @@ def segments(closes, t0, t1):
             segs.append((start, t + 1))
             start = t + 1
     return segs
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_step_kernel_qwen_gdn_traffic.md")
+KERNEL_SOURCES = ("decode_step.hip", "lq_common.h", "lq_launch.h")
+
+
+def measured_traffic(wl, bits):
+    """HBM bytes per decode launch from the committed counter profile (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's reading), or None when the profile does not
+    cover this workload or the kernel sources changed since it was taken."""
+    import hashlib
+    if wl.name != "qwen_gdn" or bits != 8 or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for ln in open(TRAFFIC_PROFILE):
+        if ":" in ln and ln.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = ln.split(":", 1)
+            fields[k] = v.strip()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "linear_attention_recurrent_kda_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def run_gpu(args, wl, bits):
@@ -266,6 +312,9 @@ def cpu_baseline(wl, bits, sample):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode path has no cross-GPU exchange (heads and "
               f"sequences shard with no communication), so --gpus {args.gpus} is not run.",
@@ -305,7 +354,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(r["dec_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl, bits),
             "kernel": "decode_step_kernel",
             "avg_launch_us": round(r["dec_us"], 3),
             "bytes_per_launch": round(r["dec_bytes"] / max(r["n_dec"], 1)),
