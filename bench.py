@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--bits", type=int, default=None)
     p.add_argument("--no-fp32", action="store_true", help="skip the FP32-state baseline")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    p.add_argument("--cpu-sample", default="8x128", help="oracle sample: sequences x steps")
+    p.add_argument("--cpu-sample", default="32x256", help="oracle sample: sequences x steps")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy three times (the reference dispatch "
                         "for scaling hardware byte counters), then exit")

@@ -95,8 +95,13 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
   constexpr int B = D / 16;
   constexpr int Q = BITS == 8 ? 127 : 7;
   constexpr int CB = D * BITS / 8;  // code bytes per value column
-  __shared__ float sh_n[16];
-  __shared__ float sh_c[4][D];
+  constexpr int CH = 16;            // entries staged in LDS per fold pass
+  constexpr int GL = KDA ? D : 1;   // G values per entry
+  __shared__ float sh_n[2][16];     // partial squared norms (double-buffered)
+  __shared__ float sh_c[2][4][D];   // per-wave column partials (double-buffered)
+  __shared__ __align__(16) float sh_k[DENSE ? 1 : CH][D];
+  __shared__ __align__(16) float sh_u[DENSE ? 1 : CH][D];
+  __shared__ __align__(16) float sh_g[DENSE ? 1 : CH][GL];
 
   const int t = threadIdx.x, tj = t & 15, ti = t >> 4, lane = t & 63, wave = t >> 6;
   const int H = a.heads;
@@ -115,7 +120,7 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
   const int r = a.r;
   const size_t erow = size_t(bh) * (r + a.w_max);  // first entry row of this head
 
-  // ---- the dense state block M[a][bb] = S[i0 + a][j0 + bb]
+  // ---- the dense state block M[x][bb] = S[i0 + x][j0 + bb]
   float M[B][B];
   if constexpr (DENSE) {
 #pragma unroll
@@ -129,15 +134,23 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
     // fold: S = exp(G_n) (.) diag(s) C diag(c) + sum_e exp(G_n - G_e) (.) k_e u_e^T
     // over the entries e < r + n (compensators carry G_e = 0); G_n is the G of
     // the last entry (0 when there is none)
-    const int n = a.blen[bh];
+    const int n = __builtin_amdgcn_readfirstlane(a.blen[bh]);
     if (n < 0 || n > a.w_max) {  // corrupted buffer length: leave the head untouched
       if (t == 0 && a.err) atomicOr(a.err, LQ_DEVERR_BAD_LEN);
       return;
     }
     const int E = r + n;
-    float si[B], cj[B];
+    float si[B], cj[B], Gn[KDA ? B : 1];
     loadB<B>(a.s + hD + i0, si);
     loadB<B>(a.c + hD + j0, cj);
+    if constexpr (KDA) {
+      if (E > 0) loadB<B>(a.eg + (erow + E - 1) * D + i0, Gn);
+      else
+#pragma unroll
+        for (int x = 0; x < B; ++x) Gn[x] = 0.f;
+    } else {
+      Gn[0] = E > 0 ? a.eg[erow + E - 1] : 0.f;
+    }
     const uint8_t* cb = static_cast<const uint8_t*>(a.codes) + hD * CB + i0 * BITS / 8;
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) {
@@ -146,54 +159,62 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
 #pragma unroll
       for (int x = 0; x < B; ++x) M[x][bb] = (si[x] * float(code[x])) * cj[bb];
     }
-    if constexpr (KDA) {
-      float Gn[B];
-      if (E > 0) loadB<B>(a.eg + (erow + E - 1) * D + i0, Gn);
-      else
 #pragma unroll
-        for (int x = 0; x < B; ++x) Gn[x] = 0.f;
+    for (int x = 0; x < B; ++x) {
+      const float e = expf(KDA ? Gn[x] : Gn[0]);
 #pragma unroll
-      for (int x = 0; x < B; ++x) {
-        const float e = expf(Gn[x]);
+      for (int bb = 0; bb < B; ++bb) M[x][bb] *= e;
+    }
+    // entries, CH at a time: the workgroup stages the rows in LDS with one
+    // round of loads, then every thread applies them to its block
+    constexpr int V4 = D / 4;                       // float4 per row
+    constexpr int PER = (CH * V4 + 255) / 256;      // float4 per thread per array
+    for (int m0 = 0; m0 < E; m0 += CH) {
+      const int cnt = min(CH, E - m0);
+      __syncthreads();  // the previous pass has consumed the staged rows
 #pragma unroll
-        for (int bb = 0; bb < B; ++bb) M[x][bb] *= e;
-      }
-      for (int m = 0; m < E; ++m) {
-        float km[B], um[B], gm[B];
-        loadB<B>(a.ek + (erow + m) * D + i0, km);
-        loadB<B>(a.eu + (erow + m) * D + j0, um);
-        loadB<B>(a.eg + (erow + m) * D + i0, gm);
-#pragma unroll
-        for (int x = 0; x < B; ++x) {
-          const float kf = expf(Gn[x] - gm[x]) * km[x];
-#pragma unroll
-          for (int bb = 0; bb < B; ++bb) M[x][bb] = fmaf(kf, um[bb], M[x][bb]);
+      for (int p = 0; p < PER; ++p) {
+        const int idx = t + 256 * p;
+        if (idx < cnt * V4) {
+          const int row = idx / V4, c4 = idx % V4;
+          const size_t g = (erow + m0 + row) * D + 4 * c4;
+          reinterpret_cast<float4*>(&sh_k[row][0])[c4] = *reinterpret_cast<const float4*>(a.ek + g);
+          reinterpret_cast<float4*>(&sh_u[row][0])[c4] = *reinterpret_cast<const float4*>(a.eu + g);
+          if constexpr (KDA) reinterpret_cast<float4*>(&sh_g[row][0])[c4] = *reinterpret_cast<const float4*>(a.eg + g);
         }
       }
-    } else {
-      const float Gn = E > 0 ? a.eg[erow + E - 1] : 0.f;
-      const float e = expf(Gn);
-#pragma unroll
-      for (int x = 0; x < B; ++x)
-#pragma unroll
-        for (int bb = 0; bb < B; ++bb) M[x][bb] *= e;
-      for (int m = 0; m < E; ++m) {
+      if constexpr (!KDA) {
+        if (t < cnt) sh_g[t][0] = a.eg[erow + m0 + t];
+      }
+      __syncthreads();
+      for (int m = 0; m < cnt; ++m) {
         float km[B], um[B];
-        loadB<B>(a.ek + (erow + m) * D + i0, km);
-        loadB<B>(a.eu + (erow + m) * D + j0, um);
-        const float f = expf(Gn - a.eg[erow + m]);
+        loadB<B>(&sh_k[m][i0], km);
+        loadB<B>(&sh_u[m][j0], um);
+        if constexpr (KDA) {
+          float gm[B];
+          loadB<B>(&sh_g[m][i0], gm);
 #pragma unroll
-        for (int x = 0; x < B; ++x) {
-          const float kf = f * km[x];
+          for (int x = 0; x < B; ++x) km[x] *= expf(Gn[x] - gm[x]);
+        } else {
+          const float f = expf(Gn[0] - sh_g[m][0]);
 #pragma unroll
-          for (int bb = 0; bb < B; ++bb) M[x][bb] = fmaf(kf, um[bb], M[x][bb]);
+          for (int x = 0; x < B; ++x) km[x] *= f;
         }
+#pragma unroll
+        for (int x = 0; x < B; ++x)
+#pragma unroll
+          for (int bb = 0; bb < B; ++bb) M[x][bb] = fmaf(km[x], um[bb], M[x][bb]);
       }
     }
   }
 
-  // ---- compensators: power method with deflation
+  // ---- compensators: power method with deflation. One barrier per
+  // iteration: kappa = M v is complete inside each 16-lane row; the column
+  // partials of M^T kappa and the squared norm of kappa go to LDS together
+  // (double-buffered, so the next iteration may write while this one is read)
   bool live = true;
+  int par = 0;
   for (int l = 0; l < r; ++l) {
     float kk[B], w[B], v[B];
 #pragma unroll
@@ -206,9 +227,9 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
         p = fmaf(v[bb], v[bb], p);
       }
       p = group_sum<16>(p);
-      const float nv = sqrtf(p);
+      const float inv_nv = __builtin_amdgcn_rsqf(p);
 #pragma unroll
-      for (int bb = 0; bb < B; ++bb) v[bb] = v[bb] / nv;
+      for (int bb = 0; bb < B; ++bb) v[bb] *= inv_nv;
       for (int it = 0; it < a.T; ++it) {
         // kappa = M v  (sum over value columns: DPP across the 16 tj lanes)
         float kap[B];
@@ -221,46 +242,46 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
           kap[x] = group_sum<16>(s);
           pk = fmaf(kap[x], kap[x], pk);
         }
-        if (tj == 0) sh_n[ti] = pk;
-        __syncthreads();
-        float nk2 = 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) nk2 += sh_n[q];
-        if (!(nk2 > 0.f) || !isfinite(nk2)) {  // uniform: every thread read the same sums
-          live = false;
-          break;
-        }
-        const float rk = sqrtf(nk2);
-#pragma unroll
-        for (int x = 0; x < B; ++x) kk[x] = kap[x] / rk;
-        // w = M^T k  (sum over key rows: wave rows, then waves through LDS)
+        // M^T kappa (sum over key rows: the wave's four rows, then the waves)
 #pragma unroll
         for (int bb = 0; bb < B; ++bb) {
           float s = 0.f;
 #pragma unroll
-          for (int x = 0; x < B; ++x) s = fmaf(M[x][bb], kk[x], s);
+          for (int x = 0; x < B; ++x) s = fmaf(M[x][bb], kap[x], s);
           s = rows_sum(s);
-          if (lane < 16) sh_c[wave][j0 + bb] = s;
+          if (lane < 16) sh_c[par][wave][j0 + bb] = s;
         }
+        if (tj == 0) sh_n[par][ti] = pk;
         __syncthreads();
+        float nk2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) nk2 += sh_n[par][q];
+        if (!(nk2 > 0.f) || !isfinite(nk2)) {  // uniform: every thread read the same sums
+          live = false;
+          break;
+        }
+        const float inv_rk = __builtin_amdgcn_rsqf(nk2);
+#pragma unroll
+        for (int x = 0; x < B; ++x) kk[x] = kap[x] * inv_rk;
+        // w = M^T k = (M^T kappa) / |kappa|
         float pw = 0.f;
 #pragma unroll
         for (int bb = 0; bb < B; ++bb) {
           const int j = j0 + bb;
-          w[bb] = (sh_c[0][j] + sh_c[1][j]) + (sh_c[2][j] + sh_c[3][j]);
+          w[bb] = ((sh_c[par][0][j] + sh_c[par][1][j]) + (sh_c[par][2][j] + sh_c[par][3][j])) * inv_rk;
           pw = fmaf(w[bb], w[bb], pw);
         }
-        pw = group_sum<16>(pw);
+        par ^= 1;
+        pw = group_sum<16>(pw);  // the same total in every row
         if (!(pw > 0.f) || !isfinite(pw)) {
           live = false;
           break;
         }
-        const float rw = sqrtf(pw);
+        const float inv_rw = __builtin_amdgcn_rsqf(pw);
 #pragma unroll
-        for (int bb = 0; bb < B; ++bb) v[bb] = w[bb] / rw;
+        for (int bb = 0; bb < B; ++bb) v[bb] = w[bb] * inv_rw;
       }
     }
-    __syncthreads();  // sh_n / sh_c are reused after a degenerate early exit
     if (!live) {
 #pragma unroll
       for (int x = 0; x < B; ++x) kk[x] = w[x] = 0.f;
@@ -303,27 +324,27 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
     for (int bb = 0; bb < B; ++bb) m = fmaxf(m, fabsf(M[x][bb]));
     m = group_max<16>(m);
     sa[x] = (a.smoothing && m > 0.f) ? m : 1.f;
+    const float rs = 1.f / sa[x];
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) M[x][bb] *= rs;
   }
-#pragma unroll
-  for (int x = 0; x < B; ++x)
-#pragma unroll
-    for (int bb = 0; bb < B; ++bb) M[x][bb] = M[x][bb] / sa[x];
 
   // ---- value-column scales and codes
+  __syncthreads();  // the power method's last reads of sh_c are done
 #pragma unroll
   for (int bb = 0; bb < B; ++bb) {
     float m = 0.f;
 #pragma unroll
     for (int x = 0; x < B; ++x) m = fmaxf(m, fabsf(M[x][bb]));
     m = rows_max(m);
-    if (lane < 16) sh_c[wave][j0 + bb] = m;
+    if (lane < 16) sh_c[0][wave][j0 + bb] = m;
   }
   __syncthreads();
   float cs[B], inv[B];
 #pragma unroll
   for (int bb = 0; bb < B; ++bb) {
     const int j = j0 + bb;
-    const float m = fmaxf(fmaxf(sh_c[0][j], sh_c[1][j]), fmaxf(sh_c[2][j], sh_c[3][j]));
+    const float m = fmaxf(fmaxf(sh_c[0][0][j], sh_c[0][1][j]), fmaxf(sh_c[0][2][j], sh_c[0][3][j]));
     cs[bb] = m / float(Q);
     inv[bb] = m > 0.f ? float(Q) / m : 0.f;
   }
