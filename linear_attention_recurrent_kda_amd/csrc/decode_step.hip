@@ -169,8 +169,9 @@ struct HeadStep {
   // Inputs of one head in registers.
   struct In {
     CT cw[RBW][KB];  // residual codes, MFMA operand order
-    float kx, qx, si, cc, gi, beta, gs, Gp;
-    float4 v4;
+    uint32_t kx_raw, qx_raw;  // q_t, k_t as loaded (bf16 or fp32 bits); converted when used
+    uint4 v_raw;              // v_t quad as loaded (bf16: .x, .y)
+    float si, cc, gi, beta, gs, Gp;
     float kr[KPF][CPL], gr[KDA ? KPF : 1][CPL], Gm[KPF];
     float4 uv[PFE];
   };
@@ -186,46 +187,44 @@ struct HeadStep {
                a.eg + size_t(bh) * NE * (KDA ? D : 1)};
   }
 
-  // Issue every load of head bh with n buffered tokens (0 <= n < w_max).
+  // Loads that do not depend on the buffer length, issued while it is in
+  // flight: the first half of the codes, then the per-channel inputs.
+  __device__ static __forceinline__ void load_early(const StepArgs& a, int bh, In& h) {
+    const int t = threadIdx.x;
+    const int q4 = t % NQ;
+    const bool chan = NT == D || t < D;
+    const int tc = chan ? t : 0;
+    const Ptr P = ptr(a, bh);
+    load_codes(a, P, h, 0, RBW / 2);
+    __builtin_amdgcn_sched_barrier(0);  // keep these codes first in the issue order
+    if constexpr (BF16) {
+      h.kx_raw = static_cast<const uint16_t*>(a.k)[P.hD + tc];
+      h.qx_raw = static_cast<const uint16_t*>(a.q)[P.hD + tc];
+      const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + P.hD + 4 * q4);
+      h.v_raw = make_uint4(w.x, w.y, 0u, 0u);
+    } else {
+      h.kx_raw = static_cast<const uint32_t*>(a.k)[P.hD + tc];
+      h.qx_raw = static_cast<const uint32_t*>(a.q)[P.hD + tc];
+      h.v_raw = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.v) + P.hD + 4 * q4);
+    }
+    h.si = a.s[P.hD + tc];
+    h.cc = a.c[P.hD + tc];
+    h.gi = KDA ? a.g[P.hD + tc] : 0.f;
+    h.gs = KDA ? 0.f : a.g[bh];
+    h.beta = a.beta[bh];
+    // the buffer length is checked after these loads are issued
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // The loads that need the buffer length n (0 <= n < w_max): the entries,
+  // then the second half of the codes.
   __device__ static __forceinline__ void load(const StepArgs& a, int bh, int n, In& h) {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x;
     const int grp = t / 16, li = t % 16, i0 = li * CPL;
     const int q4 = t % NQ, ph = t / NQ;
     const bool chan = NT == D || t < D;
     const int tc = chan ? t : 0;
     const Ptr P = ptr(a, bh);
-    // residual codes in MFMA operand order: lane -> value column
-    // 16*rb + lane%16, key channels 64*kb + 16*(lane/16) .. +16
-    {
-      const int jl = lane & 15, il = 16 * (lane >> 4);
-      const auto rc = buf_rsrc(static_cast<const uint8_t*>(a.codes) + P.hD * CB, D * CB);
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int j = 16 * (wave * RBW + rb) + jl, i = 64 * kb + il;
-          const uint32_t off = j * CB + i * BITS / 8;
-          if (D >= 64 || i < D) {
-            if constexpr (BITS == 8) {
-              const v4u w = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, CODES_POLICY);
-              h.cw[rb][kb] = make_uint4(w[0], w[1], w[2], w[3]);
-            } else {
-              const v2u w = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, CODES_POLICY);
-              h.cw[rb][kb] = make_uint2(w[0], w[1]);
-            }
-          } else {
-            h.cw[rb][kb] = CT{};
-          }
-        }
-    }
-    h.kx = load_act<BF16>(a.k, P.hD + tc);
-    h.qx = load_act<BF16>(a.q, P.hD + tc);
-    h.si = a.s[P.hD + tc];
-    h.cc = a.c[P.hD + tc];
-    h.gi = KDA ? a.g[P.hD + tc] : 0.f;
-    h.gs = KDA ? 0.f : a.g[bh];
-    h.v4 = load_act4<BF16>(a.v, P.hD + 4 * q4);
-    h.beta = a.beta[bh];
     // entries e = 0..E-1: r compensators (window position 0, G = 0), then the
     // n buffered tokens. The entry buffers end at entry E, so rows past the
     // last entry read as zeros and cost no memory traffic.
@@ -244,7 +243,37 @@ struct HeadStep {
     // G_{t-1}: G of the last entry (compensators carry 0), 0 with no entries
     if constexpr (KDA) h.Gp = E > 0 ? P.eg[(E - 1) * D + tc] : 0.f;
     else h.Gp = E > 0 ? P.eg[E - 1] : 0.f;
-    if (!chan) h.kx = h.qx = 0.f;
+    // The second half of the codes is issued last: loads complete in issue
+    // order, so the entry arithmetic can start while those codes stream in.
+    load_codes(a, P, h, RBW / 2, RBW);
+  }
+
+  // Codes of row blocks [lo, hi) in MFMA operand order: lane -> value column
+  // 16*rb + lane%16, key channels 64*kb + 16*(lane/16) .. +16.
+  __device__ static __forceinline__ void load_codes(const StepArgs& a, const Ptr& P, In& h, int lo, int hi) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int jl = lane & 15, il = 16 * (lane >> 4);
+    const auto rc = buf_rsrc(static_cast<const uint8_t*>(a.codes) + P.hD * CB, D * CB);
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      if (rb < lo || rb >= hi) continue;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int j = 16 * (wave * RBW + rb) + jl, i = 64 * kb + il;
+        const uint32_t off = j * CB + i * BITS / 8;
+        if (D >= 64 || i < D) {
+          if constexpr (BITS == 8) {
+            const v4u w = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, CODES_POLICY);
+            h.cw[rb][kb] = make_uint4(w[0], w[1], w[2], w[3]);
+          } else {
+            const v2u w = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, CODES_POLICY);
+            h.cw[rb][kb] = make_uint2(w[0], w[1]);
+          }
+        } else {
+          h.cw[rb][kb] = CT{};
+        }
+      }
+    }
   }
 
   // The step of head bh from its loaded inputs; writes o, appends entry E.
@@ -256,19 +285,21 @@ struct HeadStep {
     const Ptr P = ptr(a, bh);
     const int E = a.r + n;
     const float G = KDA ? 0.f : h.Gp + h.gs;  // GDN: G_t
+    const float kx = !chan ? 0.f : BF16 ? as_f(h.kx_raw << 16) : as_f(h.kx_raw);
+    const float qx = !chan ? 0.f : BF16 ? as_f(h.qx_raw << 16) : as_f(h.qx_raw);
 
     // (1) per key channel: z^x = s (.) exp(G_t) (.) x, block max |z^x|, k_t . q_t
     const float Gi = KDA ? h.Gp + h.gi : G;
     const float eG = exp_fast(Gi);
-    const float zk = h.si * (eG * h.kx), zq = h.si * (eG * h.qx);
+    const float zk = h.si * (eG * kx), zq = h.si * (eG * qx);
     if (chan) {
-      sm.x[0][t] = h.kx;
-      sm.x[1][t] = h.qx;
+      sm.x[0][t] = kx;
+      sm.x[1][t] = qx;
       if constexpr (KDA) sm.G[t] = Gi;
       sm.c[t] = h.cc;
     }
     {
-      const float kq = rows_sum(group_sum<16>(h.kx * h.qx));
+      const float kq = rows_sum(group_sum<16>(kx * qx));
       const uint32_t mk = rows_umax(group_umax<16>(as_u(fabsf(zk))));
       const uint32_t mq = rows_umax(group_umax<16>(as_u(fabsf(zq))));
       if (lane == 0) {
@@ -369,7 +400,31 @@ struct HeadStep {
     }
     __syncthreads();
 
-    // (4) residual readout on the matrix cores: for every value column j and
+    // (4) value-side sums: sum_e u_e[j] kappa^x_e for this thread's four value
+    // columns over the entries of its phase (e = ph, ph + EP, ...)
+    {
+      float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+#pragma unroll
+      for (int k = 0; k < PFE; ++k) {
+        const int e = ph + EP * k;
+        if (e >= E && k > 0) continue;  // (past the last entry u = 0 and kappa = 0)
+        const float ak = sm.kap[0][e], aq = sm.kap[1][e];
+        pk.x = fmaf(h.uv[k].x, ak, pk.x), pk.y = fmaf(h.uv[k].y, ak, pk.y);
+        pk.z = fmaf(h.uv[k].z, ak, pk.z), pk.w = fmaf(h.uv[k].w, ak, pk.w);
+        pq.x = fmaf(h.uv[k].x, aq, pq.x), pq.y = fmaf(h.uv[k].y, aq, pq.y);
+        pq.z = fmaf(h.uv[k].z, aq, pq.z), pq.w = fmaf(h.uv[k].w, aq, pq.w);
+      }
+      const auto ru = buf_rsrc(P.eu, uint32_t(E) * D * 4);
+      for (int e = ph + EP * PFE; e < E; e += EP) {
+        const float4 u = buf_load4(ru, uint32_t(e * D + 4 * q4) * 4);
+        const float ak = sm.kap[0][e], aq = sm.kap[1][e];
+        pk.x = fmaf(u.x, ak, pk.x), pk.y = fmaf(u.y, ak, pk.y), pk.z = fmaf(u.z, ak, pk.z), pk.w = fmaf(u.w, ak, pk.w);
+        pq.x = fmaf(u.x, aq, pq.x), pq.y = fmaf(u.y, aq, pq.y), pq.z = fmaf(u.z, aq, pq.z), pq.w = fmaf(u.w, aq, pq.w);
+      }
+      *reinterpret_cast<float4*>(&sm.vs[ph][0][4 * q4]) = pk;
+      *reinterpret_cast<float4*>(&sm.vs[ph][1][4 * q4]) = pq;
+    }
+    // (5) residual readout on the matrix cores: for every value column j and
     // x in {k, q}, sum_i Z^x_i C_ij exactly in int32, limb by limb (A = limbs,
     // rows 4x+l; B = codes, columns j). Lane l of row block rb then holds the
     // four limb sums of x = l/16 for column j = 16 rb + l%16 and combines them:
@@ -399,30 +454,6 @@ struct HeadStep {
       }
     }
 
-    // (5) value-side sums: sum_e u_e[j] kappa^x_e for this thread's four value
-    // columns over the entries of its phase (e = ph, ph + EP, ...)
-    {
-      float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
-#pragma unroll
-      for (int k = 0; k < PFE; ++k) {
-        const int e = ph + EP * k;
-        if (e >= E && k > 0) continue;  // (past the last entry u = 0 and kappa = 0)
-        const float ak = sm.kap[0][e], aq = sm.kap[1][e];
-        pk.x = fmaf(h.uv[k].x, ak, pk.x), pk.y = fmaf(h.uv[k].y, ak, pk.y);
-        pk.z = fmaf(h.uv[k].z, ak, pk.z), pk.w = fmaf(h.uv[k].w, ak, pk.w);
-        pq.x = fmaf(h.uv[k].x, aq, pq.x), pq.y = fmaf(h.uv[k].y, aq, pq.y);
-        pq.z = fmaf(h.uv[k].z, aq, pq.z), pq.w = fmaf(h.uv[k].w, aq, pq.w);
-      }
-      const auto ru = buf_rsrc(P.eu, uint32_t(E) * D * 4);
-      for (int e = ph + EP * PFE; e < E; e += EP) {
-        const float4 u = buf_load4(ru, uint32_t(e * D + 4 * q4) * 4);
-        const float ak = sm.kap[0][e], aq = sm.kap[1][e];
-        pk.x = fmaf(u.x, ak, pk.x), pk.y = fmaf(u.y, ak, pk.y), pk.z = fmaf(u.z, ak, pk.z), pk.w = fmaf(u.w, ak, pk.w);
-        pq.x = fmaf(u.x, aq, pq.x), pq.y = fmaf(u.y, aq, pq.y), pq.z = fmaf(u.z, aq, pq.z), pq.w = fmaf(u.w, aq, pq.w);
-      }
-      *reinterpret_cast<float4*>(&sm.vs[ph][0][4 * q4]) = pk;
-      *reinterpret_cast<float4*>(&sm.vs[ph][1][4 * q4]) = pq;
-    }
     __syncthreads();
 
     // (6) delta, output, append (k_t, u_t, G_t) as entry E: one thread per
@@ -443,7 +474,8 @@ struct HeadStep {
         yk.x += a4.x, yk.y += a4.y, yk.z += a4.z, yk.w += a4.w;
         yq.x += b4.x, yq.y += b4.y, yq.z += b4.z, yq.w += b4.w;
       }
-      const float4 v4 = h.v4;
+      const float4 v4 = BF16 ? make_float4(bf16_lo(h.v_raw.x), bf16_hi(h.v_raw.x), bf16_lo(h.v_raw.y), bf16_hi(h.v_raw.y))
+                             : make_float4(as_f(h.v_raw.x), as_f(h.v_raw.y), as_f(h.v_raw.z), as_f(h.v_raw.w));
       const float beta = h.beta;
       float4 u, o;
       u.x = beta * (v4.x - yk.x), u.y = beta * (v4.y - yk.y), u.z = beta * (v4.z - yk.z), u.w = beta * (v4.w - yk.w);
@@ -472,12 +504,18 @@ decode_step_kernel(StepArgs a) {
   using HS = HeadStep<D, BITS, KDA, BF16>;
   __shared__ typename HS::Smem sm;
   const int bh = blockIdx.x;
-  const int n = __builtin_amdgcn_readfirstlane(a.blen[bh]);  // every entry address depends on it
+  // The buffer length comes first (every entry address depends on it) and
+  // through the vector memory path, whose loads complete in issue order: the
+  // wait for it then lets the loads issued after it stay in flight.
+  const uint32_t n_raw = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(a.blen + bh, 4), 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  typename HS::In in;
+  HS::load_early(a, bh, in);
+  const int n = __builtin_amdgcn_readfirstlane(int(n_raw));
   if (n < 0 || n >= a.w_max) {  // precondition violated: the head is left untouched
     if (threadIdx.x == 0 && a.err) atomicOr(a.err, n < 0 ? LQ_DEVERR_BAD_LEN : LQ_DEVERR_BUFFER_FULL);
     return;
   }
-  typename HS::In in;
   HS::load(a, bh, n, in);
   HS::compute(a, bh, n, in, sm);
 }
