@@ -12,7 +12,7 @@
  *
  * Per (sequence b, head h) -- a "head" below -- the recurrent state
  * S in R^{d_k x d_v} (row i = key channel, column j = value channel) is held as
- * a window-start residual diag(s) C diag(c) (symmetric int8/int4 codes C with
+ * a window-start residual diag(s) C diag(c) (symmetric 8-, 6- or 4-bit codes C with
  * per-key-row smoothing scales s and per-value-column scales c), fixed for a
  * window, plus a list of fp32 rank-one entries (k_e, u_e, G_e):
  *   S = exp(G) (.) diag(s) C diag(c) + sum_e exp(G - G_e) (.) k_e u_e^T
@@ -53,7 +53,7 @@ extern "C" {
 #define LQ_OK 0
 #define LQ_ERR_NULL (-1)   /* a required pointer is NULL */
 #define LQ_ERR_SHAPE (-2)  /* unsupported batch/heads/d_k/d_v */
-#define LQ_ERR_BITS (-3)   /* bits not 4 or 8 */
+#define LQ_ERR_BITS (-3)   /* bits not 4, 6 or 8 */
 #define LQ_ERR_CONFIG (-4) /* w_max, n_comp, power_iters, flags or close list out of range */
 #define LQ_ERR_LAUNCH (-5) /* the HIP launch failed */
 #define LQ_ERR_ALIGN (-6)  /* a buffer is not 16-byte aligned */
@@ -74,7 +74,7 @@ typedef struct lq_dims {
   int32_t d_k, d_v;          /* key / value head dims; equal, in {32, 64, 128} */
   int32_t w_max;             /* buffer capacity per head, 1..64 (>= every window length used) */
   int32_t n_comp;            /* r compensators, 0..8 */
-  int32_t bits;              /* 8 or 4 */
+  int32_t bits;              /* 8, 6 or 4 */
   int32_t decay_per_channel; /* 0: GDN, g is [B][H]; 1: KDA, g is [B][H][d_k] */
   int32_t act_dtype;         /* LQ_ACT_F32 or LQ_ACT_BF16 for q, k, v */
   int32_t smoothing;         /* 1: per-key-row smoothing scales; 0: s == 1 */
@@ -85,10 +85,18 @@ typedef struct lq_dims {
    Entry arrays hold r + w_max entries per head: entries 0..r-1 are the
    compensators, entries r..r+n-1 the buffered tokens (n = buf_len). */
 typedef struct lq_state {
-  void* codes;       /* int8 [B*H][d_v][d_k] two's complement, or int4 packed
-                        [B*H][d_v][d_k/2] with key channel 2m in the low nibble
-                        and 2m+1 in the high nibble of byte m; codes in [-Q, Q],
-                        Q = 127 (int8) or 7 (int4) */
+  void* codes;       /* codes in [-Q, Q], Q = 2^(bits-1) - 1; per head
+                        (d = d_k = d_v, value column j, key channel i):
+                        8 bits: int8 [d_v][d_k], two's complement;
+                        4 bits: [d_v][d_k/2] bytes, channel 2m in the low
+                        nibble and 2m+1 in the high nibble of byte m;
+                        6 bits: 3*d*d/4 bytes in two planes, code = 4*hi + lo:
+                        first d*d/2 bytes: hi = code >> 2 (arithmetic, in
+                        [-8, 7]) in the 4-bit layout; then d*d/16 little-endian
+                        32-bit words W[j % 16][i / 16][j / 16], word holding
+                        lo = code & 3 of channels 16*(i/16) .. +15 of column
+                        j, channel c = i % 16 at bits 8*(p%4) + 2*(p/4) with
+                        p = c/2 for even c and 8 + c/2 for odd c. */
   float* row_scale;  /* s [B*H][d_k] key-row smoothing scales */
   float* col_scale;  /* c [B*H][d_v] value-column scales */
   float* ent_k;      /* [B*H][r + w_max][d_k] entry keys (compensator keys are unit vectors) */

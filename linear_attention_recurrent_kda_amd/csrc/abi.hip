@@ -21,7 +21,7 @@ int check_dims(const lq_dims* d, bool method) {
   if (d->decay_per_channel != 0 && d->decay_per_channel != 1) return LQ_ERR_CONFIG;
   if (d->act_dtype != LQ_ACT_F32 && d->act_dtype != LQ_ACT_BF16) return LQ_ERR_CONFIG;
   if (method) {
-    if (d->bits != 8 && d->bits != 4) return LQ_ERR_BITS;
+    if (d->bits != 8 && d->bits != 6 && d->bits != 4) return LQ_ERR_BITS;
     if (d->w_max < 1 || d->w_max > 64) return LQ_ERR_CONFIG;
     if (d->n_comp < 0 || d->n_comp > 8) return LQ_ERR_CONFIG;
     if (d->power_iters < 1 || d->power_iters > 64) return LQ_ERR_CONFIG;
@@ -198,7 +198,7 @@ const char* lq_status_string(int status) {
     case LQ_OK: return "ok";
     case LQ_ERR_NULL: return "a required pointer is NULL";
     case LQ_ERR_SHAPE: return "unsupported shape (d_k == d_v in {32, 64, 128}, batch, heads >= 0)";
-    case LQ_ERR_BITS: return "bits must be 4 or 8";
+    case LQ_ERR_BITS: return "bits must be 4, 6 or 8";
     case LQ_ERR_CONFIG: return "parameter out of range (w_max, n_comp, power_iters, flags, close list)";
     case LQ_ERR_LAUNCH: return "HIP kernel launch failed";
     case LQ_ERR_ALIGN: return "buffer not aligned (16 bytes for state buffers and dense states)";

@@ -106,23 +106,59 @@ struct StepShape {
   static constexpr int PFE = PRE / EP;            // value rows per thread prefetched
 };
 
-// Code bytes one lane feeds to one MFMA: 16 key channels of one value column.
+// Code bytes one lane feeds to the matrix cores: 16 key channels of one
+// value column. load() fetches them from the column's bytes at key channel
+// i; mfma() accumulates sum_i code_i * z_i * SCALE^-1 for the 16 channels
+// against the z-limb operand, whose channel order matches chan_pos<BITS>.
 template <int BITS>
 struct CodeLoad;
 template <>
 struct CodeLoad<8> {
   using T = uint4;
-  __device__ static v4i operand(const T& w) { return v4i{int(w.x), int(w.y), int(w.z), int(w.w)}; }
+  static constexpr float INV_SCALE = 1.f;
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t col, int i, int) {
+    const v4u w = __builtin_amdgcn_raw_buffer_load_b128(r, col + i, 0, CODES_POLICY);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __device__ static v4i mfma(v4i z, const T& w, v4i acc) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(z, v4i{int(w.x), int(w.y), int(w.z), int(w.w)}, acc, 0, 0, 0);
+  }
 };
+// Nibble n (two's complement) masked into a byte's high half is the int8
+// 16*n, exactly. Even channels (low nibbles) go first, then odd ones.
+__device__ __forceinline__ v4i nibbles_x16(uint2 w) {
+  return v4i{int((w.x << 4) & 0xF0F0F0F0u), int((w.y << 4) & 0xF0F0F0F0u), int(w.x & 0xF0F0F0F0u),
+             int(w.y & 0xF0F0F0F0u)};
+}
 template <>
 struct CodeLoad<4> {
   using T = uint2;
-  // Nibble n (two's complement) masked into a byte's high half is the int8
-  // 16*n, exactly. Even channels (low nibbles) go first, then odd ones; the
-  // z-limb operand is written in the same channel order.
-  __device__ static v4i operand(const T& w) {
-    return v4i{int((w.x << 4) & 0xF0F0F0F0u), int((w.y << 4) & 0xF0F0F0F0u), int(w.x & 0xF0F0F0F0u),
-               int(w.y & 0xF0F0F0F0u)};
+  static constexpr float INV_SCALE = 0.0625f;  // bytes hold 16 * code
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t col, int i, int) {
+    const v2u w = __builtin_amdgcn_raw_buffer_load_b64(r, col + i / 2, 0, CODES_POLICY);
+    return make_uint2(w[0], w[1]);
+  }
+  __device__ static v4i mfma(v4i z, const T& w, v4i acc) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(z, nibbles_x16(w), acc, 0, 0, 0);
+  }
+};
+// 6-bit codes (code = 4 hi + lo): hi in the head's first plane as 4-bit
+// nibbles, laid out and loaded like 4-bit codes; lo as 2-bit fields in the
+// second plane (loaded separately, see HeadStep::load_lo), placed so that
+// field m of byte k (bits 8k + 2m) is operand position 4m + k. The byte 16*hi
+// (high nibble) and 4*lo (bits 2-3) do not overlap, so their bitwise or is
+// the int8 4*code: one product per block.
+template <>
+struct CodeLoad<6> {
+  using T = uint2;
+  static constexpr float INV_SCALE = 0.25f;  // bytes hold 4 * code
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t col, int i, int d) {
+    return CodeLoad<4>::load(r, col, i, d);
+  }
+  __device__ static v4i mfma(v4i z, const T& w, uint32_t l, v4i acc) {
+    const v4i lo4 = v4i{int((l << 2) & 0x0C0C0C0Cu), int(l & 0x0C0C0C0Cu), int((l >> 2) & 0x0C0C0C0Cu),
+                        int((l >> 4) & 0x0C0C0C0Cu)};
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(z, nibbles_x16(w) | lo4, acc, 0, 0, 0);
   }
 };
 
@@ -150,7 +186,8 @@ struct HeadStep {
   using SS = StepShape<D, KDA>;
   static constexpr int NT = SS::NT, NW = SS::NW, RBW = SS::RBW, KB = SS::KB, CPL = SS::CPL, NG = SS::NG;
   static constexpr int KPF = SS::KPF, NQ = SS::NQ, EP = SS::EP, PFE = SS::PFE;
-  static constexpr int CB = D * BITS / 8;  // code bytes per value column
+  static constexpr int CB = D * (BITS == 6 ? 4 : BITS) / 8;  // bytes per value column (6 bits: hi plane)
+  static constexpr int HEAD_CODE_BYTES = D * D * BITS / 8;
   static constexpr float L2E = 1.4426950408889634f;
   using CL = CodeLoad<BITS>;
   using CT = typename CL::T;
@@ -169,6 +206,7 @@ struct HeadStep {
   // Inputs of one head in registers.
   struct In {
     CT cw[RBW][KB];  // residual codes, MFMA operand order
+    uint32_t lo6[BITS == 6 ? KB : 1][BITS == 6 ? RBW : 1];  // 6 bits: lo fields of the same blocks
     uint32_t kx_raw, qx_raw;  // q_t, k_t as loaded (bf16 or fp32 bits); converted when used
     uint4 v_raw;              // v_t quad as loaded (bf16: .x, .y)
     float si, cc, gi, beta, gs, Gp;
@@ -196,6 +234,7 @@ struct HeadStep {
     const int tc = chan ? t : 0;
     const Ptr P = ptr(a, bh);
     load_codes(a, P, h, 0, RBW / 2);
+    if constexpr (BITS == 6) load_lo(a, P, h);
     __builtin_amdgcn_sched_barrier(0);  // keep these codes first in the issue order
     if constexpr (BF16) {
       h.kx_raw = static_cast<const uint16_t*>(a.k)[P.hD + tc];
@@ -253,24 +292,46 @@ struct HeadStep {
   __device__ static __forceinline__ void load_codes(const StepArgs& a, const Ptr& P, In& h, int lo, int hi) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int jl = lane & 15, il = 16 * (lane >> 4);
-    const auto rc = buf_rsrc(static_cast<const uint8_t*>(a.codes) + P.hD * CB, D * CB);
+    const auto rc = buf_rsrc(static_cast<const uint8_t*>(a.codes) + size_t(HEAD_CODE_BYTES) * (P.hD / D),
+                             HEAD_CODE_BYTES);
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       if (rb < lo || rb >= hi) continue;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int j = 16 * (wave * RBW + rb) + jl, i = 64 * kb + il;
-        const uint32_t off = j * CB + i * BITS / 8;
-        if (D >= 64 || i < D) {
-          if constexpr (BITS == 8) {
+        if (D >= 64 || i < D) h.cw[rb][kb] = CL::load(rc, uint32_t(j * CB), i, D);
+        else h.cw[rb][kb] = CT{};
+      }
+    }
+  }
+
+  // 6 bits: the lo fields of every block of this lane. The second plane holds
+  // 32-bit words W[j % 16][i / 16][j / 16] (j value column, i key channel),
+  // so a lane's words for its row blocks (consecutive j / 16) are adjacent.
+  __device__ static __forceinline__ void load_lo(const StepArgs& a, const Ptr& P, In& h) {
+    if constexpr (BITS == 6) {
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      const auto rc = buf_rsrc(static_cast<const uint8_t*>(a.codes) + size_t(HEAD_CODE_BYTES) * (P.hD / D),
+                               HEAD_CODE_BYTES);
+      constexpr int NJ = D / 16;  // column groups j / 16, and channel groups i / 16
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int g = 4 * kb + (lane >> 4);
+        const uint32_t off = uint32_t(D * D / 2) + 4u * uint32_t(((lane & 15) * NJ + g) * NJ + wave * RBW);
+        if (D >= 64 || 16 * g < D) {
+          if constexpr (RBW == 4) {
             const v4u w = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, CODES_POLICY);
-            h.cw[rb][kb] = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) h.lo6[kb][rb] = w[rb];
           } else {
+            static_assert(RBW == 2, "row blocks per wave");
             const v2u w = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, CODES_POLICY);
-            h.cw[rb][kb] = make_uint2(w[0], w[1]);
+            h.lo6[kb][0] = w[0], h.lo6[kb][1] = w[1];
           }
         } else {
-          h.cw[rb][kb] = CT{};
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) h.lo6[kb][rb] = 0u;
         }
       }
     }
@@ -440,10 +501,11 @@ struct HeadStep {
         acc[rb] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-          acc[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[kb], CL::operand(h.cw[rb][kb]), acc[rb], 0, 0, 0);
+          if constexpr (BITS == 6) acc[rb] = CL::mfma(aop[kb], h.cw[rb][kb], h.lo6[kb][rb], acc[rb]);
+          else acc[rb] = CL::mfma(aop[kb], h.cw[rb][kb], acc[rb]);
       }
       const int xs = lane >> 4;
-      const float zs = (xs == 0 ? zscale[0] : zscale[1]) * (BITS == 4 ? 0.0625f : 1.f);
+      const float zs = (xs == 0 ? zscale[0] : zscale[1]) * CL::INV_SCALE;
       if (xs < 2) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
@@ -536,7 +598,11 @@ hipError_t launch_db(const lq_dims& d, const StepArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const lq_dims& d, const StepArgs& a, hipStream_t s) {
-  return d.bits == 8 ? launch_db<D, 8>(d, a, s) : launch_db<D, 4>(d, a, s);
+  switch (d.bits) {
+    case 8: return launch_db<D, 8>(d, a, s);
+    case 6: return launch_db<D, 6>(d, a, s);
+    default: return launch_db<D, 4>(d, a, s);
+  }
 }
 
 }  // namespace

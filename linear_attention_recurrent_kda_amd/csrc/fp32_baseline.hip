@@ -94,13 +94,21 @@ __global__ void __launch_bounds__(256) dequant_kernel(lq_state st, int r, int n_
   const size_t hD = size_t(bh) * D, erow = size_t(bh) * n_ent;
   for (int idx = threadIdx.x; idx < D * D; idx += 256) {
     const int j = idx / D, i = idx % D;
+    const uint8_t* head = static_cast<const uint8_t*>(st.codes) + size_t(bh) * (D * D * BITS / 8);
     int code;
     if constexpr (BITS == 8) {
-      code = static_cast<const int8_t*>(st.codes)[(hD + j) * D + i];
+      code = int(int8_t(head[j * D + i]));
     } else {
-      const uint8_t byte = static_cast<const uint8_t*>(st.codes)[(hD + j) * (D / 2) + i / 2];
+      const uint8_t byte = head[j * (D / 2) + i / 2];
       const uint32_t nib = (i & 1) ? (byte >> 4) : (byte & 0xFu);
       code = int(nib ^ 0x8u) - 8;
+      if constexpr (BITS == 6) {  // nibble = hi; lo = 2-bit field of the second plane
+        constexpr int NJ = D / 16;
+        const int c = i & 15, p = (c & 1) ? 8 + (c >> 1) : (c >> 1);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(
+            head + D * D / 2 + 4 * (((j & 15) * NJ + (i >> 4)) * NJ + (j >> 4)));
+        code = 4 * code + int((w >> (8 * (p & 3) + 2 * (p >> 2))) & 3u);
+      }
     }
     float val = (st.row_scale[hD + i] * float(code)) * st.col_scale[hD + j];
     for (int l = 0; l < r; ++l) val = fmaf(st.ent_k[(erow + l) * D + i], st.ent_u[(erow + l) * D + j], val);
@@ -130,7 +138,11 @@ hipError_t launch_dq(const lq_dims& d, const lq_state& st, float* out, hipStream
 
 template <int D>
 hipError_t launch_dq_d(const lq_dims& d, const lq_state& st, float* out, hipStream_t s) {
-  return d.bits == 8 ? launch_dq<D, 8>(d, st, out, s) : launch_dq<D, 4>(d, st, out, s);
+  switch (d.bits) {
+    case 8: return launch_dq<D, 8>(d, st, out, s);
+    case 6: return launch_dq<D, 6>(d, st, out, s);
+    default: return launch_dq<D, 4>(d, st, out, s);
+  }
 }
 
 }  // namespace

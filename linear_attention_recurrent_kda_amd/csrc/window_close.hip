@@ -90,11 +90,38 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const int (&c)[B]) {
   }
 }
 
+// 6-bit codes (code = 4 hi + lo), two planes per head: hi in [-8, 7] as
+// 4-bit nibbles, [d_v][d_k/2] like 4-bit codes; then lo = code & 3 as 2-bit
+// fields in 32-bit words W[j % 16][i / 16][j / 16] (value column j, key
+// channel i). Channel c of a 16-channel group sits at bit
+// 8 (p % 4) + 2 (p / 4), p = c/2 for even c and 8 + c/2 for odd c.
+__device__ __forceinline__ int lo_bit(int c) {
+  const int p = (c & 1) ? 8 + (c >> 1) : (c >> 1);
+  return 8 * (p & 3) + 2 * (p >> 2);
+}
+
+template <int D>
+__device__ __forceinline__ size_t lo_word(int j, int g) {
+  constexpr int NJ = D / 16;
+  return size_t(D * D / 2) + 4 * size_t(((j & 15) * NJ + g) * NJ + (j >> 4));
+}
+
+// B codes of value column j, key channels i0..i0+B-1 (i0 % B == 0, B <= 16).
+template <int B, int D>
+__device__ __forceinline__ void load_codes6(const uint8_t* head, int j, int i0, int (&c)[B]) {
+  int hi[B];
+  load_codes<B, 4>(head + size_t(j) * (D / 2) + i0 / 2, hi);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(head + lo_word<D>(j, i0 / 16));
+#pragma unroll
+  for (int a = 0; a < B; ++a) c[a] = 4 * hi[a] + int((w >> lo_bit((i0 + a) & 15)) & 3u);
+}
+
 template <int D, int BITS, bool KDA, bool DENSE>
 __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
   constexpr int B = D / 16;
-  constexpr int Q = BITS == 8 ? 127 : 7;
-  constexpr int CB = D * BITS / 8;  // code bytes per value column
+  constexpr int Q = (1 << (BITS - 1)) - 1;  // 127, 31 or 7
+  constexpr int CB = D * BITS / 8;  // code bytes per value column (8 and 4 bits)
+  constexpr int HB = D * D * BITS / 8;  // code bytes per head
   constexpr int CH = 16;            // entries staged in LDS per fold pass
   constexpr int GL = KDA ? D : 1;   // G values per entry
   __shared__ float sh_n[2][16];     // partial squared norms (double-buffered)
@@ -102,6 +129,7 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
   __shared__ __align__(16) float sh_k[DENSE ? 1 : CH][D];
   __shared__ __align__(16) float sh_u[DENSE ? 1 : CH][D];
   __shared__ __align__(16) float sh_g[DENSE ? 1 : CH][GL];
+  __shared__ uint32_t sh_lo[BITS == 6 ? D : 1][BITS == 6 ? D / 16 : 1];  // 6-bit: lo words per column
 
   const int t = threadIdx.x, tj = t & 15, ti = t >> 4, lane = t & 63, wave = t >> 6;
   const int H = a.heads;
@@ -151,11 +179,12 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
     } else {
       Gn[0] = E > 0 ? a.eg[erow + E - 1] : 0.f;
     }
-    const uint8_t* cb = static_cast<const uint8_t*>(a.codes) + hD * CB + i0 * BITS / 8;
+    const uint8_t* cb = static_cast<const uint8_t*>(a.codes) + size_t(bh) * HB;
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) {
       int code[B];
-      load_codes<B, BITS>(cb + size_t(j0 + bb) * CB, code);
+      if constexpr (BITS == 6) load_codes6<B, D>(cb, j0 + bb, i0, code);
+      else load_codes<B, BITS>(cb + size_t(j0 + bb) * CB + i0 * BITS / 8, code);
 #pragma unroll
       for (int x = 0; x < B; ++x) M[x][bb] = (si[x] * float(code[x])) * cj[bb];
     }
@@ -339,6 +368,9 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
     m = rows_max(m);
     if (lane < 16) sh_c[0][wave][j0 + bb] = m;
   }
+  if constexpr (BITS == 6) {
+    for (int idx = t; idx < D * (D / 16); idx += 256) sh_lo[idx / (D / 16)][idx % (D / 16)] = 0u;
+  }
   __syncthreads();
   float cs[B], inv[B];
 #pragma unroll
@@ -348,7 +380,7 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
     cs[bb] = m / float(Q);
     inv[bb] = m > 0.f ? float(Q) / m : 0.f;
   }
-  uint8_t* cb = static_cast<uint8_t*>(a.codes) + hD * CB + i0 * BITS / 8;
+  uint8_t* cb = static_cast<uint8_t*>(a.codes) + size_t(bh) * HB;
 #pragma unroll
   for (int bb = 0; bb < B; ++bb) {
     int code[B];
@@ -357,7 +389,26 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
       const float qv = fminf(fmaxf(rintf(M[x][bb] * inv[bb]), -float(Q)), float(Q));
       code[x] = int(qv);
     }
-    store_codes<B, BITS>(cb + size_t(j0 + bb) * CB, code);
+    if constexpr (BITS == 6) {
+      int hi[B];
+      uint32_t lo = 0;
+#pragma unroll
+      for (int x = 0; x < B; ++x) {
+        hi[x] = code[x] >> 2;  // arithmetic: floor(code / 4)
+        lo |= uint32_t(code[x] & 3) << lo_bit((i0 + x) & 15);
+      }
+      store_codes<B, 4>(cb + size_t(j0 + bb) * (D / 2) + i0 / 2, hi);
+      atomicOr(&sh_lo[j0 + bb][i0 / 16], lo);  // the threads of a 16-channel group meet in LDS
+    } else {
+      store_codes<B, BITS>(cb + size_t(j0 + bb) * CB + i0 * BITS / 8, code);
+    }
+  }
+  if constexpr (BITS == 6) {
+    __syncthreads();
+    for (int idx = t; idx < D * (D / 16); idx += 256) {
+      const int j = idx / (D / 16), g = idx % (D / 16);
+      *reinterpret_cast<uint32_t*>(cb + lo_word<D>(j, g)) = sh_lo[j][g];
+    }
   }
   if (tj == 0) storeB<B>(a.s + hD + i0, sa);
   if (ti == 0) storeB<B>(a.c + hD + j0, cs);
@@ -379,7 +430,11 @@ hipError_t launch_b(const lq_dims& d, const CloseArgs& a, int nb, hipStream_t s)
 
 template <int D>
 hipError_t launch_d(const lq_dims& d, const CloseArgs& a, int nb, hipStream_t s) {
-  return d.bits == 8 ? launch_b<D, 8>(d, a, nb, s) : launch_b<D, 4>(d, a, nb, s);
+  switch (d.bits) {
+    case 8: return launch_b<D, 8>(d, a, nb, s);
+    case 6: return launch_b<D, 6>(d, a, nb, s);
+    default: return launch_b<D, 4>(d, a, nb, s);
+  }
 }
 
 }  // namespace

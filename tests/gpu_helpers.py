@@ -17,17 +17,43 @@ from tests.oracle_inputs import flat_steps, rel_l2  # noqa: F401
 
 
 # ---- code format (include/leapquant.h): [BH][d_v][d_k] int8, or int4 packed
+def _lo_bits() -> np.ndarray:
+    """6-bit codes: bit offset of the 2-bit low field of channel c (0..15) of a
+    16-channel group inside its 32-bit word (include/leapquant.h)."""
+    c = np.arange(16)
+    p = np.where(c % 2 == 0, c // 2, 8 + c // 2)
+    return 8 * (p % 4) + 2 * (p // 4)
+
+
+def _unpack_nibbles(u: np.ndarray) -> np.ndarray:
+    """[..][d/2] bytes -> [..][d] signed 4-bit values (channel 2m low nibble)."""
+    u = u.astype(np.int32)
+    out = np.empty(u.shape[:-1] + (2 * u.shape[-1],), np.int32)
+    out[..., 0::2], out[..., 1::2] = ((u & 0xF) ^ 8) - 8, ((u >> 4) ^ 8) - 8
+    return out
+
+
+def _pack_nibbles(x: np.ndarray) -> np.ndarray:
+    return ((x[..., 0::2] & 0xF) | ((x[..., 1::2] & 0xF) << 4)).astype(np.uint8)
+
+
 def unpack_codes(raw: np.ndarray, bits: int, d: int) -> np.ndarray:
-    """Device codes [BH][d_v][d_k*bits/8] (int8 bytes) -> math layout [BH][d_k][d_v] int32."""
+    """Device codes [BH][d_v][d_k*bits/8] (bytes) -> math layout [BH][d_k][d_v] int32."""
     raw = np.asarray(raw)
+    u = raw.view(np.uint8).reshape(-1, d, d * bits // 8)
     if bits == 8:
-        C = raw.astype(np.int32).reshape(-1, d, d)
+        Ct = raw.view(np.int8).reshape(-1, d, d).astype(np.int32)
+    elif bits == 4:
+        Ct = _unpack_nibbles(u)
     else:
-        u = raw.view(np.uint8).reshape(-1, d, d // 2).astype(np.int32)
-        lo, hi = ((u & 0xF) ^ 8) - 8, ((u >> 4) ^ 8) - 8
-        C = np.empty((u.shape[0], d, d), np.int32)
-        C[:, :, 0::2], C[:, :, 1::2] = lo, hi
-    return np.ascontiguousarray(np.swapaxes(C, 1, 2))
+        head = raw.view(np.uint8).reshape(-1, 3 * d * d // 4)
+        n, nj = head.shape[0], d // 16
+        hi = _unpack_nibbles(head[:, : d * d // 2].reshape(n, d, d // 2))           # [BH][d_v][d_k]
+        W = np.ascontiguousarray(head[:, d * d // 2:]).view("<u4").reshape(n, 16, nj, nj)  # [jl][g][jh]
+        words = W.transpose(0, 3, 1, 2).reshape(n, d, nj).astype(np.int64)         # [BH][j][g]
+        lo = (words[:, :, :, None] >> _lo_bits()[None, None, None, :]) & 3          # [BH][d_v][g][16]
+        Ct = 4 * hi + lo.reshape(hi.shape).astype(np.int32)
+    return np.ascontiguousarray(np.swapaxes(Ct, 1, 2))
 
 
 def pack_codes(C: np.ndarray, bits: int) -> np.ndarray:
@@ -35,8 +61,16 @@ def pack_codes(C: np.ndarray, bits: int) -> np.ndarray:
     Ct = np.swapaxes(np.asarray(C, np.int32), 1, 2)
     if bits == 8:
         return np.ascontiguousarray(Ct.astype(np.int8))
-    lo, hi = Ct[:, :, 0::2] & 0xF, Ct[:, :, 1::2] & 0xF
-    return np.ascontiguousarray((lo | (hi << 4)).astype(np.uint8).view(np.int8))
+    if bits == 4:
+        return np.ascontiguousarray(_pack_nibbles(Ct).view(np.int8))
+    n, d, _ = Ct.shape
+    nj = d // 16
+    hi, lo = Ct >> 2, (Ct & 3).astype(np.uint32)
+    words = (lo.reshape(n, d, nj, 16) << _lo_bits().astype(np.uint32)).sum(axis=3, dtype=np.uint32)  # [j][g]
+    W = words.reshape(n, nj, 16, nj).transpose(0, 2, 3, 1)                        # [jl][g][jh]
+    lo_bytes = np.ascontiguousarray(W.astype("<u4")).view(np.uint8).reshape(n, d * d // 4)
+    hi_bytes = _pack_nibbles(hi).reshape(n, d * d // 2)
+    return np.ascontiguousarray(np.concatenate([hi_bytes, lo_bytes], axis=1).reshape(n, d, 3 * d // 4).view(np.int8))
 
 
 def T(x: np.ndarray) -> np.ndarray:

@@ -53,7 +53,8 @@ def step(d, st, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE):
     (dict(d_k=96, d_v=96), L.LQ_ERR_SHAPE),
     (dict(d_k=128, d_v=64), L.LQ_ERR_SHAPE),
     (dict(batch=-1), L.LQ_ERR_SHAPE),
-    (dict(bits=6), L.LQ_ERR_BITS),
+    (dict(bits=5), L.LQ_ERR_BITS),
+    (dict(bits=7), L.LQ_ERR_BITS),
     (dict(w_max=0), L.LQ_ERR_CONFIG),
     (dict(w_max=65), L.LQ_ERR_CONFIG),
     (dict(n_comp=9), L.LQ_ERR_CONFIG),
@@ -134,6 +135,8 @@ def test_state_sizes():
     assert s["row_scale"] == s["col_scale"] == BH * 128 * 4 and s["buf_len"] == BH * 4
     s4 = L.state_sizes(L.Dims(128, 32, 128, w_max=16, n_comp=4, bits=4, kda=True))
     assert s4["codes"] == 128 * 32 * 128 * 64 and s4["ent_g"] == 128 * 32 * (4 + 16) * 128 * 4
+    s6 = L.state_sizes(L.Dims(64, 32, 128, w_max=16, n_comp=4, bits=6))
+    assert s6["codes"] == BH * 128 * 96  # 6-bit: two planes, 96 bytes per value column
     s0 = L.state_sizes(L.Dims(2, 3, 32, w_max=1, n_comp=0))
     assert s0["ent_k"] == 6 * 1 * 32 * 4
 

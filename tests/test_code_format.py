@@ -1,0 +1,60 @@
+"""Host-side code layouts (include/leapquant.h, lq_state.codes): the test
+helpers that pack and unpack device code bytes, checked against the layout
+definition written out by hand (CPU only)."""
+import numpy as np
+import pytest
+
+from tests import gpu_helpers as gh
+
+QMAX = {8: 127, 6: 31, 4: 7}
+
+
+@pytest.mark.parametrize("bits", [8, 6, 4])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_pack_unpack_round_trip(bits, d):
+    rng = np.random.default_rng(bits * 1000 + d)
+    Q = QMAX[bits]
+    C = rng.integers(-Q, Q + 1, size=(3, d, d)).astype(np.int32)
+    C[0, 0, :] = Q
+    C[0, 1, :] = -Q
+    raw = gh.pack_codes(C, bits)
+    assert raw.shape == (3, d, d * bits // 8)
+    assert np.array_equal(gh.unpack_codes(raw, bits, d), C)
+
+
+def _code_by_definition(head: bytes, j: int, i: int, bits: int, d: int) -> int:
+    """Code of value column j, key channel i from one head's bytes, read off
+    the header's layout definition one field at a time."""
+    if bits == 8:
+        b = head[j * d + i]
+        return b - 256 if b >= 128 else b
+    nib = (head[j * (d // 2) + i // 2] >> (4 * (i % 2))) & 0xF
+    hi = nib - 16 if nib >= 8 else nib
+    if bits == 4:
+        return hi
+    nj = d // 16
+    w = d * d // 2 + 4 * (((j % 16) * nj + i // 16) * nj + j // 16)
+    word = int.from_bytes(head[w: w + 4], "little")
+    c = i % 16
+    p = c // 2 if c % 2 == 0 else 8 + c // 2
+    lo = (word >> (8 * (p % 4) + 2 * (p // 4))) & 3
+    return 4 * hi + lo
+
+
+@pytest.mark.parametrize("bits", [8, 6, 4])
+@pytest.mark.parametrize("d", [32, 64])
+def test_layout_matches_definition(bits, d):
+    rng = np.random.default_rng(7)
+    Q = QMAX[bits]
+    C = rng.integers(-Q, Q + 1, size=(1, d, d)).astype(np.int32)   # math layout [d_k][d_v]
+    head = bytes(gh.pack_codes(C, bits).view(np.uint8).reshape(-1))
+    for j in range(d):
+        for i in range(d):
+            assert _code_by_definition(head, j, i, bits, d) == C[0, i, j], (bits, i, j)
+
+
+def test_six_bit_split():
+    """code = 4 hi + lo with hi = floor(code / 4) in [-8, 7] and lo in [0, 3]."""
+    for code in range(-31, 32):
+        hi, lo = code >> 2, code & 3
+        assert -8 <= hi <= 7 and 0 <= lo <= 3 and 4 * hi + lo == code

@@ -45,7 +45,8 @@ def _encode_case(wl, bits):
     return dims, S0.reshape(-1, wl.d_k, wl.d_v), host, R
 
 
-@pytest.mark.parametrize("name,bits", [("tiny_gdn", 8), ("qwen_gdn", 8), ("kda_int4", 4), ("kda_int4", 8)])
+@pytest.mark.parametrize("name,bits", [("tiny_gdn", 8), ("qwen_gdn", 8), ("kda_int4", 4), ("kda_int4", 8),
+                                       ("qwen_gdn", 6), ("tiny_gdn", 6)])
 def test_encode_codes_and_decomposition(name, bits):
     wl = W[name]
     if name == "kda_int4":
@@ -68,7 +69,7 @@ def test_encode_codes_and_decomposition(name, bits):
     print("end-to-end code agreement", float(np.mean(host["C"] == ref.codes)))
 
 
-@pytest.mark.parametrize("name,bits", [("tiny_gdn", 8), ("kda_int4", 4)])
+@pytest.mark.parametrize("name,bits", [("tiny_gdn", 8), ("kda_int4", 4), ("qwen_gdn", 6), ("tiny_gdn", 6)])
 def test_dequantize_matches_oracle_decode(name, bits):
     wl = W[name].replace(batch=min(W[name].batch, 4))
     dims, S0, host, R = _encode_case(wl, bits)
@@ -86,7 +87,8 @@ def lqk_state_from_host(dims, host):
 
 
 @pytest.mark.parametrize("name,bits,n_pre", [("tiny_gdn", 8, 5), ("qwen_gdn", 8, 7), ("kda_int4", 4, 9),
-                                              ("kda_int4", 8, 0), ("prefix_mix", 8, 20)])
+                                              ("kda_int4", 8, 0), ("prefix_mix", 8, 20), ("qwen_gdn", 6, 7),
+                                              ("kda_int4", 6, 9)])
 def test_single_step_from_uploaded_state(name, bits, n_pre):
     """G4: oracle state after n_pre buffered tokens, rounded to fp32 and uploaded."""
     wl = W[name]
@@ -132,6 +134,8 @@ G3_CASES = [
     ("kda_int4", 4, 48, {}),
     ("kda_int4", 8, 48, {}),
     ("prefix_mix", 8, 64, {}),
+    ("qwen_gdn", 6, 64, {}),
+    ("kda_int4", 6, 48, {}),
 ]
 
 
@@ -185,6 +189,8 @@ def test_outputs_free_running(name, bits, steps, kw):
     ("kda_int4", 8, 16, None),
     ("tiny_gdn", 8, 5, [1]),            # partial window, one sequence of two
     ("prefix_mix", 8, 11, [0, 3, 5]),   # partial windows, a close list
+    ("qwen_gdn", 6, 16, None),
+    ("tiny_gdn", 6, 5, [1]),
 ])
 def test_close_codes_and_decomposition(name, bits, n_tok, close_seqs):
     """G1 + G2 at a window close: the oracle folds the GPU's pre-close buffers;
