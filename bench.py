@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--no-fp32", action="store_true", help="skip the FP32-state baseline")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--cpu-sample", default="32x256", help="oracle sample: sequences x steps")
+    p.add_argument("--prefill-tokens", type=int, default=256,
+                   help="prompt length of the prefill-handoff leg (0: skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy three times (the reference dispatch "
                         "for scaling hardware byte counters), then exit")
@@ -280,6 +282,47 @@ def run_gpu(args, wl, bits):
     return res
 
 
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X, fp32 vector (counts packed dual-rate FP32)
+
+
+def run_prefill(wl, bits, n_tokens):
+    """Prefill handoff: the exact recurrence over a prompt of n_tokens (fp32 state
+    on chip), then the encode into LeapQuant form. ALU-bound: 7 d^2 flops per
+    head-token (decay, the two column sums S'^T k and S'^T q, the rank-one update)."""
+    import torch
+
+    from linear_attention_recurrent_kda_amd import leapquant as lqk
+    from linear_attention_recurrent_kda_amd import runner
+    from linear_attention_recurrent_kda_amd import workloads as wk
+
+    dims = runner.dims_for(wl, bits)
+    N, d = wl.batch * wl.heads, wl.d_k
+    S0 = runner.states_to_device(wk.initial_states(wl, range(wl.batch)))
+    x = wk.device_tokens(wl, n_tokens, seed=100)
+    o = torch.empty((n_tokens, N, d), dtype=torch.float32, device="cuda")
+    S = torch.empty_like(S0)
+    st = lqk.State(dims)
+    runs = []
+    for rep in range(3):
+        S.copy_(S0)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        lqk.prefill(dims, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        e1.record()
+        lqk.encode(dims, S, st)
+        e2.record()
+        torch.cuda.synchronize()
+        runs.append((e0.elapsed_time(e1) * 1e3, e1.elapsed_time(e2) * 1e3))
+    pre_us, enc_us = min(runs)
+    flops = 7.0 * d * d * N * n_tokens
+    tflops = flops / (pre_us * 1e-6) / 1e12
+    return {"prompt_tokens": n_tokens, "head_tokens_per_s": round(N * n_tokens / (pre_us * 1e-6), 1),
+            "prefill_us": round(pre_us, 1), "encode_us": round(enc_us, 1),
+            "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4)}}
+
+
 def cpu_baseline(wl, bits, sample):
     """The fp64 oracle (plain definition) on a bounded sample of the same workload."""
     import numpy as np
@@ -369,6 +412,8 @@ def main():
                                  "avg_launch_us": round(r["fp32_us"], 3),
                                  "achieved_gbs": round(r["fp32_gbs"], 1)}
         line["speedup_vs_fp32"] = round(value / fval, 3)
+    if args.prefill_tokens > 0:
+        line["prefill_handoff"] = run_prefill(wl, bits, args.prefill_tokens)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, bits, args.cpu_sample)
     print(json.dumps(line), flush=True)

@@ -169,6 +169,25 @@ int gdn_decode_fp32_baseline(const lq_dims* dims, float* S, const void* q, const
                              const void* v, const float* g, const float* beta, float* o,
                              void* stream);
 
+/* Prefill handoff: the exact gated delta rule (decay first, as
+   gdn_decode_fp32_baseline) over n_tokens prompt tokens with the fp32 state
+   held on chip, then, when st is not NULL, the encode of the final state
+   into st (as leapquant_encode: compensators, smoothing, quantization, empty
+   buffer), so that decoding starts from the prompt. The pages quantize the
+   state per window of decoded tokens (wink.run article, per-window
+   quantization; LeapQuant abstract); the prompt runs at full precision and
+   is quantized once, at the handoff.
+   S: fp32 [B*H][d_v][d_k] (transposed), the state before the prompt on
+   entry and after it on return. Tokens are time-major: q, k: [n_tokens][B][H]
+   [d_k]; v: [n_tokens][B][H][d_v] (fp32 or bf16 per act_dtype); g: fp32
+   [n_tokens][B][H] (GDN) or [n_tokens][B][H][d_k] (KDA), the log-decay;
+   beta: fp32 [n_tokens][B][H]; o: fp32 [n_tokens][B][H][d_v] (output).
+   n_tokens >= 0 (0: encode only). The method fields of dims (w_max, n_comp,
+   bits, smoothing, power_iters) are validated only when st is not NULL. */
+int leapquant_prefill(const lq_dims* dims, float* S, int32_t n_tokens, const void* q,
+                      const void* k, const void* v, const float* g, const float* beta,
+                      float* o, const lq_state* st, void* stream);
+
 /* Dense window-start state Shat_0 = sum_{e<r} k_e u_e^T + diag(s) C diag(c)
    (compensators plus residual) of every head into S_out: fp32
    [B*H][d_v][d_k] (transposed). Test helper. */

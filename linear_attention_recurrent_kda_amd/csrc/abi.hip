@@ -170,6 +170,28 @@ int gdn_decode_fp32_baseline(const lq_dims* d, float* S, const void* q, const vo
   return launched(lq::launch_baseline(*d, a, static_cast<hipStream_t>(stream)));
 }
 
+int leapquant_prefill(const lq_dims* d, float* S, int32_t n_tokens, const void* q, const void* k,
+                      const void* v, const float* g, const float* beta, float* o, const lq_state* st,
+                      void* stream) {
+  int rc = check_dims(d, st != nullptr);
+  if (rc) return rc;
+  if (n_tokens < 0) return LQ_ERR_CONFIG;
+  if (empty(d)) return LQ_OK;
+  if (!S) return LQ_ERR_NULL;
+  if (!aligned(S, 16)) return LQ_ERR_ALIGN;
+  if (n_tokens > 0 && (rc = check_acts(d, q, k, v, g, beta, o))) return rc;
+  if (st && (rc = check_state(d, st, 1))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_tokens > 0) {
+    lq::PrefillArgs a{S, q, k, v, g, beta, o, n_tokens, d->batch * d->heads};
+    if ((rc = launched(lq::launch_prefill(*d, a, s)))) return rc;
+  }
+  if (!st) return LQ_OK;
+  lq::CloseArgs a = close_args(d, st);  // the handoff: encode the prompt's final state
+  a.S = S;
+  return launched(lq::launch_close(*d, a, d->batch * d->heads, s));
+}
+
 int leapquant_dequantize(const lq_dims* d, const lq_state* st, float* S_out, void* stream) {
   int rc = check_dims(d, true);
   if (rc) return rc;

@@ -59,6 +59,19 @@ struct BaselineArgs {
   float* o;
 };
 
+struct PrefillArgs {
+  float* S;  // [BH][D][D] fp32, value-column major (in/out)
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  float* o;
+  int n_tokens;
+  int n_heads;
+};
+
+hipError_t launch_prefill(const lq_dims& d, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_step(const lq_dims& d, const StepArgs& a, hipStream_t stream);
 hipError_t launch_close(const lq_dims& d, const CloseArgs& a, int n_blocks, hipStream_t stream);
 hipError_t launch_baseline(const lq_dims& d, const BaselineArgs& a, hipStream_t stream);

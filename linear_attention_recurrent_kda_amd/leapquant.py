@@ -25,7 +25,8 @@ LQ_STATE_NBUF = 8
 STATE_FIELDS = ("codes", "row_scale", "col_scale", "ent_k", "ent_u", "ent_g", "buf_len", "err")
 
 EXPORTS = ("lq_state_sizes", "leapquant_encode", "leapquant_decode_step", "leapquant_window_close",
-           "gdn_decode_fp32_baseline", "leapquant_dequantize", "lq_close_list", "lq_status_string")
+           "gdn_decode_fp32_baseline", "leapquant_prefill", "leapquant_dequantize", "lq_close_list",
+           "lq_status_string")
 
 
 class CDims(ctypes.Structure):
@@ -51,6 +52,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "leapquant_decode_step": (ctypes.c_int, [pd, ps, P, P, P, P, P, P, P]),
         "leapquant_window_close": (ctypes.c_int, [pd, ps, P, I32, P, P]),
         "gdn_decode_fp32_baseline": (ctypes.c_int, [pd, P, P, P, P, P, P, P, P]),
+        "leapquant_prefill": (ctypes.c_int, [pd, P, I32, P, P, P, P, P, P, ps, P]),
         "leapquant_dequantize": (ctypes.c_int, [pd, ps, P, P]),
         "lq_close_list": (I32, [P, P, I32, I64, P]),
         "lq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -208,6 +210,18 @@ def fp32_baseline_step(dims: Dims, S: torch.Tensor, q, k, v, g, beta, o) -> None
     cd = dims.c()
     _check("gdn_decode_fp32_baseline", _lib.gdn_decode_fp32_baseline(
         ctypes.byref(cd), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o), _stream()))
+
+
+def prefill(dims: Dims, S: torch.Tensor, q, k, v, g, beta, o, st: Optional[State] = None) -> None:
+    """Exact recurrence over a time-major prompt chunk (q, k, v: [L][B*H][d]; g:
+    [L][B*H] or [L][B*H][d]; beta: [L][B*H]; o: [L][B*H][d]) on the fp32 state S
+    ([B*H][d_v][d_k], in/out); then encode S into st when st is given."""
+    cd = dims.c()
+    n_tokens = 0 if q is None else int(q.shape[0])
+    cs = st.c() if st is not None else None
+    _check("leapquant_prefill", _lib.leapquant_prefill(
+        ctypes.byref(cd), _ptr(S), n_tokens, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
+        ctypes.byref(cs) if cs is not None else None, _stream()))
 
 
 def dequantize(dims: Dims, st: State, out: torch.Tensor) -> None:

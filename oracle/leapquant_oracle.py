@@ -467,6 +467,31 @@ def fold_window(S0, buf_k, buf_u, buf_G, n, kda: bool) -> np.ndarray:
     return np.exp(Gn)[:, None, None] * S0 + np.einsum("nm,nmi,nmj->nij", rho, buf_k, buf_u)
 
 
+# ---------------------------------------------------------------------------
+# Prefill handoff. [article] and [abstract] quantize the recurrent state once
+# per window of decoded tokens; the prompt before decoding runs at full
+# precision (reading: the exact recurrence) and its final state enters the
+# LeapQuant form once, by the encode above, as a window start with an empty
+# buffer.
+# ---------------------------------------------------------------------------
+def prefill(S_init, tokens: Iterable[Dict[str, np.ndarray]]):
+    """The exact gated delta rule over the prompt tokens in order; returns
+    (S after the prompt, [o_t for every prompt token])."""
+    S = _f64(S_init)
+    outs: List[np.ndarray] = []
+    for tk in tokens:
+        S, o, _ = exact_step(S, _f64(tk["q"]), _f64(tk["k"]), _f64(tk["v"]), tk["g"], tk["beta"])
+        outs.append(o)
+    return S, outs
+
+
+def prefill_handoff(S_init, tokens, *, r: int, T: int = 4, bits: int = 8, smoothing: bool = True):
+    """prefill(), then the encode of its final state: the window-start state
+    decoding continues from. Returns (Encoded, S after the prompt, outputs)."""
+    S, outs = prefill(S_init, tokens)
+    return encode(S, r, T, bits, smoothing), S, outs
+
+
 def outlier_ratio(X: np.ndarray) -> np.ndarray:
     """max |X| / median |X| per head (the pages' outlier-to-median measure,
     [article] residual-smoothing paragraph; the exact statistic is a reading)."""

@@ -104,6 +104,24 @@ def test_null_and_alignment_validation():
     assert L.raw_call("leapquant_dequantize", ctypes.byref(d), ctypes.byref(state()), None, None) == L.LQ_ERR_NULL
 
 
+def test_prefill_validation():
+    d = dims()
+    pf = lambda S, n, q=FAKE, st=None: L.raw_call("leapquant_prefill", ctypes.byref(d), S, n, q, FAKE, FAKE, FAKE,
+                                                  FAKE, FAKE, st, None)
+    assert pf(FAKE, -1) == L.LQ_ERR_CONFIG
+    assert pf(None, 4) == L.LQ_ERR_NULL
+    assert pf(FAKE + 4, 4) == L.LQ_ERR_ALIGN
+    assert pf(FAKE, 4, q=None) == L.LQ_ERR_NULL
+    assert pf(FAKE, 4, q=FAKE + 2) == L.LQ_ERR_ALIGN
+    assert pf(FAKE, 0, st=ctypes.byref(state(codes=None))) == L.LQ_ERR_NULL
+    bad = dims(bits=5)
+    assert L.raw_call("leapquant_prefill", ctypes.byref(bad), FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                      ctypes.byref(state()), None) == L.LQ_ERR_BITS
+    e = dims(batch=0)
+    assert L.raw_call("leapquant_prefill", ctypes.byref(e), None, 4, None, None, None, None, None, None, None,
+                      None) == L.LQ_OK
+
+
 def test_close_list_argument_validation():
     d = dims()
     st = state()

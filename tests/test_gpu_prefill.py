@@ -1,0 +1,99 @@
+"""GPU parity of the prefill handoff (leapquant_prefill through the C ABI)
+against the fp64 oracle's prefill: the prompt's outputs and final state, the
+encode at the handoff, and decoding on from the handed-over state."""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_recurrent_kda_amd import leapquant as lqk
+from linear_attention_recurrent_kda_amd import runner
+from linear_attention_recurrent_kda_amd import workloads as wk
+from oracle import leapquant_oracle as lq
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+W = wk.WORKLOADS
+
+CASES = [
+    ("tiny_gdn", dict(batch=2, heads=3)),
+    ("qwen_gdn", dict(batch=4)),                 # bf16 activations, d = 128
+    ("kda_int4", dict(batch=2)),                 # per-channel decay
+    ("tiny_gdn", dict(batch=2, heads=2, d_k=64, d_v=64, kda=True)),
+]
+
+
+def _prompt(wl, L):
+    raw = wk.TokenStream(wl).next(L)
+    return raw, gh.flat_steps(raw)
+
+
+@pytest.mark.parametrize("name,kw", CASES)
+def test_prefill_matches_exact_recurrence(name, kw):
+    """The prompt's outputs and final state against the exact fp64 recurrence
+    (fp32 state on the GPU: 1e-5 relative over 48 tokens)."""
+    wl = W[name].replace(**kw)
+    L = 48
+    dims = runner.dims_for(wl)
+    S0 = wk.initial_states(wl, range(wl.batch))
+    S = runner.states_to_device(S0)
+    raw, toks = _prompt(wl, L)
+    dev = runner.upload_tokens(raw, wl.act_bf16)
+    N, d = wl.batch * wl.heads, wl.d_k
+    o = torch.empty((L, N, d), dtype=torch.float32, device="cuda")
+    lqk.prefill(dims, S, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], o)
+    torch.cuda.synchronize()
+    S_ref, outs = lq.prefill(S0.reshape(N, d, d).astype(np.float64), toks)
+    o_gpu = o.cpu().numpy()
+    worst = max(gh.rel_l2(o_gpu[t], outs[t]) for t in range(L))
+    s_err = gh.rel_l2(gh.T(S.cpu().numpy()), S_ref)
+    print(name, kw, "prefill max rel L2 o", worst, "state", s_err)
+    assert worst <= 1e-5 and s_err <= 1e-5
+
+
+@pytest.mark.parametrize("name,kw,bits", [("qwen_gdn", dict(batch=4), 8), ("kda_int4", dict(batch=2), 4),
+                                          ("tiny_gdn", dict(batch=2, heads=3), 6)])
+def test_handoff_encode_and_decode_on(name, kw, bits):
+    """The encode at the handoff equals leapquant_encode of the prompt's final
+    state (bit for bit, G1/G2 on it), and decoding on from the handed-over
+    state matches the oracle's buffered decode from that same state."""
+    wl = W[name].replace(**kw)
+    L, n_dec = 40, 12
+    dims = runner.dims_for(wl, bits)
+    N, d = wl.batch * wl.heads, wl.d_k
+    S0 = wk.initial_states(wl, range(wl.batch))
+    S = runner.states_to_device(S0)
+    raw = wk.TokenStream(wl).next(L + n_dec)
+    dev = runner.upload_tokens(raw, wl.act_bf16)
+    toks = gh.flat_steps(raw)
+    st = lqk.State(dims)
+    o = torch.empty((L, N, d), dtype=torch.float32, device="cuda")
+    lqk.prefill(dims, S, dev["q"][:L], dev["k"][:L], dev["v"][:L], dev["g"][:L], dev["beta"][:L], o, st)
+    # the same encode, called directly with the pre-quantisation residual
+    st2 = lqk.State(dims)
+    dbg = torch.empty((N, d, d), dtype=torch.float32, device="cuda")
+    lqk.encode(dims, S, st2, dbg)
+    a, b = gh.download_state(st, dims), gh.download_state(st2, dims)
+    for f in lqk.STATE_FIELDS:
+        assert np.array_equal(a[f], b[f]), f
+    R = gh.T(dbg.cpu().numpy())
+    g1 = gh.g1_check(R, a, bits, wl.smoothing)
+    S_fin = gh.T(S.cpu().numpy()).astype(np.float64)
+    rebuilt = np.einsum("nli,nlj->nij", a["comp_k"].astype(np.float64), a["comp_u"]) + R
+    g2 = np.max(np.linalg.norm(rebuilt - S_fin, axis=(1, 2)) / np.linalg.norm(S_fin, axis=(1, 2)))
+    print(name, bits, g1, "G2", g2)
+    assert g1["same"] >= 0.9999 and g1["max_diff"] <= 1 and g1["s_exact"] and g1["c_ulps"] <= 2.0
+    assert g2 <= 1e-6
+    # decode on: n_dec tokens inside the first window (no close), oracle from the GPU's encoding
+    bo = lq.BufferedOracle(S_fin, np.full(N, 10 ** 6), np.zeros(N), w_max=wl.w_max, r=wl.n_comp,
+                           T=wl.power_iters, bits=bits, smoothing=wl.smoothing, kda=wl.kda)
+    bo.base = gh.encoded_of(a)
+    out = torch.empty((N, d), dtype=torch.float32, device="cuda")
+    worst = 0.0
+    for i in range(min(n_dec, wl.w_max)):
+        t = L + i
+        lqk.decode_step(dims, st, dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], out)
+        o_ref, _ = bo.step(toks[t]["q"], toks[t]["k"], toks[t]["v"], toks[t]["g"], toks[t]["beta"])
+        worst = max(worst, gh.rel_l2(out.cpu().numpy(), o_ref))
+    print("decode after handoff max rel L2", worst)
+    assert worst <= 1e-5
