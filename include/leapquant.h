@@ -188,6 +188,31 @@ int leapquant_prefill(const lq_dims* dims, float* S, int32_t n_tokens, const voi
                       const void* k, const void* v, const float* g, const float* beta,
                       float* o, const lq_state* st, void* stream);
 
+/* Prefix-cache snapshots. At a window boundary the buffer is empty and a
+   head's state is its codes, scales and compensators (LeapQuant abstract;
+   wink.run article, prefix caching and memory paragraphs), which is all a
+   snapshot keeps. One record per head, in this order: codes
+   (d_k*d_v*bits/8 bytes, the layout of lq_state.codes), row scales (4*d_k),
+   column scales (4*d_v), compensator keys (4*r*d_k), compensator values
+   (4*r*d_v). snap: [n_seq][H][record] (or [B][H][record] when seq_ids is
+   NULL), 16-byte aligned, caller-owned. */
+
+/* Host-only: bytes of one head's snapshot record. */
+int lq_snapshot_bytes(const lq_dims* dims, size_t* bytes_per_head);
+
+/* Copy the state of the listed sequences (NULL: all) into snap. Every listed
+   head must be at a window boundary (buf_len == 0); a head that is not is
+   skipped, its record left as it was, and LQ_DEVERR_BAD_LEN is or-ed into
+   *st->err. Ids outside [0, B) set LQ_DEVERR_BAD_SEQ. */
+int leapquant_snapshot(const lq_dims* dims, const lq_state* st, const int32_t* seq_ids,
+                       int32_t n_seq, void* snap, void* stream);
+
+/* Write snapshot records back into the listed sequences: codes, scales and
+   compensators, compensator G = 0, buf_len = 0 (a window start). The
+   records of snap are taken in the same order as seq_ids. */
+int leapquant_restore(const lq_dims* dims, const lq_state* st, const int32_t* seq_ids,
+                      int32_t n_seq, const void* snap, void* stream);
+
 /* Dense window-start state Shat_0 = sum_{e<r} k_e u_e^T + diag(s) C diag(c)
    (compensators plus residual) of every head into S_out: fp32
    [B*H][d_v][d_k] (transposed). Test helper. */

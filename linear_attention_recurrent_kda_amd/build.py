@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libleapquant.so")
-SOURCES = ["abi.hip", "decode_step.hip", "window_close.hip", "fp32_baseline.hip", "prefill.hip"]
+SOURCES = ["abi.hip", "decode_step.hip", "window_close.hip", "fp32_baseline.hip", "prefill.hip", "snapshot.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

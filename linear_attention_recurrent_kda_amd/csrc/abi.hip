@@ -192,6 +192,61 @@ int leapquant_prefill(const lq_dims* d, float* S, int32_t n_tokens, const void* 
   return launched(lq::launch_close(*d, a, d->batch * d->heads, s));
 }
 
+int lq_snapshot_bytes(const lq_dims* d, size_t* bytes_per_head) {
+  int rc = check_dims(d, true);
+  if (rc) return rc;
+  if (!bytes_per_head) return LQ_ERR_NULL;
+  const size_t D = size_t(d->d_k);
+  *bytes_per_head = D * D * size_t(d->bits) / 8 + 2 * 4 * D + 2 * 4 * size_t(d->n_comp) * D;
+  return LQ_OK;
+}
+
+namespace {
+
+int snapshot_call(const lq_dims* d, const lq_state* st, const int32_t* seq_ids, int32_t n_seq, const void* snap,
+                  bool save, void* stream) {
+  int rc = check_dims(d, true);
+  if (rc) return rc;
+  if (seq_ids && (n_seq < 0 || n_seq > d->batch)) return LQ_ERR_CONFIG;
+  if (empty(d) || (seq_ids && n_seq == 0)) return LQ_OK;
+  if ((rc = check_state(d, st, 1))) return rc;
+  if (!snap) return LQ_ERR_NULL;
+  if (!aligned(snap, 16) || (seq_ids && !aligned(seq_ids, 4))) return LQ_ERR_ALIGN;
+  lq::SnapshotArgs a{};
+  a.codes = st->codes;
+  a.s = st->row_scale;
+  a.c = st->col_scale;
+  a.ek = st->ent_k;
+  a.eu = st->ent_u;
+  a.eg = st->ent_g;
+  a.blen = st->buf_len;
+  a.err = st->err;
+  a.seq_ids = seq_ids;
+  a.snap = const_cast<void*>(snap);
+  lq_snapshot_bytes(d, &a.record_bytes);
+  a.batch = d->batch;
+  a.heads = d->heads;
+  a.d = d->d_k;
+  a.r = d->n_comp;
+  a.w_max = d->w_max;
+  a.bits = d->bits;
+  a.kda = d->decay_per_channel;
+  const int n_blocks = (seq_ids ? n_seq : d->batch) * d->heads;
+  return launched(lq::launch_snapshot(a, n_blocks, save, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int leapquant_snapshot(const lq_dims* d, const lq_state* st, const int32_t* seq_ids, int32_t n_seq, void* snap,
+                       void* stream) {
+  return snapshot_call(d, st, seq_ids, n_seq, snap, true, stream);
+}
+
+int leapquant_restore(const lq_dims* d, const lq_state* st, const int32_t* seq_ids, int32_t n_seq,
+                      const void* snap, void* stream) {
+  return snapshot_call(d, st, seq_ids, n_seq, snap, false, stream);
+}
+
 int leapquant_dequantize(const lq_dims* d, const lq_state* st, float* S_out, void* stream) {
   int rc = check_dims(d, true);
   if (rc) return rc;

@@ -71,6 +71,28 @@ struct PrefillArgs {
   int n_heads;
 };
 
+struct SnapshotArgs {
+  void* codes;
+  float* s;
+  float* c;
+  float* ek;
+  float* eu;
+  float* eg;
+  int32_t* blen;
+  int32_t* err;
+  const int32_t* seq_ids;  // NULL: all sequences
+  void* snap;              // [n_seq][heads][record_bytes]
+  size_t record_bytes;
+  int batch;
+  int heads;
+  int d;
+  int r;
+  int w_max;
+  int bits;
+  int kda;
+};
+
+hipError_t launch_snapshot(const SnapshotArgs& a, int n_blocks, bool save, hipStream_t stream);
 hipError_t launch_prefill(const lq_dims& d, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_step(const lq_dims& d, const StepArgs& a, hipStream_t stream);
 hipError_t launch_close(const lq_dims& d, const CloseArgs& a, int n_blocks, hipStream_t stream);

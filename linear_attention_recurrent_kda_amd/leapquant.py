@@ -25,8 +25,8 @@ LQ_STATE_NBUF = 8
 STATE_FIELDS = ("codes", "row_scale", "col_scale", "ent_k", "ent_u", "ent_g", "buf_len", "err")
 
 EXPORTS = ("lq_state_sizes", "leapquant_encode", "leapquant_decode_step", "leapquant_window_close",
-           "gdn_decode_fp32_baseline", "leapquant_prefill", "leapquant_dequantize", "lq_close_list",
-           "lq_status_string")
+           "gdn_decode_fp32_baseline", "leapquant_prefill", "lq_snapshot_bytes", "leapquant_snapshot",
+           "leapquant_restore", "leapquant_dequantize", "lq_close_list", "lq_status_string")
 
 
 class CDims(ctypes.Structure):
@@ -53,6 +53,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "leapquant_window_close": (ctypes.c_int, [pd, ps, P, I32, P, P]),
         "gdn_decode_fp32_baseline": (ctypes.c_int, [pd, P, P, P, P, P, P, P, P]),
         "leapquant_prefill": (ctypes.c_int, [pd, P, I32, P, P, P, P, P, P, ps, P]),
+        "lq_snapshot_bytes": (ctypes.c_int, [pd, ctypes.POINTER(SZ)]),
+        "leapquant_snapshot": (ctypes.c_int, [pd, ps, P, I32, P, P]),
+        "leapquant_restore": (ctypes.c_int, [pd, ps, P, I32, P, P]),
         "leapquant_dequantize": (ctypes.c_int, [pd, ps, P, P]),
         "lq_close_list": (I32, [P, P, I32, I64, P]),
         "lq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -222,6 +225,29 @@ def prefill(dims: Dims, S: torch.Tensor, q, k, v, g, beta, o, st: Optional[State
     _check("leapquant_prefill", _lib.leapquant_prefill(
         ctypes.byref(cd), _ptr(S), n_tokens, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
         ctypes.byref(cs) if cs is not None else None, _stream()))
+
+
+def snapshot_bytes(dims: Dims) -> int:
+    """Bytes of one head's snapshot record."""
+    out = ctypes.c_size_t()
+    cd = dims.c()
+    _check("lq_snapshot_bytes", _lib.lq_snapshot_bytes(ctypes.byref(cd), ctypes.byref(out)))
+    return int(out.value)
+
+
+def snapshot(dims: Dims, st: State, snap: torch.Tensor, seq_ids: Optional[torch.Tensor] = None) -> None:
+    """Copy the listed sequences' window-boundary state into snap ([n][H][record] bytes)."""
+    cd, cs = dims.c(), st.c()
+    n = 0 if seq_ids is None else seq_ids.numel()
+    _check("leapquant_snapshot", _lib.leapquant_snapshot(ctypes.byref(cd), ctypes.byref(cs), _ptr(seq_ids), n,
+                                                         _ptr(snap), _stream()))
+
+
+def restore(dims: Dims, st: State, snap: torch.Tensor, seq_ids: Optional[torch.Tensor] = None) -> None:
+    cd, cs = dims.c(), st.c()
+    n = 0 if seq_ids is None else seq_ids.numel()
+    _check("leapquant_restore", _lib.leapquant_restore(ctypes.byref(cd), ctypes.byref(cs), _ptr(seq_ids), n,
+                                                       _ptr(snap), _stream()))
 
 
 def dequantize(dims: Dims, st: State, out: torch.Tensor) -> None:

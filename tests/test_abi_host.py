@@ -122,6 +122,21 @@ def test_prefill_validation():
                       None) == L.LQ_OK
 
 
+def test_snapshot_sizes_and_validation():
+    assert L.snapshot_bytes(L.Dims(64, 32, 128, n_comp=4, bits=8)) == 128 * 128 + 8 * 128 + 8 * 4 * 128
+    assert L.snapshot_bytes(L.Dims(64, 32, 128, n_comp=4, bits=4)) == 128 * 64 + 8 * 128 + 8 * 4 * 128
+    assert L.snapshot_bytes(L.Dims(1, 1, 32, n_comp=2, bits=6)) == 32 * 24 + 8 * 32 + 8 * 2 * 32
+    d = dims()
+    for fn in ("leapquant_snapshot", "leapquant_restore"):
+        call = lambda st, ids, n, snap: L.raw_call(fn, ctypes.byref(d), ctypes.byref(st), ids, n, snap, None)
+        assert call(state(), None, 0, None) == L.LQ_ERR_NULL
+        assert call(state(), None, 0, FAKE + 4) == L.LQ_ERR_ALIGN
+        assert call(state(), FAKE, 3, FAKE) == L.LQ_ERR_CONFIG
+        assert call(state(), FAKE, 0, None) == L.LQ_OK          # empty list: nothing to do
+        assert call(state(ent_k=None), None, 0, FAKE) == L.LQ_ERR_NULL
+        assert L.raw_call(fn, ctypes.byref(dims(bits=5)), ctypes.byref(state()), None, 0, FAKE, None) == L.LQ_ERR_BITS
+
+
 def test_close_list_argument_validation():
     d = dims()
     st = state()
