@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--layers", type=int, default=8)
     p.add_argument("--workload", default="qwen_gdn")
     p.add_argument("--bits", type=int, default=None)
+    p.add_argument("--power-iters", type=int, default=None, help="power iterations per compensator")
+    p.add_argument("--warm-start", action="store_true",
+                   help="start each close's power method from the closing window's compensators")
     p.add_argument("--no-fp32", action="store_true", help="skip the FP32-state baseline")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--cpu-sample", default="32x256", help="oracle sample: sequences x steps")
@@ -366,6 +369,10 @@ def main():
     from linear_attention_recurrent_kda_amd import workloads as wk
 
     wl = wk.WORKLOADS[args.workload]
+    if args.power_iters is not None:
+        wl = wl.replace(power_iters=args.power_iters)
+    if args.warm_start:
+        wl = wl.replace(warm_start=True)
     bits = wl.bits if args.bits is None else args.bits
     r = run_gpu(args, wl, bits)
     value = r["head_tokens"] / r["wall"]
@@ -389,6 +396,7 @@ def main():
                         f"{args.layers} layers' state sets advanced per step",
             "batch": wl.batch, "heads": wl.heads, "d_k": wl.d_k, "d_v": wl.d_v, "window": wl.window,
             "n_comp": wl.n_comp, "state_bits": bits, "layers": args.layers,
+            "power_iters": wl.power_iters, "warm_start": wl.warm_start,
             "state_mb_per_layer": round(r["state_mb"], 1),
         },
         "roofline": {

@@ -79,6 +79,12 @@ typedef struct lq_dims {
   int32_t act_dtype;         /* LQ_ACT_F32 or LQ_ACT_BF16 for q, k, v */
   int32_t smoothing;         /* 1: per-key-row smoothing scales; 0: s == 1 */
   int32_t power_iters;       /* T power iterations per compensator, 1..64 */
+  int32_t warm_start;        /* 0: every close starts the power method from the fixed
+                                SplitMix64 vectors; 1: a close starts compensator l from
+                                the head's current compensator value u_l (the window that
+                                is closing), falling back to the fixed vector where u_l is
+                                zero. A variant, not on the pages; encode always starts
+                                from the fixed vectors. */
 } lq_dims;
 
 /* The LeapQuant state of all B*H heads (device buffers owned by the caller).

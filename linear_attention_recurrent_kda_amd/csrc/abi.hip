@@ -26,6 +26,7 @@ int check_dims(const lq_dims* d, bool method) {
     if (d->n_comp < 0 || d->n_comp > 8) return LQ_ERR_CONFIG;
     if (d->power_iters < 1 || d->power_iters > 64) return LQ_ERR_CONFIG;
     if (d->smoothing != 0 && d->smoothing != 1) return LQ_ERR_CONFIG;
+    if (d->warm_start != 0 && d->warm_start != 1) return LQ_ERR_CONFIG;
   }
   return LQ_OK;
 }
@@ -86,6 +87,7 @@ lq::CloseArgs close_args(const lq_dims* d, const lq_state* st) {
   a.w_max = d->w_max;
   a.T = d->power_iters;
   a.smoothing = d->smoothing;
+  a.warm = d->warm_start;
   return a;
 }
 
@@ -276,7 +278,7 @@ const char* lq_status_string(int status) {
     case LQ_ERR_NULL: return "a required pointer is NULL";
     case LQ_ERR_SHAPE: return "unsupported shape (d_k == d_v in {32, 64, 128}, batch, heads >= 0)";
     case LQ_ERR_BITS: return "bits must be 4, 6 or 8";
-    case LQ_ERR_CONFIG: return "parameter out of range (w_max, n_comp, power_iters, flags, close list)";
+    case LQ_ERR_CONFIG: return "parameter out of range (w_max, n_comp, power_iters, flags, token or close list)";
     case LQ_ERR_LAUNCH: return "HIP kernel launch failed";
     case LQ_ERR_ALIGN: return "buffer not aligned (16 bytes for state buffers and dense states)";
     default: return "unknown status";

@@ -47,6 +47,7 @@ struct CloseArgs {
   int w_max;
   int T;
   int smoothing;
+  int warm;                // start compensator l from the current entry l's value (close only)
 };
 
 struct BaselineArgs {

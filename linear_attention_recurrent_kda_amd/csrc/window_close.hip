@@ -250,12 +250,23 @@ __global__ void __launch_bounds__(256) close_kernel(CloseArgs a) {
     for (int x = 0; x < B; ++x) kk[x] = w[x] = 0.f;
     if (live) {
       float p = 0.f;
+      if (!DENSE && a.warm) {
+        // warm start: the value of compensator l of the window being closed
+        // (entry l is rewritten only after this compensator is extracted)
+        loadB<B>(a.eu + (erow + l) * D + j0, v);
 #pragma unroll
-      for (int bb = 0; bb < B; ++bb) {
-        v[bb] = start_vec(l, j0 + bb, D);
-        p = fmaf(v[bb], v[bb], p);
+        for (int bb = 0; bb < B; ++bb) p = fmaf(v[bb], v[bb], p);
+        p = group_sum<16>(p);  // the same total in every row
       }
-      p = group_sum<16>(p);
+      if (!(p > 0.f) || !isfinite(p)) {  // cold start, or no usable warm vector
+        p = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb) {
+          v[bb] = start_vec(l, j0 + bb, D);
+          p = fmaf(v[bb], v[bb], p);
+        }
+        p = group_sum<16>(p);
+      }
       const float inv_nv = __builtin_amdgcn_rsqf(p);
 #pragma unroll
       for (int bb = 0; bb < B; ++bb) v[bb] *= inv_nv;

@@ -32,7 +32,7 @@ EXPORTS = ("lq_state_sizes", "leapquant_encode", "leapquant_decode_step", "leapq
 class CDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "heads", "d_k", "d_v", "w_max", "n_comp", "bits", "decay_per_channel", "act_dtype",
-        "smoothing", "power_iters")]
+        "smoothing", "power_iters", "warm_start")]
 
 
 class CState(ctypes.Structure):
@@ -98,11 +98,12 @@ class Dims:
     bf16: bool = False
     smoothing: bool = True
     power_iters: int = 4
+    warm_start: bool = False
 
     def c(self) -> CDims:
         return CDims(self.batch, self.heads, self.d, self.d, self.w_max, self.n_comp, self.bits,
                      int(self.kda), LQ_ACT_BF16 if self.bf16 else LQ_ACT_F32, int(self.smoothing),
-                     self.power_iters)
+                     self.power_iters, int(self.warm_start))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

@@ -22,7 +22,7 @@ from .workloads import Workload, window_lengths, window_offsets
 def dims_for(wl: Workload, bits: Optional[int] = None) -> lqk.Dims:
     return lqk.Dims(batch=wl.batch, heads=wl.heads, d=wl.d_k, w_max=wl.w_max, n_comp=wl.n_comp,
                     bits=wl.bits if bits is None else bits, kda=wl.kda, bf16=wl.act_bf16,
-                    smoothing=wl.smoothing, power_iters=wl.power_iters)
+                    smoothing=wl.smoothing, power_iters=wl.power_iters, warm_start=wl.warm_start)
 
 
 def upload_tokens(tok: Dict[str, np.ndarray], bf16: bool, device="cuda") -> Dict[str, torch.Tensor]:

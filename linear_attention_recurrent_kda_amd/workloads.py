@@ -66,6 +66,7 @@ class Workload:
     mixed_window: bool = False     # W=16 for even sequences, 32 for odd
     smoothing: bool = True
     power_iters: int = 4
+    warm_start: bool = False       # compensators start from the closing window's (a variant)
     seed: int = 0
 
     @property

@@ -107,7 +107,7 @@ def exact_step(S, q, k, v, g, beta):
 # few high-precision rank-one outer products shaped like token updates; the
 # rest is smoothed per key row and quantised once per window.
 # ---------------------------------------------------------------------------
-def extract_compensators(S: np.ndarray, r: int, T: int):
+def extract_compensators(S: np.ndarray, r: int, T: int, start: Optional[np.ndarray] = None):
     """E2: r compensators by a fixed-iteration power method with deflation.
 
     For l = 0..r-1: v <- v0[l]/|v0[l]|; T times: kappa = M v, k = kappa/|kappa|,
@@ -115,6 +115,8 @@ def extract_compensators(S: np.ndarray, r: int, T: int):
     least-squares value for that key) and M <- M - k w^T.
     Degenerate head (|kappa|^2 or |w|^2 zero or not finite): compensators
     l..r-1 are zero and M is left as it is.
+    start [N][r][d_v] (warm start, not on the pages): where start[n, l] has a
+    finite nonzero norm it replaces the fixed start vector v0[l] of head n.
     Returns (comp_k [N][r][d_k], comp_u [N][r][d_v], residual M [N][d_k][d_v]).
     """
     M = np.array(S, dtype=np.float64, copy=True)
@@ -127,6 +129,11 @@ def extract_compensators(S: np.ndarray, r: int, T: int):
         for l in range(r):
             ok = live.copy()
             v = np.repeat((v0[l] / np.sqrt(np.sum(v0[l] ** 2)))[None, :], N, axis=0)
+            if start is not None:
+                sv = _f64(start[:, l])
+                ns = np.sum(sv * sv, axis=1)
+                use = np.isfinite(ns) & (ns > 0)
+                v = np.where(use[:, None], sv / np.sqrt(np.where(use, ns, 1.0))[:, None], v)
             k = np.zeros((N, dk))
             w = np.zeros((N, dv))
             for _ in range(T):
@@ -189,9 +196,11 @@ class Encoded:
                        self.codes[idx], resid, self.quantized)
 
 
-def encode(S, r: int, T: int, bits: int, smoothing: bool = True, quantize: bool = True) -> Encoded:
-    """Enc(S) = E1..E4 (E1: work on a float64 copy of S)."""
-    ck, cu, R = extract_compensators(S, r, T)
+def encode(S, r: int, T: int, bits: int, smoothing: bool = True, quantize: bool = True,
+           start: Optional[np.ndarray] = None) -> Encoded:
+    """Enc(S) = E1..E4 (E1: work on a float64 copy of S); start as in
+    extract_compensators (warm-started compensators)."""
+    ck, cu, R = extract_compensators(S, r, T, start)
     s, c, C = smooth_quantize(R, bits, smoothing)
     return Encoded(ck, cu, s, c, C, R, quantize)
 
@@ -224,7 +233,8 @@ class CloseEvent:
 
 def run_dense(S_init, tokens: Iterable[Dict[str, np.ndarray]], win_len, win_off, *, r: int,
               T: int = 4, bits: int = 8, smoothing: bool = True, quantize: bool = True,
-              record: bool = False, rounding_noise: float = 0.0, noise_seed: int = 0):
+              record: bool = False, rounding_noise: float = 0.0, noise_seed: int = 0,
+              warm_start: bool = False):
     """Run LeapQuant decoding as its plain definition.
 
     S <- Dec(Enc(S_init)); for each token: S <- exact step; when the head's
@@ -238,18 +248,24 @@ def run_dense(S_init, tokens: Iterable[Dict[str, np.ndarray]], win_len, win_off,
     of fp32 rounding size this measures how well the plain definition's
     outputs are determined by its inputs (rounding decisions near ties).
 
+    warm_start (a variant, not on the pages): each close starts compensator l's
+    power method from the same head's compensator value u_l of the window
+    that is closing (the fixed start vector where that is zero); the initial
+    encode starts cold.
+
     S_init [N][d_k][d_v]; tokens yields per-step dicts with q, k [N][d_k],
     v [N][d_v], g [N] or [N][d_k], beta [N]; win_len, win_off [N].
     Returns dict(o [T][N][d_v], u [T][N][d_v], S final, enc0, closes).
     """
     rng = np.random.default_rng(noise_seed)
 
-    def enc(X):
+    def enc(X, start=None):
         if rounding_noise:
             X = X * (1.0 + rounding_noise * rng.standard_normal(X.shape))
-        return encode(X, r, T, bits, smoothing, quantize)
+        return encode(X, r, T, bits, smoothing, quantize, start)
 
     enc0 = enc(_f64(S_init))
+    comp_u = enc0.comp_u.copy()
     S = decode(enc0)
     pos = np.array(win_off, np.int64).copy()
     W = np.array(win_len, np.int64)
@@ -261,10 +277,11 @@ def run_dense(S_init, tokens: Iterable[Dict[str, np.ndarray]], win_len, win_off,
         pos += 1
         idx = np.nonzero(pos == W)[0]
         if idx.size:
-            e = enc(S[idx])
+            e = enc(S[idx], comp_u[idx] if warm_start else None)
             if record:
                 closes.append(CloseEvent(t, idx, S[idx].copy(), e))
             S[idx] = decode(e)
+            comp_u[idx] = e.comp_u
             pos[idx] = 0
     return dict(o=np.array(outs), u=np.array(us), S=S, enc0=enc0, closes=closes)
 
@@ -282,10 +299,12 @@ class BufferedOracle:
     for KDA)."""
 
     def __init__(self, S_init, win_len, win_off, *, w_max: int, r: int, T: int = 4,
-                 bits: int = 8, smoothing: bool = True, quantize: bool = True, kda: bool = False):
+                 bits: int = 8, smoothing: bool = True, quantize: bool = True, kda: bool = False,
+                 warm_start: bool = False):
         S_init = _f64(S_init)
         self.N, self.dk, self.dv = S_init.shape
         self.r, self.T, self.bits, self.smoothing, self.quantize, self.kda = r, T, bits, smoothing, quantize, kda
+        self.warm_start = warm_start
         self.w_max = w_max
         self.W = np.array(win_len, np.int64)
         self.pos = np.array(win_off, np.int64).copy()
@@ -371,7 +390,8 @@ class BufferedOracle:
         if idx.size == 0:
             return idx
         S = self.fold(idx)
-        e = encode(S, self.r, self.T, self.bits, self.smoothing, self.quantize)
+        start = self.base.comp_u[idx] if self.warm_start else None
+        e = encode(S, self.r, self.T, self.bits, self.smoothing, self.quantize, start)
         self.closes.append(CloseEvent(t, idx, S, e))
         for name in ("comp_k", "comp_u", "s", "c", "codes", "resid"):
             getattr(self.base, name)[idx] = getattr(e, name)
@@ -381,9 +401,9 @@ class BufferedOracle:
 
 
 def run_buffered(S_init, tokens, win_len, win_off, *, w_max: int, r: int, T: int = 4, bits: int = 8,
-                 smoothing: bool = True, quantize: bool = True, kda: bool = False):
+                 smoothing: bool = True, quantize: bool = True, kda: bool = False, warm_start: bool = False):
     st = BufferedOracle(S_init, win_len, win_off, w_max=w_max, r=r, T=T, bits=bits,
-                        smoothing=smoothing, quantize=quantize, kda=kda)
+                        smoothing=smoothing, quantize=quantize, kda=kda, warm_start=warm_start)
     outs, us = [], []
     for t, tok in enumerate(tokens):
         o, u = st.step(tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"])

@@ -179,7 +179,7 @@ def run_oracle(wl: wk.Workload, steps: int, seqs: Sequence[int], bits=None, reco
     win_off = np.repeat(wk.window_offsets(wl)[list(seqs)], H)
     res = lq.run_dense(S0, toks, win_len, win_off, r=wl.n_comp, T=wl.power_iters,
                        bits=wl.bits if bits is None else bits, smoothing=wl.smoothing, record=record,
-                       rounding_noise=rounding_noise, noise_seed=noise_seed)
+                       rounding_noise=rounding_noise, noise_seed=noise_seed, warm_start=wl.warm_start)
     res["o"] = res["o"].reshape(steps, len(seqs), H, wl.d_v)
     return res
 

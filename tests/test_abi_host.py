@@ -31,7 +31,7 @@ def test_every_declared_function_is_exported():
 
 def dims(**kw):
     base = dict(batch=2, heads=3, d_k=128, d_v=128, w_max=16, n_comp=4, bits=8, decay_per_channel=0,
-                act_dtype=0, smoothing=1, power_iters=4)
+                act_dtype=0, smoothing=1, power_iters=4, warm_start=0)
     base.update(kw)
     return L.CDims(**base)
 
@@ -62,6 +62,7 @@ def step(d, st, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE):
     (dict(act_dtype=2), L.LQ_ERR_CONFIG),
     (dict(decay_per_channel=2), L.LQ_ERR_CONFIG),
     (dict(smoothing=3), L.LQ_ERR_CONFIG),
+    (dict(warm_start=2), L.LQ_ERR_CONFIG),
 ])
 def test_dims_validation(kw, code):
     d = dims(**kw)

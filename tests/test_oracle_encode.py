@@ -193,3 +193,54 @@ def test_outlier_ratio_drops_through_compensators_and_smoothing():
     r_R = np.median(lq.outlier_ratio(e.resid))
     r_Rt = np.median(lq.outlier_ratio(e.resid / e.s[:, :, None]))
     assert r_S > 10 * r_R and r_R > r_Rt
+
+
+def test_warm_start_from_exact_singular_vectors_gives_the_svd_in_one_step():
+    """Started from the exact right singular vectors, one power step lands on
+    the singular pairs, compensator after compensator (deflation removes each
+    pair exactly): compare with numpy.linalg.svd."""
+    rng = np.random.default_rng(21)
+    N, d, r = 3, 12, 3
+    U, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    V, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    sig = np.array([9.0, 5.0, 3.0] + [0.5] * (d - 3))
+    S = np.stack([U @ np.diag(sig) @ V.T for _ in range(N)])
+    _, sv, Vt = np.linalg.svd(S[0])
+    start = np.repeat(Vt[None, :r, :], N, axis=0) * 3.0          # any positive scale
+    ck, cu, R = lq.extract_compensators(S, r, T=1, start=start)
+    for l in range(r):
+        np.testing.assert_allclose(np.abs(ck[:, l] @ U[:, l]), 1.0, atol=1e-12)
+        np.testing.assert_allclose(np.linalg.norm(cu[:, l], axis=1), sv[l], rtol=1e-12)
+    # a cold start with one step is far from the singular vectors
+    ck0, _, _ = lq.extract_compensators(S, r, T=1)
+    assert np.abs(ck0[0, 0] @ U[:, 0]) < 0.999
+
+
+def test_warm_start_falls_back_where_the_start_is_zero():
+    rng = np.random.default_rng(22)
+    S = rng.standard_normal((4, 8, 8))
+    start = rng.standard_normal((4, 2, 8))
+    start[1] = 0.0
+    start[2, 1] = np.nan
+    a = lq.extract_compensators(S, 2, 3, start)
+    cold = lq.extract_compensators(S, 2, 3)
+    np.testing.assert_array_equal(a[0][1], cold[0][1])           # head 1: fixed start vectors
+    warm_only = lq.extract_compensators(S[2:3], 2, 3, start[2:3])
+    np.testing.assert_array_equal(a[0][2], warm_only[0][0])
+    assert not np.array_equal(a[0][0], cold[0][0])               # head 0 did start warm
+
+
+def test_warm_windowed_dense_equals_buffered():
+    """The plain definition and the buffered form agree with warm starts too."""
+    from tests.oracle_inputs import random_tokens
+    rng = np.random.default_rng(23)
+    N, d, L = 3, 8, 20
+    S0 = rng.standard_normal((N, d, d))
+    toks = random_tokens(rng, L, N, d, d, kda=False)
+    W = np.array([4, 5, 6])
+    off = np.zeros(N, np.int64)
+    a = lq.run_dense(S0, toks, W, off, r=2, T=1, warm_start=True)
+    b = lq.run_buffered(S0, toks, W, off, w_max=6, r=2, T=1, warm_start=True)
+    np.testing.assert_allclose(a["o"], b["o"], rtol=1e-9, atol=1e-9)
+    c = lq.run_dense(S0, toks, W, off, r=2, T=1)
+    assert not np.allclose(a["o"], c["o"], rtol=1e-12, atol=1e-12)  # the variant does change the closes
