@@ -51,6 +51,7 @@ def parse():
     p.add_argument("--cpu-sample", default="32x256", help="oracle sample: sequences x steps")
     p.add_argument("--prefill-tokens", type=int, default=256,
                    help="prompt length of the prefill-handoff leg (0: skip)")
+    p.add_argument("--no-snapshot", action="store_true", help="skip timing snapshot/restore")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy three times (the reference dispatch "
                         "for scaling hardware byte counters), then exit")
@@ -326,6 +327,45 @@ def run_prefill(wl, bits, n_tokens):
                          "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4)}}
 
 
+def run_snapshot(wl, bits):
+    """Prefix-cache snapshot and restore of every sequence at a window boundary.
+    HBM-bound copies: one record per head read and written once each way."""
+    import torch
+
+    from linear_attention_recurrent_kda_amd import leapquant as lqk
+    from linear_attention_recurrent_kda_amd import runner
+    from linear_attention_recurrent_kda_amd import workloads as wk
+
+    dims = runner.dims_for(wl, bits)
+    N, d = wl.batch * wl.heads, wl.d_k
+    st = lqk.State(dims)
+    lqk.encode(dims, runner.states_to_device(wk.initial_states(wl, range(wl.batch))), st)
+    rec = lqk.snapshot_bytes(dims)
+    snap = torch.empty((wl.batch, wl.heads, rec), dtype=torch.uint8, device="cuda")
+    best = {}
+    for name, fn in (("snapshot", lqk.snapshot), ("restore", lqk.restore)):
+        fn(dims, st, snap)  # warm-up
+        torch.cuda.synchronize()
+        times = []
+        reps = 20  # back to back, so that host call overhead does not idle the GPU
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn(dims, st, snap)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / reps)
+        best[name] = min(times)
+    assert int(st.err.item()) == 0
+    moved = 2.0 * rec * N  # each record read once and written once
+    gbs = moved / (best["snapshot"] * 1e-6) / 1e9
+    return {"record_bytes_per_head": rec, "fp32_state_bytes_per_head": 4 * d * d,
+            "heads": N, "snapshot_us": round(best["snapshot"], 1), "restore_us": round(best["restore"], 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(wl, bits, sample):
     """The fp64 oracle (plain definition) on a bounded sample of the same workload."""
     import numpy as np
@@ -422,6 +462,8 @@ def main():
         line["speedup_vs_fp32"] = round(value / fval, 3)
     if args.prefill_tokens > 0:
         line["prefill_handoff"] = run_prefill(wl, bits, args.prefill_tokens)
+    if not args.no_snapshot:
+        line["snapshot"] = run_snapshot(wl, bits)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, bits, args.cpu_sample)
     print(json.dumps(line), flush=True)
