@@ -97,3 +97,34 @@ def test_handoff_encode_and_decode_on(name, kw, bits):
         worst = max(worst, gh.rel_l2(out.cpu().numpy(), o_ref))
     print("decode after handoff max rel L2", worst)
     assert worst <= 1e-5
+
+
+@pytest.mark.parametrize("L", [0, 1, 5])
+def test_prefill_short_and_empty_prompts(L):
+    """An empty prompt leaves the state as it is and the handoff is the plain
+    encode; one token and a few tokens match the exact recurrence."""
+    wl = W["tiny_gdn"].replace(batch=2, heads=2, kda=True)
+    dims = runner.dims_for(wl)
+    N, d = wl.batch * wl.heads, wl.d_k
+    S0 = wk.initial_states(wl, range(wl.batch))
+    S = runner.states_to_device(S0)
+    S_before = S.clone()
+    raw, toks = _prompt(wl, max(L, 1))
+    dev = runner.upload_tokens(raw, wl.act_bf16)
+    o = torch.full((max(L, 1), N, d), -7.0, dtype=torch.float32, device="cuda")
+    st = lqk.State(dims)
+    lqk.prefill(dims, S, dev["q"][:L], dev["k"][:L], dev["v"][:L], dev["g"][:L], dev["beta"][:L], o[:L], st)
+    st2 = lqk.State(dims)
+    lqk.encode(dims, S, st2)
+    torch.cuda.synchronize()
+    a, b = gh.download_state(st, dims), gh.download_state(st2, dims)
+    for f in lqk.STATE_FIELDS:
+        assert np.array_equal(a[f], b[f]), f
+    if L == 0:
+        assert torch.equal(S, S_before)
+        assert torch.all(o == -7.0)  # nothing written
+        return
+    S_ref, outs = lq.prefill(S0.reshape(N, d, d).astype(np.float64), toks[:L])
+    o_gpu = o.cpu().numpy()
+    assert max(gh.rel_l2(o_gpu[t], outs[t]) for t in range(L)) <= 1e-5
+    assert gh.rel_l2(gh.T(S.cpu().numpy()), S_ref) <= 1e-5

@@ -40,6 +40,14 @@ def test_snapshot_restore_round_trip(name, bits):
     for f in ("codes", "row_scale", "col_scale", "comp_k", "comp_u"):
         assert np.array_equal(a[f][heads], b[f][heads]), f
     assert np.all(b["comp_g"][heads] == 0) and np.all(b["buf_len"][heads] == 0)
+    # the record layout as the header states it: codes, s, c, compensator keys, values
+    host = snap.cpu().numpy()
+    for slot, seq in enumerate(seqs):
+        for h in range(H):
+            n = seq * H + h
+            want = b"".join(np.ascontiguousarray(x).tobytes() for x in (
+                a["codes"][n], a["row_scale"][n], a["col_scale"][n], a["comp_k"][n], a["comp_u"][n]))
+            assert host[slot, h].tobytes() == want, (seq, h)
     assert int(dec.state.err.item()) == 0 and int(fresh.err.item()) == 0
     # decoding on: the restored heads give the original heads' outputs exactly
     o1 = torch.empty((N, d), device="cuda")

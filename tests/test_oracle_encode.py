@@ -122,7 +122,7 @@ def _nearest_code(x, Q):
     return best
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 6, 4])
 @pytest.mark.parametrize("smoothing", [True, False])
 def test_quantiser_brute_force_4x4(bits, smoothing):
     # symmetric b-bit codes: the largest magnitude a signed b-bit integer
@@ -135,7 +135,7 @@ def test_quantiser_brute_force_4x4(bits, smoothing):
     R[2] = np.array([[0.5, -1.0, 0.25, 2.0]] * 4) * 3.0
     # exact ties on the code grid: every row max is 1 (so s = 1) and column 0
     # has max Q/2^p, so c_0 = 2^-p and the other entries land on x.5 exactly
-    p2 = 128.0 if bits == 8 else 8.0
+    p2 = 2.0 ** (bits - 1)
     R[3] = 0.0
     R[3, :, 3] = 1.0
     R[3, :, 0] = np.array([Q, 2.5, -3.5, 0.5]) / p2
