@@ -327,6 +327,34 @@ def run_prefill(wl, bits, n_tokens):
                          "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4)}}
 
 
+def outlier_report(wl, bits, n_seq=8):
+    """Outlier-to-median ratio max|X| / median|X| per head, median over the heads of
+    the first n_seq sequences: the initial state S, the GPU encode's residual R (after
+    the compensators) and R / s (after key-row smoothing). Reported in kind with the
+    pages' example, not a target."""
+    import numpy as np
+    import torch
+
+    from linear_attention_recurrent_kda_amd import leapquant as lqk
+    from linear_attention_recurrent_kda_amd import runner
+    from linear_attention_recurrent_kda_amd import workloads as wk
+
+    small = wl.replace(batch=n_seq)
+    dims = runner.dims_for(small, bits)
+    N, d = small.batch * small.heads, small.d_k
+    S = runner.states_to_device(wk.initial_states(small, range(n_seq)))
+    st = lqk.State(dims)
+    R = torch.empty((N, d, d), dtype=torch.float32, device="cuda")
+    lqk.encode(dims, S, st, R)
+    torch.cuda.synchronize()
+    # both stored transposed ([d_v][d_k]); the ratio does not depend on orientation
+    s_rows = st.row_scale.cpu().numpy()  # per key channel
+    Rh = R.cpu().numpy()
+    ratio = lambda X: float(np.median([np.max(np.abs(x)) / np.median(np.abs(x)) for x in X]))
+    return {"heads": N, "state": round(ratio(S.cpu().numpy()), 1), "after_compensators": round(ratio(Rh), 1),
+            "after_smoothing": round(ratio(Rh / s_rows[:, None, :]), 1)}
+
+
 def run_snapshot(wl, bits):
     """Prefix-cache snapshot and restore of every sequence at a window boundary.
     HBM-bound copies: one record per head read and written once each way."""
@@ -464,6 +492,7 @@ def main():
         line["prefill_handoff"] = run_prefill(wl, bits, args.prefill_tokens)
     if not args.no_snapshot:
         line["snapshot"] = run_snapshot(wl, bits)
+    line["outlier_ratio"] = outlier_report(wl, bits)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, bits, args.cpu_sample)
     print(json.dumps(line), flush=True)

@@ -6,24 +6,34 @@
 // encoded once at the handoff (the encode entry point, launched after this
 // kernel by the C ABI).
 //
-// One workgroup of 256 threads per head keeps the d_k x d_v state in
-// registers for the whole chunk (16 x 16 thread grid, thread (ti, tj) holds
-// key rows [ti*B, ti*B+B) and value columns [tj*B, tj*B+B), B = D/16), so the
-// state is read and written once per chunk, not once per token. Per token,
-// decay first (Gated DeltaNet scalar gate; Kimi Delta Attention per-channel
-// gate):
-//   S' = alpha (.)_rows S,  u = beta (v - S'^T k),  o = S'^T q + (k . q) u,
-//   S = S' + k u^T
-// (o = S^T q with S = S' + k u^T). The two column sums S'^T k and S'^T q and
-// the partial k . q travel through LDS together: one barrier per token,
-// double-buffered. The next token's inputs are loaded while the current one
-// is computed.
+// Per token, decay first (Gated DeltaNet scalar gate; Kimi Delta Attention
+// per-channel gate):
+//   S' = alpha (.)_rows S,  u = beta (v - S'^T k),  S = S' + k u^T,  o = S^T q
+// (o = S'^T q + (k . q) u). Two kernels, one per activation type, both
+// keeping the state in registers for the whole chunk (read and written once):
+//
+// - fp32 activations, prefill_columns_kernel: every value column j evolves on
+//   its own (u_j needs column j of S' and k; o_j column j of S and q), so one
+//   thread owns one column, all d_k key rows, and a token costs it two passes
+//   over its column with no exchange between threads: no LDS, no barrier, no
+//   cross-lane reduction. k, q, beta and the GDN gate are the same for every
+//   thread of a head and arrive through scalar loads as instruction operands;
+//   the KDA per-channel gates are exponentiated two channels per lane and
+//   broadcast with readlane. One wave covers 64 columns of a head.
+// - bf16 activations, prefill_blocks_kernel: through scalar loads a bf16 pair
+//   costs a scalar-unit split per value, which measured slower than sharing
+//   the sums: 256 threads per head on a 16 x 16 grid, each with a B x B block
+//   (B = D/16); the column partials of S'^T k and S'^T q and the partial k . q
+//   go through LDS with one barrier per token, double-buffered, and the next
+//   token's inputs load while the current one computes.
 #include "lq_common.h"
 #include "lq_launch.h"
 
 namespace lq {
 
 namespace {
+
+// ---- bf16 activations: 256 threads per head, B x B register blocks
 
 template <int N>
 __device__ __forceinline__ void ld(const float* p, float (&x)[N]) {
@@ -82,7 +92,7 @@ __device__ __forceinline__ void load_tok(const PrefillArgs& a, int t, int bh, in
 }
 
 template <int D, bool KDA, bool BF16>
-__global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(256) prefill_blocks_kernel(PrefillArgs a) {
   constexpr int B = D / 16;
   __shared__ float sh_kq[2][4];       // per-wave partial k . q
   __shared__ float sh_p[2][4][2][D];  // per-wave column partials of S'^T k and S'^T q
@@ -160,9 +170,141 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   }
 }
 
+// ---- fp32 activations: one thread per value column
+
+// Read-only inputs seen through the constant address space: a load at a
+// uniform address then goes through the scalar unit into SGPRs, where every
+// lane reads it as an instruction operand.
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T*;
+
+template <typename T>
+__device__ __forceinline__ cptr<T> as_const(const void* p) {
+  return (cptr<T>)(p);
+}
+
+// Uniform activation value (fp32 or bf16) at element row + i, row even. The
+// scalar unit loads whole dwords: a bf16 pair is read as one word and split.
+template <bool BF16>
+__device__ __forceinline__ float act_at(const void* p, size_t row, int i) {
+  if constexpr (BF16) {
+    const uint32_t w = as_const<uint32_t>(p)[(row + i) / 2];
+    return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+  } else {
+    return as_const<float>(p)[row + i];
+  }
+}
+
+// Per-lane activation value (fp32 or bf16) at element idx.
+template <bool BF16>
+__device__ __forceinline__ float act_lane(const void* p, size_t idx) {
+  if constexpr (BF16) return as_f(uint32_t(static_cast<const uint16_t*>(p)[idx]) << 16);
+  else return static_cast<const float*>(p)[idx];
+}
+
+template <int D, bool KDA, bool BF16>
+__global__ void __launch_bounds__(64) prefill_columns_kernel(PrefillArgs a) {
+  constexpr int WPH = D > 64 ? D / 64 : 1;  // waves per head
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x / WPH;
+  const int j = (blockIdx.x % WPH) * 64 + lane;  // this thread's value column
+  const bool col = D >= 64 || j < D;            // D = 32: the upper half-wave idles
+  const size_t hD = size_t(bh) * D;
+
+  float M[D];  // M[i] = S[i][j]
+  if (col) {
+#pragma unroll
+    for (int w = 0; w < D / 4; ++w) {
+      const float4 t = reinterpret_cast<const float4*>(a.S + (hD + j) * D)[w];
+      M[4 * w] = t.x, M[4 * w + 1] = t.y, M[4 * w + 2] = t.z, M[4 * w + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) M[i] = 0.f;
+  }
+
+  // Inputs of token tt + 1 are loaded while token tt computes: the per-lane v
+  // and gate values into registers, the uniform beta (and GDN gate) into
+  // scalar registers, and one touch per line of its k and q rows, which warms
+  // the cache for that token's scalar loads.
+  const int n_tok = a.n_tokens;
+  auto th_of = [&](int tt) { return size_t(tt) * a.n_heads + bh; };  // [token][head]
+  const int pfi = min(2 * lane, D - 2);  // element of a k / q row this lane touches
+  const int jc = min(j, D - 1);          // in-bounds column for the idle lanes' loads
+  const int gc = min(lane, D - 1);       // KDA: this lane's first gate channel
+  // loads without branches (clamped indices), so that no join forces an early wait
+  auto load_tok = [&](int tt, float& beta, float& g, float& vj, float& e0, float& e1) {
+    const size_t th = th_of(tt), row = th * D;
+    beta = as_const<float>(a.beta)[th];
+    vj = act_lane<BF16>(a.v, row + jc);
+    if constexpr (KDA) {
+      e0 = a.g[row + gc];
+      e1 = D > 64 ? a.g[row + 64 + lane] : 0.f;
+    } else {
+      g = as_const<float>(a.g)[th];
+    }
+  };
+  float beta_c = 0.f, g_c = 0.f, vj_c = 0.f, e0_c = 0.f, e1_c = 0.f;
+  if (n_tok > 0) load_tok(0, beta_c, g_c, vj_c, e0_c, e1_c);
+  for (int tt = 0; tt < n_tok; ++tt) {
+    const size_t th = th_of(tt);
+    const size_t row = th * D;
+    const int tn = min(tt + 1, n_tok - 1);  // the last token reloads itself
+    float beta_n = 0.f, g_n = 0.f, vj_n = 0.f, e0_n = 0.f, e1_n = 0.f;
+    load_tok(tn, beta_n, g_n, vj_n, e0_n, e1_n);
+    const size_t rown = th_of(tn) * D;
+    const float touch = act_lane<BF16>(a.k, rown + pfi) + act_lane<BF16>(a.q, rown + pfi);
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the token's arithmetic
+    // pass 1: decay, and u_j = beta (v_j - sum_i S'[i][j] k_i)
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KDA) {
+      // alpha_i = exp(g_i): lane l holds channels l and l + 64
+      const float a0 = expf(e0_c), a1 = expf(e1_c);
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        const float al = as_f(__builtin_amdgcn_readlane(as_u(i < 64 ? a0 : a1), i & 63));
+        M[i] *= al;
+        s[i & 3] = fmaf(M[i], act_at<BF16>(a.k, row, i), s[i & 3]);
+      }
+    } else {
+      const float al = expf(g_c);
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        M[i] *= al;
+        s[i & 3] = fmaf(M[i], act_at<BF16>(a.k, row, i), s[i & 3]);
+      }
+    }
+    const float u = col ? beta_c * (vj_c - ((s[0] + s[1]) + (s[2] + s[3]))) : 0.f;
+    // pass 2: S = S' + k u^T, and o_j = sum_i S[i][j] q_i
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      M[i] = fmaf(act_at<BF16>(a.k, row, i), u, M[i]);
+      p[i & 3] = fmaf(M[i], act_at<BF16>(a.q, row, i), p[i & 3]);
+    }
+    // the next token's loads are complete here, before the output store: a
+    // wait at the loop's end then never covers the store
+    asm volatile("" ::"v"(touch), "v"(vj_n), "v"(e0_n), "v"(e1_n));
+    if (col) a.o[row + j] = (p[0] + p[1]) + (p[2] + p[3]);
+    beta_c = beta_n, g_c = g_n, vj_c = vj_n, e0_c = e0_n, e1_c = e1_n;
+  }
+
+  if (col) {
+#pragma unroll
+    for (int w = 0; w < D / 4; ++w)
+      reinterpret_cast<float4*>(a.S + (hD + j) * D)[w] = make_float4(M[4 * w], M[4 * w + 1], M[4 * w + 2], M[4 * w + 3]);
+  }
+}
+
 template <int D, bool KDA, bool BF16>
 hipError_t launch(const lq_dims& d, const PrefillArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, KDA, BF16>), dim3(d.batch * d.heads), dim3(256), 0, stream, a);
+  if constexpr (BF16) {
+    hipLaunchKernelGGL((prefill_blocks_kernel<D, KDA, BF16>), dim3(d.batch * d.heads), dim3(256), 0, stream, a);
+  } else {
+    constexpr int WPH = D > 64 ? D / 64 : 1;
+    hipLaunchKernelGGL((prefill_columns_kernel<D, KDA, BF16>), dim3(d.batch * d.heads * WPH), dim3(64), 0,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 
