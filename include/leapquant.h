@@ -56,7 +56,7 @@ extern "C" {
 #define LQ_ERR_BITS (-3)   /* bits not 4, 6 or 8 */
 #define LQ_ERR_CONFIG (-4) /* w_max, n_comp, power_iters, flags or close list out of range */
 #define LQ_ERR_LAUNCH (-5) /* the HIP launch failed */
-#define LQ_ERR_ALIGN (-6)  /* a buffer is not 16-byte aligned */
+#define LQ_ERR_ALIGN (-6)  /* a buffer is not aligned as the conventions above require */
 
 /* activation dtypes for q, k, v */
 #define LQ_ACT_F32 0
