@@ -80,11 +80,6 @@ __device__ __forceinline__ void buf_loadN(__amdgpu_buffer_rsrc_t r, uint32_t off
   }
 }
 
-__device__ __forceinline__ void store_nt4(float* p, float4 v) {
-  typedef float v4f __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(p));
-}
-
 __device__ __forceinline__ float4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const v4u t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, ENTRY_POLICY);
   return make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]), __uint_as_float(t[3]));
@@ -208,7 +203,7 @@ struct HeadStep {
     CT cw[RBW][KB];  // residual codes, MFMA operand order
     uint32_t lo6[BITS == 6 ? KB : 1][BITS == 6 ? RBW : 1];  // 6 bits: lo fields of the same blocks
     uint32_t kx_raw, qx_raw;  // q_t, k_t as loaded (bf16 or fp32 bits); converted when used
-    uint4 v_raw;              // v_t quad as loaded (bf16: .x, .y)
+    uint32_t vj_raw;          // v_t of this thread's value column as loaded (bf16 or fp32 bits)
     float si, cc, gi, beta, gs, Gp;
     float kr[KPF][CPL], gr[KDA ? KPF : 1][CPL], Gm[KPF];
     float4 uv[PFE];
@@ -229,7 +224,6 @@ struct HeadStep {
   // flight: the first half of the codes, then the per-channel inputs.
   __device__ static __forceinline__ void load_early(const StepArgs& a, int bh, In& h) {
     const int t = threadIdx.x;
-    const int q4 = t % NQ;
     const bool chan = NT == D || t < D;
     const int tc = chan ? t : 0;
     const Ptr P = ptr(a, bh);
@@ -239,12 +233,11 @@ struct HeadStep {
     if constexpr (BF16) {
       h.kx_raw = static_cast<const uint16_t*>(a.k)[P.hD + tc];
       h.qx_raw = static_cast<const uint16_t*>(a.q)[P.hD + tc];
-      const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + P.hD + 4 * q4);
-      h.v_raw = make_uint4(w.x, w.y, 0u, 0u);
+      h.vj_raw = static_cast<const uint16_t*>(a.v)[P.hD + tc];
     } else {
       h.kx_raw = static_cast<const uint32_t*>(a.k)[P.hD + tc];
       h.qx_raw = static_cast<const uint32_t*>(a.q)[P.hD + tc];
-      h.v_raw = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.v) + P.hD + 4 * q4);
+      h.vj_raw = static_cast<const uint32_t*>(a.v)[P.hD + tc];
     }
     h.si = a.s[P.hD + tc];
     h.cc = a.c[P.hD + tc];
@@ -461,6 +454,21 @@ struct HeadStep {
     }
     __syncthreads();
 
+    // (5a) the first half of the residual readout (see (5)): its codes were
+    // loaded first, so the matrix cores take it while (4) runs on the VALU
+    v4i aop[KB], acc[RBW];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      aop[kb] = *reinterpret_cast<const v4i*>(&sm.B[kb][lane & 15][16 * (lane >> 4)]);
+#pragma unroll
+    for (int rb = 0; rb < RBW / 2; ++rb) {
+      acc[rb] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        if constexpr (BITS == 6) acc[rb] = CL::mfma(aop[kb], h.cw[rb][kb], h.lo6[kb][rb], acc[rb]);
+        else acc[rb] = CL::mfma(aop[kb], h.cw[rb][kb], acc[rb]);
+    }
+
     // (4) value-side sums: sum_e u_e[j] kappa^x_e for this thread's four value
     // columns over the entries of its phase (e = ph, ph + EP, ...)
     {
@@ -491,13 +499,8 @@ struct HeadStep {
     // four limb sums of x = l/16 for column j = 16 rb + l%16 and combines them:
     // y^x_j / c_j = zscale_x * sum_l 256^l D[4x+l][j].
     {
-      v4i aop[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        aop[kb] = *reinterpret_cast<const v4i*>(&sm.B[kb][lane & 15][16 * (lane >> 4)]);
-      v4i acc[RBW];
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
+      for (int rb = RBW / 2; rb < RBW; ++rb) {
         acc[rb] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -519,35 +522,24 @@ struct HeadStep {
     __syncthreads();
 
     // (6) delta, output, append (k_t, u_t, G_t) as entry E: one thread per
-    // value-column quad
-    if (t < NQ) {
+    // value column (a short chain per thread: this is the step's tail)
+    if (chan) {
+      const int j = t;
       float kqs = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) kqs += sm.red[0][w];
-      const float4 c4 = *reinterpret_cast<const float4*>(&sm.c[4 * q4]);
-      float4 yk = *reinterpret_cast<const float4*>(&sm.y[0][4 * q4]);
-      float4 yq = *reinterpret_cast<const float4*>(&sm.y[1][4 * q4]);
-      yk.x *= c4.x, yk.y *= c4.y, yk.z *= c4.z, yk.w *= c4.w;
-      yq.x *= c4.x, yq.y *= c4.y, yq.z *= c4.z, yq.w *= c4.w;
+      const float cj = sm.c[j];
+      float yk = sm.y[0][j] * cj, yq = sm.y[1][j] * cj;
 #pragma unroll
-      for (int p = 0; p < EP; ++p) {
-        const float4 a4 = *reinterpret_cast<const float4*>(&sm.vs[p][0][4 * q4]);
-        const float4 b4 = *reinterpret_cast<const float4*>(&sm.vs[p][1][4 * q4]);
-        yk.x += a4.x, yk.y += a4.y, yk.z += a4.z, yk.w += a4.w;
-        yq.x += b4.x, yq.y += b4.y, yq.z += b4.z, yq.w += b4.w;
-      }
-      const float4 v4 = BF16 ? make_float4(bf16_lo(h.v_raw.x), bf16_hi(h.v_raw.x), bf16_lo(h.v_raw.y), bf16_hi(h.v_raw.y))
-                             : make_float4(as_f(h.v_raw.x), as_f(h.v_raw.y), as_f(h.v_raw.z), as_f(h.v_raw.w));
-      const float beta = h.beta;
-      float4 u, o;
-      u.x = beta * (v4.x - yk.x), u.y = beta * (v4.y - yk.y), u.z = beta * (v4.z - yk.z), u.w = beta * (v4.w - yk.w);
-      o.x = fmaf(kqs, u.x, yq.x), o.y = fmaf(kqs, u.y, yq.y), o.z = fmaf(kqs, u.z, yq.z), o.w = fmaf(kqs, u.w, yq.w);
-      *reinterpret_cast<float4*>(a.o + P.hD + 4 * q4) = o;
+      for (int p = 0; p < EP; ++p) yk += sm.vs[p][0][j], yq += sm.vs[p][1][j];
+      const float vj = BF16 ? as_f(h.vj_raw << 16) : as_f(h.vj_raw);
+      const float u = h.beta * (vj - yk);
+      a.o[P.hD + j] = fmaf(kqs, u, yq);
       // the appended entry is read again one step later, after the rest of
       // the step's state has streamed through: non-temporal stores
-      store_nt4(P.eu + E * D + 4 * q4, u);
-      store_nt4(P.ek + E * D + 4 * q4, *reinterpret_cast<const float4*>(&sm.x[0][4 * q4]));
-      if constexpr (KDA) store_nt4(P.eg + E * D + 4 * q4, *reinterpret_cast<const float4*>(&sm.G[4 * q4]));
+      __builtin_nontemporal_store(u, P.eu + E * D + j);
+      __builtin_nontemporal_store(kx, P.ek + E * D + j);
+      if constexpr (KDA) __builtin_nontemporal_store(Gi, P.eg + E * D + j);
       if (t == 0) {
         if constexpr (!KDA) P.eg[E] = G;
         a.blen[bh] = n + 1;
