@@ -20,6 +20,9 @@ CASES = [
     ("qwen_gdn", dict(batch=4)),                 # bf16 activations, d = 128
     ("kda_int4", dict(batch=2)),                 # per-channel decay
     ("tiny_gdn", dict(batch=2, heads=2, d_k=64, d_v=64, kda=True)),
+    ("tiny_gdn", dict(batch=2, heads=2, d_k=64, d_v=64, act_bf16=True)),   # bf16 block kernel, d = 64
+    ("tiny_gdn", dict(batch=2, heads=3, act_bf16=True, kda=True)),          # bf16 block kernel, d = 32, KDA
+    ("kda_int4", dict(batch=2, act_bf16=True)),                             # bf16 block kernel, KDA, d = 128
 ]
 
 
