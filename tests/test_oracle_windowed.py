@@ -150,3 +150,26 @@ def test_rounding_noise_option_and_free_running_sensitivity():
         b = lq.run_dense(S0, toks, np.full(4, W), np.zeros(4), rounding_noise=2.0 ** -24, noise_seed=1, **args)
         env = max(rel_l2(b["o"][t], a["o"][t]) for t in range(12))
         assert (env > 1e-3) == expect_big, (W, env)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_fold_window_is_the_state_after_the_buffered_tokens(kda):
+    """fold_window (the dense state a window close starts from) rebuilds, for a
+    ragged number n of buffered tokens per head, the exact recurrence's state
+    after those n tokens (quantisation off, no compensators)."""
+    rng = np.random.default_rng(31 + kda)
+    N, dk, dv, steps = 4, 8, 6, 10
+    S0 = planted_state(rng, N, dk, dv)
+    toks = random_tokens(rng, steps, N, dk, dv, kda=kda, decay_scale=0.3)
+    bo = lq.BufferedOracle(S0, np.full(N, 10 ** 6), np.zeros(N), w_max=steps, r=0, quantize=False, kda=kda)
+    exact = [S0.copy()]
+    S = S0.copy()
+    for t in toks:
+        bo.step(t["q"], t["k"], t["v"], t["g"], t["beta"])
+        S, _, _ = lq.exact_step(S, t["q"], t["k"], t["v"], t["g"], t["beta"])
+        exact.append(S.copy())
+    n = np.array([0, 3, 7, 10])
+    F = lq.fold_window(lq.decode(bo.base), bo.buf_k, bo.buf_u, bo.buf_G, n, kda)
+    want = np.stack([exact[n[h]][h] for h in range(N)])
+    assert _rel(F, want) <= 1e-12
+    assert np.array_equal(F[0], S0[0])  # nothing buffered: the window-start state itself
