@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--prefill-tokens", type=int, default=256,
                    help="prompt length of the prefill-handoff leg (0: skip)")
     p.add_argument("--no-snapshot", action="store_true", help="skip timing snapshot/restore")
+    p.add_argument("--no-stream-reference", action="store_true",
+                   help="skip timing plain library streaming of the same bytes")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy three times (the reference dispatch "
                         "for scaling hardware byte counters), then exit")
@@ -71,6 +73,31 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read_per_dispatch": n, "bytes_written_per_dispatch": n,
                                            "dispatches": 3}}), flush=True)
+
+
+def stream_reference(nbytes, layers=8, reps=20):
+    """A plain device copy moving the decode launch's byte count (half read, half
+    written) through the runtime's copy path, one buffer pair per layer so that
+    the last-level cache does not hold them, launched back to back: a reference
+    for the decode kernel's HBM fraction on this device, not part of the step."""
+    import torch
+    n = (nbytes // 2) // 4  # fp32 elements copied per launch
+    src = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(layers)]
+    dst = [torch.empty_like(x) for x in src]
+    for d, x in zip(dst, src):
+        d.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for d, x in zip(dst, src):
+            d.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * layers)
+    moved = 2 * n * 4
+    return {"kind": "device copy", "bytes_per_launch": moved, "us_per_launch": round(us, 2),
+            "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
 
 
 def schedule(win_len, win_off, total):
@@ -493,6 +520,8 @@ def main():
     if not args.no_snapshot:
         line["snapshot"] = run_snapshot(wl, bits)
     line["outlier_ratio"] = outlier_report(wl, bits)
+    if not args.no_stream_reference:
+        line["stream_reference"] = stream_reference(r["dec_bytes"] // max(r["n_dec"], 1), args.layers)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, bits, args.cpu_sample)
     print(json.dumps(line), flush=True)
