@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--prefill-tokens", type=int, default=256,
                    help="prompt length of the prefill-handoff leg (0: skip)")
     p.add_argument("--no-snapshot", action="store_true", help="skip timing snapshot/restore")
+    p.add_argument("--no-overlap", action="store_true",
+                   help="skip the schedule with window closes overlapping other layers' decodes")
     p.add_argument("--no-stream-reference", action="store_true",
                    help="skip timing plain library streaming of the same bytes")
     p.add_argument("--copy-calibration", action="store_true",
@@ -275,9 +277,32 @@ def run_gpu(args, wl, bits):
                dec_gbs=dec_bytes / (dec_us * 1e-6) / 1e9 if dec_us else 0.0,
                head_tokens=K * L * BH, state_mb=states[0].nbytes() / 1e6)
 
+    # The same steps with the window closes overlapped: runner.capture_tokens puts
+    # the close of layer l on a side stream as soon as layer l's decode is done;
+    # only layer l's next decode waits for it (bit-identical results).
+    if not args.no_overlap:
+        del states
+        decs = [runner.Decoder(dims, win_len, win_off) for _ in range(L)]
+        for d in decs:
+            d.encode(S_init)
+        g_warm = runner.capture_tokens(decs, toks, outs, 0, Wu, overlap=True)
+        g_timed = runner.capture_tokens(decs, toks, outs, Wu, total, overlap=True)
+        for d in decs:
+            d.encode(S_init)
+        torch.cuda.synchronize()
+        g_warm.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g_timed.replay()
+        torch.cuda.synchronize()
+        res["overlap_wall"] = time.perf_counter() - t0
+        assert sum(int(d.state.err.item()) for d in decs) == 0
+        del decs, g_warm, g_timed
+        states = None
+
     # FP32-state baseline on identical inputs and the same protocol
     if not args.no_fp32:
-        del states
+        states = None
         Sf = [S_init.clone() for _ in range(L)]
 
         def fp_graph(a, b):
@@ -509,6 +534,12 @@ def main():
                          "bytes_per_launch": round(r["close_bytes"] / max(r["n_close"], 1))},
         "hbm_gbs_all_in": round((r["dec_bytes"] + r["close_bytes"]) / r["wall"] / 1e9, 1),
     }
+    if "overlap_wall" in r:
+        line["overlapped_schedule"] = {
+            "value": round(r["head_tokens"] / r["overlap_wall"], 1), "unit": "head-tokens/s",
+            "ms_per_step": round(r["overlap_wall"] * 1e3 / args.steps, 4),
+            "note": "the same steps, each layer's window close on a side stream beside the other "
+                    "layers' decodes (bit-identical results); value above is the in-order schedule"}
     if "fp32_us" in r:
         fval = r["head_tokens"] / r["fp32_wall"]
         line["fp32_baseline"] = {"value": round(fval, 1), "unit": "head-tokens/s",

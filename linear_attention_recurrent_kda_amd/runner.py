@@ -91,3 +91,48 @@ class Decoder:
             self.close_due(self.t)
         self.t += 1
         return o
+
+
+def capture_tokens(decs, inputs, outs, t0: int, t1: int, overlap: bool = True) -> torch.cuda.CUDAGraph:
+    """One HIP graph that advances a stack of layers, each with its own Decoder,
+    through tokens t0..t1-1: per token the decode step of every layer in layer
+    order, and the window closes due after it.
+
+    inputs[l]: device token tensors of layer l with a leading token axis (q, k,
+    v, g, beta); outs[l]: the output buffer of layer l. overlap=False closes
+    every layer after the token's last decode. overlap=True forks the close of
+    layer l onto a side stream as soon as layer l's decode is done, and makes
+    only layer l's next decode wait for it: the closes (bound by the vector
+    ALU) then run beside the other layers' decodes (bound by HBM). Both orders
+    respect every dependency of the step, so they give the same results. All
+    side streams are joined before the graph ends. Capturing runs nothing; the
+    Decoders' own token counters are not used or changed."""
+    L = len(decs)
+    g = torch.cuda.CUDAGraph()
+    sides = [torch.cuda.Stream() for _ in range(L)] if overlap else []
+    pending = [None] * L
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for t in range(t0, t1):
+            for l, dec in enumerate(decs):
+                if pending[l] is not None:
+                    cap.wait_event(pending[l])
+                    pending[l] = None
+                x = inputs[l]
+                lqk.decode_step(dec.dims, dec.state, x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t],
+                                outs[l])
+                if overlap and dec.closes_at(t):
+                    ready = torch.cuda.Event()
+                    ready.record(cap)
+                    sides[l].wait_event(ready)
+                    with torch.cuda.stream(sides[l]):
+                        dec.close_due(t)
+                    pending[l] = torch.cuda.Event()
+                    pending[l].record(sides[l])
+            if not overlap:
+                for dec in decs:
+                    dec.close_due(t)
+        for ev in pending:
+            if ev is not None:
+                cap.wait_event(ev)
+    return g
