@@ -22,10 +22,12 @@
 //   broadcast with readlane. One wave covers 64 columns of a head.
 // - bf16 activations, prefill_blocks_kernel: through scalar loads a bf16 pair
 //   costs a scalar-unit split per value, which measured slower than sharing
-//   the sums: 256 threads per head on a 16 x 16 grid, each with a B x B block
-//   (B = D/16); the column partials of S'^T k and S'^T q and the partial k . q
-//   go through LDS with one barrier per token, double-buffered, and the next
-//   token's inputs load while the current one computes.
+//   the sums: 128 threads per head on an 8 x 16 grid, each with a block of
+//   D/8 key rows by D/16 value columns; the column partials of S'^T k and
+//   S'^T q and the partial k . q are summed over the wave's rows with the
+//   row-swap instructions and over the two waves through LDS, one barrier per
+//   token, double-buffered; the next token's inputs load (as raw bf16 pairs)
+//   while the current one computes.
 #include "lq_common.h"
 #include "lq_launch.h"
 
@@ -33,7 +35,7 @@ namespace lq {
 
 namespace {
 
-// ---- bf16 activations: 256 threads per head, B x B register blocks
+// ---- bf16 activations: 128 threads per head, 16 x 8 register blocks
 
 template <int N>
 __device__ __forceinline__ void ld(const float* p, float (&x)[N]) {
@@ -60,113 +62,137 @@ __device__ __forceinline__ void st(float* p, const float (&x)[N]) {
   }
 }
 
-// N consecutive activations (fp32 or bf16) starting at element idx.
+// N consecutive activations (N even) at element idx (even), kept as they are
+// loaded: bf16 pairs in N/2 words, or N fp32 words.
 template <int N, bool BF16>
-__device__ __forceinline__ void ld_act(const void* p, size_t idx, float (&x)[N]) {
-  if constexpr (BF16) {
-    const uint16_t* b = static_cast<const uint16_t*>(p) + idx;
+struct Raw {
+  uint32_t w[BF16 ? N / 2 : N];
+};
+
+template <int N, bool BF16>
+__device__ __forceinline__ void ld_raw(const void* p, size_t idx, Raw<N, BF16>& r) {
+  constexpr int NW = BF16 ? N / 2 : N;
+  const uint32_t* b = static_cast<const uint32_t*>(p) + (BF16 ? idx / 2 : idx);
+  if constexpr (NW % 4 == 0) {
 #pragma unroll
-    for (int a = 0; a < N; ++a) x[a] = as_f(uint32_t(b[a]) << 16);
+    for (int w = 0; w < NW / 4; ++w) {
+      const uint4 t = reinterpret_cast<const uint4*>(b)[w];
+      r.w[4 * w] = t.x, r.w[4 * w + 1] = t.y, r.w[4 * w + 2] = t.z, r.w[4 * w + 3] = t.w;
+    }
+  } else if constexpr (NW == 2) {
+    const uint2 t = *reinterpret_cast<const uint2*>(b);
+    r.w[0] = t.x, r.w[1] = t.y;
   } else {
-    ld<N>(static_cast<const float*>(p) + idx, x);
+    r.w[0] = b[0];
   }
 }
 
-// One token's inputs as one thread needs them.
-template <int B, bool KDA>
+template <int N, bool BF16>
+__device__ __forceinline__ float raw_at(const Raw<N, BF16>& r, int a) {
+  if constexpr (BF16) return (a & 1) ? bf16_hi(r.w[a / 2]) : bf16_lo(r.w[a / 2]);
+  else return as_f(r.w[a]);
+}
+
+// One token's inputs as one thread needs them, as loaded.
+template <int RB, int CB, bool KDA, bool BF16>
 struct Tok {
-  float k[B], q[B], v[B], g[KDA ? B : 1], beta;
+  Raw<RB, BF16> k, q;
+  Raw<CB, BF16> v;
+  float g[KDA ? RB : 1], beta;
 };
 
 template <int D, bool KDA, bool BF16>
 __device__ __forceinline__ void load_tok(const PrefillArgs& a, int t, int bh, int i0, int j0,
-                                         Tok<D / 16, KDA>& x) {
-  constexpr int B = D / 16;
+                                         Tok<D / 8, D / 16, KDA, BF16>& x) {
+  constexpr int RB = D / 8, CB = D / 16;
   const size_t row = (size_t(t) * a.n_heads + bh) * D;  // [token][head][channel]
-  ld_act<B, BF16>(a.k, row + i0, x.k);
-  ld_act<B, BF16>(a.q, row + i0, x.q);
-  ld_act<B, BF16>(a.v, row + j0, x.v);
-  if constexpr (KDA) ld<B>(a.g + row + i0, x.g);
+  ld_raw<RB, BF16>(a.k, row + i0, x.k);
+  ld_raw<RB, BF16>(a.q, row + i0, x.q);
+  ld_raw<CB, BF16>(a.v, row + j0, x.v);
+  if constexpr (KDA) ld<RB>(a.g + row + i0, x.g);
   else x.g[0] = a.g[size_t(t) * a.n_heads + bh];
   x.beta = a.beta[size_t(t) * a.n_heads + bh];
 }
 
 template <int D, bool KDA, bool BF16>
-__global__ void __launch_bounds__(256) prefill_blocks_kernel(PrefillArgs a) {
-  constexpr int B = D / 16;
-  __shared__ float sh_kq[2][4];       // per-wave partial k . q
-  __shared__ float sh_p[2][4][2][D];  // per-wave column partials of S'^T k and S'^T q
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) prefill_blocks_kernel(PrefillArgs a) {
+  constexpr int RB = D / 8, CB = D / 16;  // key rows and value columns per thread
+  __shared__ float sh_kq[2][2];           // per-wave partial k . q (double-buffered)
+  __shared__ float sh_p[2][2][2][D];      // per-wave column partials of S'^T k and S'^T q
 
   const int t = threadIdx.x, tj = t & 15, ti = t >> 4, lane = t & 63, wave = t >> 6;
   const int bh = blockIdx.x;
   const size_t hD = size_t(bh) * D;
-  const int i0 = ti * B, j0 = tj * B;
+  const int i0 = ti * RB, j0 = tj * CB;
 
-  float M[B][B];  // M[x][c] = S[i0 + x][j0 + c]
+  float M[RB][CB];  // M[x][c] = S[i0 + x][j0 + c]
 #pragma unroll
-  for (int c = 0; c < B; ++c) {
-    float col[B];
-    ld<B>(a.S + (hD + j0 + c) * D + i0, col);
+  for (int c = 0; c < CB; ++c) {
+    float col[RB];
+    ld<RB>(a.S + (hD + j0 + c) * D + i0, col);
 #pragma unroll
-    for (int x = 0; x < B; ++x) M[x][c] = col[x];
+    for (int x = 0; x < RB; ++x) M[x][c] = col[x];
   }
 
-  Tok<B, KDA> cur, nxt;
+  Tok<RB, CB, KDA, BF16> cur, nxt;
   if (a.n_tokens > 0) load_tok<D, KDA, BF16>(a, 0, bh, i0, j0, cur);
   int par = 0;
   for (int tt = 0; tt < a.n_tokens; ++tt) {
     if (tt + 1 < a.n_tokens) load_tok<D, KDA, BF16>(a, tt + 1, bh, i0, j0, nxt);
+    float kx[RB], qx[RB];
+#pragma unroll
+    for (int x = 0; x < RB; ++x) kx[x] = raw_at(cur.k, x), qx[x] = raw_at(cur.q, x);
     // decay, then the column partials of S'^T k and S'^T q over this thread's rows
-    float al[B];
+    float pk[CB], pq[CB], kq = 0.f;
 #pragma unroll
-    for (int x = 0; x < B; ++x) al[x] = exp_fast(KDA ? cur.g[x] : cur.g[0]);
-    float pk[B], pq[B], kq = 0.f;
+    for (int x = 0; x < RB; ++x) kq = fmaf(kx[x], qx[x], kq);
 #pragma unroll
-    for (int x = 0; x < B; ++x) kq = fmaf(cur.k[x], cur.q[x], kq);
+    for (int c = 0; c < CB; ++c) pk[c] = pq[c] = 0.f;
 #pragma unroll
-    for (int c = 0; c < B; ++c) {
-      float sk = 0.f, sq = 0.f;
+    for (int x = 0; x < RB; ++x) {
+      const float al = exp_fast(KDA ? cur.g[x] : cur.g[0]);
 #pragma unroll
-      for (int x = 0; x < B; ++x) {
-        M[x][c] *= al[x];
-        sk = fmaf(M[x][c], cur.k[x], sk);
-        sq = fmaf(M[x][c], cur.q[x], sq);
+      for (int c = 0; c < CB; ++c) {
+        M[x][c] *= al;
+        pk[c] = fmaf(M[x][c], kx[x], pk[c]);
+        pq[c] = fmaf(M[x][c], qx[x], pq[c]);
       }
-      pk[c] = rows_sum(sk);
-      pq[c] = rows_sum(sq);
     }
-    kq = rows_sum(kq);  // the wave's four key-row groups
+    // sums over key rows: the wave's four row groups, then the two waves
+#pragma unroll
+    for (int c = 0; c < CB; ++c) pk[c] = rows_sum(pk[c]), pq[c] = rows_sum(pq[c]);
+    kq = rows_sum(kq);
     if (lane < 16) {
-      st<B>(&sh_p[par][wave][0][j0], pk);
-      st<B>(&sh_p[par][wave][1][j0], pq);
+      st<CB>(&sh_p[par][wave][0][j0], pk);
+      st<CB>(&sh_p[par][wave][1][j0], pq);
       if (lane == 0) sh_kq[par][wave] = kq;
     }
     __syncthreads();
-    const float kqs = (sh_kq[par][0] + sh_kq[par][1]) + (sh_kq[par][2] + sh_kq[par][3]);
-    float u[B], o[B];
+    const float kqs = sh_kq[par][0] + sh_kq[par][1];
+    float u[CB], o[CB];
 #pragma unroll
-    for (int c = 0; c < B; ++c) {
+    for (int c = 0; c < CB; ++c) {
       const int j = j0 + c;
-      const float yk = (sh_p[par][0][0][j] + sh_p[par][1][0][j]) + (sh_p[par][2][0][j] + sh_p[par][3][0][j]);
-      const float yq = (sh_p[par][0][1][j] + sh_p[par][1][1][j]) + (sh_p[par][2][1][j] + sh_p[par][3][1][j]);
-      u[c] = cur.beta * (cur.v[c] - yk);
+      const float yk = sh_p[par][0][0][j] + sh_p[par][1][0][j];
+      const float yq = sh_p[par][0][1][j] + sh_p[par][1][1][j];
+      u[c] = cur.beta * (raw_at(cur.v, c) - yk);
       o[c] = fmaf(kqs, u[c], yq);
     }
 #pragma unroll
-    for (int x = 0; x < B; ++x)
+    for (int x = 0; x < RB; ++x)
 #pragma unroll
-      for (int c = 0; c < B; ++c) M[x][c] = fmaf(cur.k[x], u[c], M[x][c]);
-    if (ti == 0) st<B>(a.o + (size_t(tt) * a.n_heads + bh) * D + j0, o);
+      for (int c = 0; c < CB; ++c) M[x][c] = fmaf(kx[x], u[c], M[x][c]);
+    if (ti == 0) st<CB>(a.o + (size_t(tt) * a.n_heads + bh) * D + j0, o);
     par ^= 1;
     cur = nxt;
   }
 
 #pragma unroll
-  for (int c = 0; c < B; ++c) {
-    float col[B];
+  for (int c = 0; c < CB; ++c) {
+    float col[RB];
 #pragma unroll
-    for (int x = 0; x < B; ++x) col[x] = M[x][c];
-    st<B>(a.S + (hD + j0 + c) * D + i0, col);
+    for (int x = 0; x < RB; ++x) col[x] = M[x][c];
+    st<RB>(a.S + (hD + j0 + c) * D + i0, col);
   }
 }
 
@@ -299,7 +325,7 @@ __global__ void __launch_bounds__(64) prefill_columns_kernel(PrefillArgs a) {
 template <int D, bool KDA, bool BF16>
 hipError_t launch(const lq_dims& d, const PrefillArgs& a, hipStream_t stream) {
   if constexpr (BF16) {
-    hipLaunchKernelGGL((prefill_blocks_kernel<D, KDA, BF16>), dim3(d.batch * d.heads), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_blocks_kernel<D, KDA, BF16>), dim3(d.batch * d.heads), dim3(128), 0, stream, a);
   } else {
     constexpr int WPH = D > 64 ? D / 64 : 1;
     hipLaunchKernelGGL((prefill_columns_kernel<D, KDA, BF16>), dim3(d.batch * d.heads * WPH), dim3(64), 0,
