@@ -183,20 +183,23 @@ def test_outputs_free_running(name, bits, steps, kw):
     assert np.all(err_t <= np.maximum(1e-3, 4 * env_t))
 
 
-@pytest.mark.parametrize("name,bits,n_tok,close_seqs", [
-    ("qwen_gdn", 8, 16, None),          # full window, every sequence
-    ("kda_int4", 4, 16, None),
-    ("kda_int4", 8, 16, None),
-    ("tiny_gdn", 8, 5, [1]),            # partial window, one sequence of two
-    ("prefix_mix", 8, 11, [0, 3, 5]),   # partial windows, a close list
-    ("qwen_gdn", 6, 16, None),
-    ("tiny_gdn", 6, 5, [1]),
+@pytest.mark.parametrize("name,bits,n_tok,close_seqs,kw", [
+    ("qwen_gdn", 8, 16, None, {}),          # full window, every sequence
+    ("kda_int4", 4, 16, None, {}),
+    ("kda_int4", 8, 16, None, {}),
+    ("tiny_gdn", 8, 5, [1], {}),            # partial window, one sequence of two
+    ("prefix_mix", 8, 11, [0, 3, 5], {}),   # partial windows, a close list
+    ("qwen_gdn", 6, 16, None, {}),
+    ("tiny_gdn", 6, 5, [1], {}),            # d = 32: four threads share a low-bit word
+    ("tiny_gdn", 6, 7, [0], dict(d_k=64, d_v=64)),             # d = 64: two threads share it
+    ("tiny_gdn", 4, 9, None, dict(d_k=64, d_v=64, kda=True)),
 ])
-def test_close_codes_and_decomposition(name, bits, n_tok, close_seqs):
+def test_close_codes_and_decomposition(name, bits, n_tok, close_seqs, kw):
     """G1 + G2 at a window close: the oracle folds the GPU's pre-close buffers;
     the GPU's compensators plus its residual must rebuild that fold, and its
     codes must match the oracle's quantisation of its own residual."""
-    wl = W[name].replace(batch=8 if W[name].batch >= 8 else W[name].batch + 1)
+    base = W[name].replace(**kw) if kw else W[name]
+    wl = base.replace(batch=8 if base.batch >= 8 else base.batch + 1)
     dims = runner.dims_for(wl, bits)
     dec = runner.Decoder(dims, np.full(wl.batch, wl.w_max), np.zeros(wl.batch, np.int32))
     dec.encode(runner.states_to_device(wk.initial_states(wl, range(wl.batch))))
@@ -287,11 +290,15 @@ def test_max_window_and_compensators():
     assert worst <= 1e-3, worst
 
 
-@pytest.mark.parametrize("d,kda", [(64, False), (64, True), (32, True)])
-def test_other_head_dims(d, kda):
+@pytest.mark.parametrize("d,kda,bits", [(64, False, 8), (64, True, 8), (32, True, 8), (64, False, 6), (64, True, 4),
+                                         (32, False, 4), (32, True, 6)])
+def test_other_head_dims(d, kda, bits):
+    """Outputs over 40 tokens (two closes) at d = 32 and 64, teacher-forced (G3):
+    the code layouts and the close's cross-thread low-bit words of the narrower
+    heads."""
     wl = W["tiny_gdn"].replace(batch=3, heads=2, d_k=d, d_v=d, kda=kda, steps=40)
-    o_gpu, _, err = gh.run_gpu(wl, 40, [0, 1, 2])
-    ref = gh.run_oracle(wl, 40, [0, 1, 2])
+    ref = gh.run_oracle(wl, 40, [0, 1, 2], bits, record=True)
+    o_gpu, _, err = gh.run_gpu(wl, 40, [0, 1, 2], bits, force=ref)
     assert err == 0
     assert max(gh.rel_l2(o_gpu[t], ref["o"][t]) for t in range(40)) <= 1e-3
 
