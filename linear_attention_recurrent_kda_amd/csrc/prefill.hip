@@ -69,11 +69,19 @@ struct Raw {
   uint32_t w[BF16 ? N / 2 : N];
 };
 
+// fp32 rows move in 16-byte pieces; bf16 rows in 8-byte pieces, the alignment
+// the C ABI requires of bf16 activations.
 template <int N, bool BF16>
 __device__ __forceinline__ void ld_raw(const void* p, size_t idx, Raw<N, BF16>& r) {
   constexpr int NW = BF16 ? N / 2 : N;
   const uint32_t* b = static_cast<const uint32_t*>(p) + (BF16 ? idx / 2 : idx);
-  if constexpr (NW % 4 == 0) {
+  if constexpr (BF16 && NW % 2 == 0) {
+#pragma unroll
+    for (int w = 0; w < NW / 2; ++w) {
+      const uint2 t = reinterpret_cast<const uint2*>(b)[w];
+      r.w[2 * w] = t.x, r.w[2 * w + 1] = t.y;
+    }
+  } else if constexpr (NW % 4 == 0) {
 #pragma unroll
     for (int w = 0; w < NW / 4; ++w) {
       const uint4 t = reinterpret_cast<const uint4*>(b)[w];
