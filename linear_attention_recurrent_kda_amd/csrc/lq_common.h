@@ -122,7 +122,7 @@ __device__ __forceinline__ void store16(float* p, const float (&x)[16]) {
 
 // SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): output number n (1-based)
 // of the generator started from state 0.
-__device__ __forceinline__ uint64_t splitmix64(uint64_t n) {
+__host__ __device__ constexpr uint64_t splitmix64(uint64_t n) {
   uint64_t z = n * 0x9E3779B97F4A7C15ull;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
@@ -131,9 +131,20 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t n) {
 
 // Power-method start vector entry v0[l][j]: the top 23 bits m of output
 // l*d_v + j + 1 give (2m + 1 - 2^23) / 2^23, exact in fp32.
-__device__ __forceinline__ float start_vec(int l, int j, int d_v) {
+__host__ __device__ constexpr float start_vec(int l, int j, int d_v) {
   const uint64_t m = splitmix64(uint64_t(l) * uint64_t(d_v) + uint64_t(j) + 1ull) >> 41;
   return float(int32_t(2 * m + 1) - (1 << 23)) * 0x1p-23f;
 }
+
+// The start vectors of up to R compensators at head dimension D, evaluated at
+// compile time: the same for every head and every window.
+template <int R, int D>
+struct StartVectors {
+  float v[R][D];
+  constexpr StartVectors() : v{} {
+    for (int l = 0; l < R; ++l)
+      for (int j = 0; j < D; ++j) v[l][j] = start_vec(l, j, D);
+  }
+};
 
 }  // namespace lq

@@ -145,6 +145,10 @@ __device__ __forceinline__ uint32_t or_swap32(uint32_t x) {  // x | x of lane ^ 
   return uint32_t(p[0]) | uint32_t(p[1]);
 }
 
+// Power-method start vectors for up to 8 compensators (the ABI's limit).
+template <int D>
+__constant__ constexpr StartVectors<8, D> kStart{};
+
 template <int D, int BITS, bool KDA, bool DENSE>
 __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   constexpr int RB = D / 8;   // key rows per thread
@@ -294,7 +298,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
         p = 0.f;
 #pragma unroll
         for (int bb = 0; bb < CB; ++bb) {
-          v[bb] = start_vec(l, j0 + bb, D);
+          v[bb] = kStart<D>.v[l][j0 + bb];
           p = fmaf(v[bb], v[bb], p);
         }
         p = group_sum<16>(p);
