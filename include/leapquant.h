@@ -18,7 +18,7 @@
  *   S = exp(G) (.) diag(s) C diag(c) + sum_e exp(G - G_e) (.) k_e u_e^T
  * where G is the cumulative log-decay since the window start and (.) scales
  * key rows. The first r entries are the compensator tokens (unit keys, G_e = 0:
- * they sit at window position 0 and share the update path of real tokens);
+ * they sit at window position 0 and take the same update path as tokens);
  * the next n are the window's buffered tokens, G_e = G at that token.
  *
  * Conventions for every entry point:
@@ -156,7 +156,7 @@ int leapquant_decode_step(const lq_dims* dims, const lq_state* st, const void* q
    (G_n = G of the last entry), re-extract the compensators into entries
    0..r-1, re-smooth, requantise, and empty the buffer (buf_len = 0).
    A partly filled buffer is legal (a partial window). Sources: LeapQuant
-   abstract (quantize once at the window end; compensators and smoothing).
+   abstract (one requantization per window; compensators and smoothing).
    seq_ids: int32 [n_seq] distinct sequence ids in [0, B), or NULL for all B
    sequences (n_seq is then ignored). An id outside [0, B) is skipped and
    LQ_DEVERR_BAD_SEQ is or-ed into *st->err. Duplicated ids race.

@@ -1,11 +1,10 @@
 // LeapQuant decode step for GDN / KDA recurrent states on gfx950.
 //
 // Per-window quantization (LeapQuant abstract; wink.run article, first
-// technique): inside a window the low-bit state is fixed and each token's
-// update is buffered in fp32; the token's output is read from the fixed state
-// plus the buffered updates. Compensators are rank-one terms of the same form
-// as token updates sitting at window position 0 (abstract; article, second
-// technique). The gated delta rule itself follows Gated DeltaNet (Yang et al.)
+// technique): the quantized state stays frozen for a window, each token's
+// update joins an fp32 buffer, and a token's output combines the frozen state
+// with that buffer. Compensators are rank-one terms shaped like token updates,
+// parked at window position 0 (abstract; article, second technique). The gated delta rule itself follows Gated DeltaNet (Yang et al.)
 // and Kimi Delta Attention (Kimi Linear report).
 //
 // One workgroup of D threads (two waves for D = 128) per head, small enough

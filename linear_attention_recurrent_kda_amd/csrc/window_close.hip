@@ -1,6 +1,6 @@
 // LeapQuant window close and initial encode on gfx950.
 //
-// At a window boundary (LeapQuant abstract: quantize once at the window end)
+// At a window boundary (LeapQuant abstract: a single requantization per window)
 // the buffered token updates are folded into the dense state, the largest
 // outliers are re-extracted as r rank-one compensator tokens (abstract and
 // wink.run article, compensator tokens; here a T-step power method with

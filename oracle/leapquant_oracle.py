@@ -103,9 +103,9 @@ def exact_step(S, q, k, v, g, beta):
 
 # ---------------------------------------------------------------------------
 # Window close / encode: compensators, smoothing, quantisation
-# [abstract] and [article]: compensator tokens keep the largest outliers as a
-# few high-precision rank-one outer products shaped like token updates; the
-# rest is smoothed per key row and quantised once per window.
+# [abstract] and [article]: the biggest outliers leave the state as a few
+# fp32 rank-one terms with the shape of token updates (the compensator
+# tokens); what remains is smoothed per key row and quantised once per window.
 # ---------------------------------------------------------------------------
 def extract_compensators(S: np.ndarray, r: int, T: int, start: Optional[np.ndarray] = None):
     """E2: r compensators by a fixed-iteration power method with deflation.
@@ -289,9 +289,10 @@ def run_dense(S_init, tokens: Iterable[Dict[str, np.ndarray]], win_len, win_off,
 # ---------------------------------------------------------------------------
 # Buffered form: what a decode kernel computes inside a window, written
 # separately from run_dense. Used to pin the window algebra.
-# [abstract]: inside a window outputs come from the fixed low-bit state plus
-# high-precision buffered updates; compensators share the update path of
-# real tokens (they sit at window position 0 and decay with the residual).
+# [abstract]: within a window an output reads the frozen quantised state and
+# the fp32 updates buffered so far; compensators are handled exactly like
+# buffered token updates (they sit at window position 0 and decay with the
+# residual).
 # ---------------------------------------------------------------------------
 class BufferedOracle:
     """State = (window-start Enc, buffer of (k_m, u_m, G_m)), G = cumulative
