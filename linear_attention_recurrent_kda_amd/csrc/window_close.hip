@@ -145,6 +145,32 @@ __device__ __forceinline__ uint32_t or_swap32(uint32_t x) {  // x | x of lane ^ 
   return uint32_t(p[0]) | uint32_t(p[1]);
 }
 
+// Column sums over the four 16-lane rows of a wave, the work split across the
+// rows: each row-swap step pairs two columns, one kept by each half of the
+// lanes. For CB >= 4, lane row g ends with the totals of columns
+// g * CB / 4 + m (m < CB / 4); for CB = 2, with column g / 2's total.
+template <int CB>
+__device__ __forceinline__ void rows_sum_split(float (&p)[CB], float (&out)[CB >= 4 ? CB / 4 : 1]) {
+  constexpr int H = CB / 2;
+  float q[H];
+#pragma unroll
+  for (int m = 0; m < H; ++m) {
+    auto s = __builtin_amdgcn_permlane32_swap(as_u(p[m]), as_u(p[m + H]), false, false);
+    q[m] = as_f(s[0]) + as_f(s[1]);  // lanes 0-31: column m; lanes 32-63: column m + H
+  }
+  if constexpr (CB >= 4) {
+    constexpr int Q = CB / 4;
+#pragma unroll
+    for (int m = 0; m < Q; ++m) {
+      auto s = __builtin_amdgcn_permlane16_swap(as_u(q[m]), as_u(q[m + Q]), false, false);
+      out[m] = as_f(s[0]) + as_f(s[1]);  // even rows: q[m]; odd rows: q[m + Q]
+    }
+  } else {
+    auto s = __builtin_amdgcn_permlane16_swap(as_u(q[0]), as_u(q[0]), false, false);
+    out[0] = as_f(s[0]) + as_f(s[1]);
+  }
+}
+
 // Power-method start vectors for up to 8 compensators (the ABI's limit).
 template <int D>
 __constant__ constexpr StartVectors<8, D> kStart{};
@@ -306,9 +332,10 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       const float inv_nv = __builtin_amdgcn_rsqf(p);
 #pragma unroll
       for (int bb = 0; bb < CB; ++bb) v[bb] *= inv_nv;
+      float inv_rk = 0.f;
       for (int it = 0; it < a.T; ++it) {
         // kappa = M v (sum over value columns: DPP across the 16 tj lanes),
-        // kept in kk and scaled to the unit key once its norm is known
+        // kept in kk; only the last iteration's is scaled to the unit key
         float pk = 0.f;
 #pragma unroll
         for (int x = 0; x < RB; ++x) {
@@ -319,13 +346,25 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
           pk = fmaf(kk[x], kk[x], pk);
         }
         // M^T kappa (sum over key rows: the wave's four rows, then the two waves)
+        {
+          float cs[CB], tot[CB >= 4 ? CB / 4 : 1];
 #pragma unroll
-        for (int bb = 0; bb < CB; ++bb) {
-          float s = 0.f;
+          for (int bb = 0; bb < CB; ++bb) {
+            float s = 0.f;
 #pragma unroll
-          for (int x = 0; x < RB; ++x) s = fmaf(M[x][bb], kk[x], s);
-          s = rows_sum(s);
-          if (lane < 16) sh_c[par][wave][j0 + bb] = s;
+            for (int x = 0; x < RB; ++x) s = fmaf(M[x][bb], kk[x], s);
+            cs[bb] = s;
+          }
+          rows_sum_split<CB>(cs, tot);
+          const int g = lane >> 4;
+          static_assert(CB == 8 || CB == 4 || CB == 2, "columns per thread");
+          if constexpr (CB == 8) {
+            *reinterpret_cast<float2*>(&sh_c[par][wave][j0 + 2 * g]) = make_float2(tot[0], tot[1]);
+          } else if constexpr (CB == 4) {
+            sh_c[par][wave][j0 + g] = tot[0];
+          } else {
+            sh_c[par][wave][j0 + (g >> 1)] = tot[0];  // rows 2m and 2m+1 hold the same total
+          }
         }
         pk = rows_sum(pk);  // the wave's rows; pk was already equal across the 16 tj lanes
         if (lane == 0) sh_n[par][wave] = pk;
@@ -335,9 +374,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
           live = false;
           break;
         }
-        const float inv_rk = __builtin_amdgcn_rsqf(nk2);
-#pragma unroll
-        for (int x = 0; x < RB; ++x) kk[x] *= inv_rk;
+        inv_rk = __builtin_amdgcn_rsqf(nk2);
         // w = M^T k = (M^T kappa) / |kappa|
         float pw = 0.f;
 #pragma unroll
@@ -356,6 +393,8 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
 #pragma unroll
         for (int bb = 0; bb < CB; ++bb) v[bb] = w[bb] * inv_rw;
       }
+#pragma unroll
+      for (int x = 0; x < RB; ++x) kk[x] *= inv_rk;
     }
     if (!live) {
 #pragma unroll
