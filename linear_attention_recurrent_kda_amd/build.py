@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 VALU instructions stay off: scalar fp32 FMA only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the window close keeps its fp32
+    # state in registers that the vector ALU reads directly
+    "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]

@@ -27,6 +27,8 @@ namespace {
 
 constexpr int NT = 128;  // threads per head
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 template <int B>
 __device__ __forceinline__ void loadB(const float* p, float (&x)[B]) {
   if constexpr (B % 4 == 0) {
@@ -184,7 +186,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   constexpr int CH = 16;                    // entries staged in LDS per fold pass
   constexpr int V4 = D / 4;                 // float4 per entry row
   constexpr int PER = CH * V4 / NT;         // float4 per thread per staged array
-  static_assert(NT % V4 == 0 && PER >= 1, "staging shape");
+  static_assert(NT % V4 == 0 && PER >= 1 && PER * NT == CH * V4, "staging shape");
   __shared__ float sh_n[2][2];                // per-wave squared norms (double-buffered)
   __shared__ __align__(16) float sh_c[2][2][D];  // per-wave column partials (double-buffered)
   __shared__ __align__(16) float sh_k[DENSE ? 1 : CH][D];  // keys scaled by their decay to the window end
@@ -208,14 +210,15 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   const size_t erow = size_t(bh) * (r + a.w_max);  // first entry row of this head
 
   // ---- the dense state block M[x][bb] = S[i0 + x][j0 + bb]
-  float M[RB][CB];
+  // (four consecutive key rows of one value column form one MFMA accumulator)
+  v4f M[RB / 4][CB];
   if constexpr (DENSE) {
 #pragma unroll
     for (int bb = 0; bb < CB; ++bb) {
       float col[RB];
       loadB<RB>(a.S + (hD + j0 + bb) * D + i0, col);
 #pragma unroll
-      for (int x = 0; x < RB; ++x) M[x][bb] = col[x];
+      for (int x = 0; x < RB; ++x) M[x >> 2][bb][x & 3] = col[x];
     }
   } else {
     // fold: S = exp(G_n) (.) diag(s) C diag(c) + sum_e exp(G_n - G_e) (.) k_e u_e^T
@@ -245,13 +248,13 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       if constexpr (BITS == 6) load_codes6<RB, D>(cb, j0 + bb, i0, code);
       else load_codes<RB, BITS>(cb + size_t(j0 + bb) * (D * BITS / 8) + i0 * BITS / 8, code);
 #pragma unroll
-      for (int x = 0; x < RB; ++x) M[x][bb] = (si[x] * float(code[x])) * cj[bb];
+      for (int x = 0; x < RB; ++x) M[x >> 2][bb][x & 3] = (si[x] * float(code[x])) * cj[bb];
     }
 #pragma unroll
     for (int x = 0; x < RB; ++x) {
       const float e = expf(KDA ? Gn[x] : Gn[0]);
 #pragma unroll
-      for (int bb = 0; bb < CB; ++bb) M[x][bb] *= e;
+      for (int bb = 0; bb < CB; ++bb) M[x >> 2][bb][x & 3] *= e;
     }
     // entries, CH at a time: the workgroup stages the rows in LDS with one
     // round of loads, each key already multiplied by its decay to the window
@@ -262,15 +265,26 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     if constexpr (KDA) {
       if (E > 0) gq = *reinterpret_cast<const float4*>(a.eg + (erow + E - 1) * D + 4 * c4);
     }
+    // The rank-CH update M += K^T U of a pass runs on the matrix cores
+    // (v_mfma_f32_16x16x4f32, four entries per instruction). Its 16 x 16
+    // output tile puts rows 4 (lane / 16) + q of column lane % 16 in lane
+    // 'lane', register q; the operands' rows and columns are chosen so that
+    // these are exactly this thread's key rows i0 + 4 a + q and value column
+    // j0 + bb, for tile (a, bb).
+    const int e_of_lane = lane >> 4;  // the operands' entry within a block of four
+    const int a_row = wave * 4 * RB + RB * ((lane & 15) >> 2) + (lane & 3);  // + 4 a
+    const int b_col = CB * (lane & 15);                                      // + bb
     for (int m0 = 0; m0 < E; m0 += CH) {
       const int cnt = min(CH, E - m0);
       __syncthreads();  // the previous pass has consumed the staged rows
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
-        const int row = (t + NT * p) / V4;
+        const int row = (t + NT * p) / V4;  // covers all CH rows; rows past cnt are zeros
+        float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), uq = kq;
         if (row < cnt) {
           const size_t g = (erow + m0 + row) * D + 4 * c4;
-          float4 kq = *reinterpret_cast<const float4*>(a.ek + g);
+          kq = *reinterpret_cast<const float4*>(a.ek + g);
+          uq = *reinterpret_cast<const float4*>(a.eu + g);
           if constexpr (KDA) {
             const float4 ge = *reinterpret_cast<const float4*>(a.eg + g);
             kq.x *= expf(gq.x - ge.x);
@@ -281,19 +295,22 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
             const float f = expf(Gn[0] - a.eg[erow + m0 + row]);
             kq.x *= f, kq.y *= f, kq.z *= f, kq.w *= f;
           }
-          reinterpret_cast<float4*>(&sh_k[row][0])[c4] = kq;
-          reinterpret_cast<float4*>(&sh_u[row][0])[c4] = *reinterpret_cast<const float4*>(a.eu + g);
         }
+        reinterpret_cast<float4*>(&sh_k[row][0])[c4] = kq;
+        reinterpret_cast<float4*>(&sh_u[row][0])[c4] = uq;
       }
       __syncthreads();
-      for (int m = 0; m < cnt; ++m) {
-        float km[RB], um[CB];
-        loadB<RB>(&sh_k[m][i0], km);
-        loadB<CB>(&sh_u[m][j0], um);
+      const int nkb = (cnt + 3) >> 2;
+      for (int kb = 0; kb < nkb; ++kb) {
+        const int e = 4 * kb + e_of_lane;
+        float ka[RB / 4], ub[CB];
 #pragma unroll
-        for (int x = 0; x < RB; ++x)
+        for (int q = 0; q < RB / 4; ++q) ka[q] = sh_k[e][a_row + 4 * q];
+        loadB<CB>(&sh_u[e][b_col], ub);
 #pragma unroll
-          for (int bb = 0; bb < CB; ++bb) M[x][bb] = fmaf(km[x], um[bb], M[x][bb]);
+        for (int q = 0; q < RB / 4; ++q)
+#pragma unroll
+          for (int bb = 0; bb < CB; ++bb) M[q][bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[q], ub[bb], M[q][bb], 0, 0, 0);
       }
     }
   }
@@ -341,7 +358,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
         for (int x = 0; x < RB; ++x) {
           float s = 0.f;
 #pragma unroll
-          for (int bb = 0; bb < CB; ++bb) s = fmaf(M[x][bb], v[bb], s);
+          for (int bb = 0; bb < CB; ++bb) s = fmaf(M[x >> 2][bb][x & 3], v[bb], s);
           kk[x] = group_sum<16>(s);
           pk = fmaf(kk[x], kk[x], pk);
         }
@@ -352,7 +369,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
           for (int bb = 0; bb < CB; ++bb) {
             float s = 0.f;
 #pragma unroll
-            for (int x = 0; x < RB; ++x) s = fmaf(M[x][bb], kk[x], s);
+            for (int x = 0; x < RB; ++x) s = fmaf(M[x >> 2][bb][x & 3], kk[x], s);
             cs[bb] = s;
           }
           rows_sum_split<CB>(cs, tot);
@@ -418,7 +435,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
 #pragma unroll
     for (int x = 0; x < RB; ++x)
 #pragma unroll
-      for (int bb = 0; bb < CB; ++bb) M[x][bb] = fmaf(-kk[x], w[bb], M[x][bb]);
+      for (int bb = 0; bb < CB; ++bb) M[x >> 2][bb][x & 3] = fmaf(-kk[x], w[bb], M[x >> 2][bb][x & 3]);
   }
 
   if (a.dbg) {
@@ -426,7 +443,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     for (int bb = 0; bb < CB; ++bb) {
       float col[RB];
 #pragma unroll
-      for (int x = 0; x < RB; ++x) col[x] = M[x][bb];
+      for (int x = 0; x < RB; ++x) col[x] = M[x >> 2][bb][x & 3];
       storeB<RB>(a.dbg + (hD + j0 + bb) * D + i0, col);
     }
   }
@@ -437,12 +454,12 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   for (int x = 0; x < RB; ++x) {
     float m = 0.f;
 #pragma unroll
-    for (int bb = 0; bb < CB; ++bb) m = fmaxf(m, fabsf(M[x][bb]));
+    for (int bb = 0; bb < CB; ++bb) m = fmaxf(m, fabsf(M[x >> 2][bb][x & 3]));
     m = group_max<16>(m);
     sa[x] = (a.smoothing && m > 0.f) ? m : 1.f;
     const float rs = 1.f / sa[x];
 #pragma unroll
-    for (int bb = 0; bb < CB; ++bb) M[x][bb] *= rs;
+    for (int bb = 0; bb < CB; ++bb) M[x >> 2][bb][x & 3] *= rs;
   }
 
   // ---- value-column scales and codes
@@ -451,7 +468,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   for (int bb = 0; bb < CB; ++bb) {
     float m = 0.f;
 #pragma unroll
-    for (int x = 0; x < RB; ++x) m = fmaxf(m, fabsf(M[x][bb]));
+    for (int x = 0; x < RB; ++x) m = fmaxf(m, fabsf(M[x >> 2][bb][x & 3]));
     m = rows_max(m);
     if (lane < 16) sh_c[0][wave][j0 + bb] = m;
   }
@@ -467,7 +484,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     int code[RB];
 #pragma unroll
     for (int x = 0; x < RB; ++x) {
-      const float qv = fminf(fmaxf(rintf(M[x][bb] * inv), -float(Q)), float(Q));
+      const float qv = fminf(fmaxf(rintf(M[x >> 2][bb][x & 3] * inv), -float(Q)), float(Q));
       code[x] = int(qv);
     }
     if constexpr (BITS == 6) {
