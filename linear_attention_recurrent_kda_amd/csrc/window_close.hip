@@ -173,6 +173,72 @@ __device__ __forceinline__ void rows_sum_split(float (&p)[CB], float (&out)[CB >
   }
 }
 
+// The same split for maxima, and its inverse: NV values per lane row (row g
+// holding columns g * NV + m) gathered so that every lane holds all 4 NV in
+// column order.
+template <int CB>
+__device__ __forceinline__ void rows_max_split(float (&p)[CB], float (&out)[CB / 4]) {
+  static_assert(CB >= 4, "columns per thread");
+  constexpr int H = CB / 2, Q = CB / 4;
+  float q[H];
+#pragma unroll
+  for (int m = 0; m < H; ++m) {
+    auto s = __builtin_amdgcn_permlane32_swap(as_u(p[m]), as_u(p[m + H]), false, false);
+    q[m] = fmaxf(as_f(s[0]), as_f(s[1]));
+  }
+#pragma unroll
+  for (int m = 0; m < Q; ++m) {
+    auto s = __builtin_amdgcn_permlane16_swap(as_u(q[m]), as_u(q[m + Q]), false, false);
+    out[m] = fmaxf(as_f(s[0]), as_f(s[1]));
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void rows_gather(const float (&x)[NV], float (&out)[4 * NV]) {
+  float y[2 * NV];
+#pragma unroll
+  for (int m = 0; m < NV; ++m) {  // rows (0, 1) and (2, 3): the even row's values first
+    auto s = __builtin_amdgcn_permlane16_swap(as_u(x[m]), as_u(x[m]), false, false);
+    y[m] = as_f(s[0]), y[NV + m] = as_f(s[1]);
+  }
+#pragma unroll
+  for (int k = 0; k < 2 * NV; ++k) {  // lanes 0-31 and 32-63: the lower half's values first
+    auto s = __builtin_amdgcn_permlane32_swap(as_u(y[k]), as_u(y[k]), false, false);
+    out[k] = as_f(s[0]), out[2 * NV + k] = as_f(s[1]);
+  }
+}
+
+// Maxima of 16 per-row values over the 16 lanes of a DPP row, the work split
+// so that lane c ends with value c's maximum: each step pairs lane c with
+// c ^ 15, c ^ 7, c ^ 2, c ^ 1 and keeps the half of the values whose index
+// bit matches c's (bit 3, 2, 1, 0), the partner sending the other half.
+__device__ __forceinline__ float row_max_split16(const float (&x)[16], int c) {
+  float a8[8], a4[4], a2[2];
+  const bool b3 = c & 8, b2 = c & 4, b1 = c & 2, b0 = c & 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    a8[k] = fmaxf(b3 ? x[k + 8] : x[k], dpp<DPP_MIRROR>(b3 ? x[k] : x[k + 8]));
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    a4[k] = fmaxf(b2 ? a8[k + 4] : a8[k], dpp<DPP_HALF_MIRROR>(b2 ? a8[k] : a8[k + 4]));
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    a2[k] = fmaxf(b1 ? a4[k + 2] : a4[k], dpp<DPP_QUAD_XOR2>(b1 ? a4[k] : a4[k + 2]));
+  return fmaxf(b0 ? a2[1] : a2[0], dpp<DPP_QUAD_XOR1>(b0 ? a2[0] : a2[1]));
+}
+
+// M[x][..] *= (value of lane x of this thread's DPP row) for x = X..15.
+template <int X, int CB, typename T>
+__device__ __forceinline__ void scale_rows_bcast(T (&M)[4][CB], float r) {
+  if constexpr (X < 16) {
+    const float f = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, r), 0x150 + X, 0xF, 0xF, false));
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) M[X >> 2][bb][X & 3] *= f;
+    scale_rows_bcast<X + 1, CB>(M, r);
+  }
+}
+
 // Power-method start vectors for up to 8 compensators (the ABI's limit).
 template <int D>
 __constant__ constexpr StartVectors<8, D> kStart{};
@@ -243,18 +309,14 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     }
     const uint8_t* cb = static_cast<const uint8_t*>(a.codes) + size_t(bh) * HB;
 #pragma unroll
+    for (int x = 0; x < RB; ++x) si[x] *= expf(KDA ? Gn[x] : Gn[0]);  // the residual's decay to the window end
+#pragma unroll
     for (int bb = 0; bb < CB; ++bb) {
       int code[RB];
       if constexpr (BITS == 6) load_codes6<RB, D>(cb, j0 + bb, i0, code);
       else load_codes<RB, BITS>(cb + size_t(j0 + bb) * (D * BITS / 8) + i0 * BITS / 8, code);
 #pragma unroll
       for (int x = 0; x < RB; ++x) M[x >> 2][bb][x & 3] = (si[x] * float(code[x])) * cj[bb];
-    }
-#pragma unroll
-    for (int x = 0; x < RB; ++x) {
-      const float e = expf(KDA ? Gn[x] : Gn[0]);
-#pragma unroll
-      for (int bb = 0; bb < CB; ++bb) M[x >> 2][bb][x & 3] *= e;
     }
     // entries, CH at a time: the workgroup stages the rows in LDS with one
     // round of loads, each key already multiplied by its decay to the window
@@ -448,43 +510,89 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     }
   }
 
-  // ---- key-row smoothing scales
+  // ---- key-row smoothing scales. At D = 128 a thread's 16 rows are the 16
+  // lanes of its DPP row: lane tj takes row i0 + tj's maximum and reciprocal,
+  // and the reciprocals are broadcast back.
   float sa[RB];
+  if constexpr (RB == 16) {
+    float rx[RB];
 #pragma unroll
-  for (int x = 0; x < RB; ++x) {
-    float m = 0.f;
+    for (int x = 0; x < RB; ++x) {
+      float m = 0.f;
 #pragma unroll
-    for (int bb = 0; bb < CB; ++bb) m = fmaxf(m, fabsf(M[x >> 2][bb][x & 3]));
-    m = group_max<16>(m);
-    sa[x] = (a.smoothing && m > 0.f) ? m : 1.f;
-    const float rs = 1.f / sa[x];
+      for (int bb = 0; bb < CB; ++bb) m = fmaxf(m, fabsf(M[x >> 2][bb][x & 3]));
+      rx[x] = m;
+    }
+    const float m = row_max_split16(rx, tj);
+    sa[0] = (a.smoothing && m > 0.f) ? m : 1.f;
+    scale_rows_bcast<0, CB>(M, 1.f / sa[0]);
+  } else {
 #pragma unroll
-    for (int bb = 0; bb < CB; ++bb) M[x >> 2][bb][x & 3] *= rs;
+    for (int x = 0; x < RB; ++x) {
+      float m = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < CB; ++bb) m = fmaxf(m, fabsf(M[x >> 2][bb][x & 3]));
+      m = group_max<16>(m);
+      sa[x] = (a.smoothing && m > 0.f) ? m : 1.f;
+      const float rs = 1.f / sa[x];
+#pragma unroll
+      for (int bb = 0; bb < CB; ++bb) M[x >> 2][bb][x & 3] *= rs;
+    }
   }
 
-  // ---- value-column scales and codes
+  // ---- value-column scales and codes. For CB >= 4 the column maxima are
+  // split across the wave's rows (row g: columns j0 + g CB/4 + m), each row
+  // divides for its own columns, and the reciprocals are gathered back.
   __syncthreads();  // the power method's last reads of sh_c are done
+  constexpr int NV = CB >= 4 ? CB / 4 : 1;
+  float cs[CB], inv[CB];
+  if constexpr (CB >= 4) {
+    float cm[CB], tot[NV];
 #pragma unroll
-  for (int bb = 0; bb < CB; ++bb) {
-    float m = 0.f;
+    for (int bb = 0; bb < CB; ++bb) {
+      float m = 0.f;
 #pragma unroll
-    for (int x = 0; x < RB; ++x) m = fmaxf(m, fabsf(M[x >> 2][bb][x & 3]));
-    m = rows_max(m);
-    if (lane < 16) sh_c[0][wave][j0 + bb] = m;
+      for (int x = 0; x < RB; ++x) m = fmaxf(m, fabsf(M[x >> 2][bb][x & 3]));
+      cm[bb] = m;
+    }
+    rows_max_split<CB>(cm, tot);
+    const int jg = j0 + (lane >> 4) * NV;
+#pragma unroll
+    for (int m = 0; m < NV; ++m) sh_c[0][wave][jg + m] = tot[m];
+    __syncthreads();
+    float iv[NV];
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const float mx = fmaxf(sh_c[0][0][jg + m], sh_c[0][1][jg + m]);
+      cs[m] = mx / float(Q);
+      iv[m] = mx > 0.f ? float(Q) / mx : 0.f;
+    }
+    rows_gather<NV>(iv, inv);
+  } else {
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) {
+      float m = 0.f;
+#pragma unroll
+      for (int x = 0; x < RB; ++x) m = fmaxf(m, fabsf(M[x >> 2][bb][x & 3]));
+      m = rows_max(m);
+      if (lane < 16) sh_c[0][wave][j0 + bb] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) {
+      const float m = fmaxf(sh_c[0][0][j0 + bb], sh_c[0][1][j0 + bb]);
+      cs[bb] = m / float(Q);
+      inv[bb] = m > 0.f ? float(Q) / m : 0.f;
+    }
   }
-  __syncthreads();
   uint8_t* cb = static_cast<uint8_t*>(a.codes) + size_t(bh) * HB;
-  float cs[CB];
 #pragma unroll
   for (int bb = 0; bb < CB; ++bb) {
     const int j = j0 + bb;
-    const float m = fmaxf(sh_c[0][0][j], sh_c[0][1][j]);
-    cs[bb] = m / float(Q);
-    const float inv = m > 0.f ? float(Q) / m : 0.f;
     int code[RB];
 #pragma unroll
     for (int x = 0; x < RB; ++x) {
-      const float qv = fminf(fmaxf(rintf(M[x >> 2][bb][x & 3] * inv), -float(Q)), float(Q));
+      const float qv = fminf(fmaxf(rintf(M[x >> 2][bb][x & 3] * inv[bb]), -float(Q)), float(Q));
       code[x] = int(qv);
     }
     if constexpr (BITS == 6) {
@@ -505,8 +613,19 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       store_codes<RB, BITS>(cb + size_t(j) * (D * BITS / 8) + i0 * BITS / 8, code);
     }
   }
-  if (tj == 0) storeB<RB>(a.s + hD + i0, sa);
-  if (ti == 0) storeB<CB>(a.c + hD + j0, cs);
+  if constexpr (RB == 16) {
+    a.s[hD + i0 + tj] = sa[0];
+  } else {
+    if (tj == 0) storeB<RB>(a.s + hD + i0, sa);
+  }
+  if constexpr (CB >= 4) {
+    if (wave == 0) {
+#pragma unroll
+      for (int m = 0; m < NV; ++m) a.c[hD + j0 + (lane >> 4) * NV + m] = cs[m];
+    }
+  } else {
+    if (ti == 0) storeB<CB>(a.c + hD + j0, cs);
+  }
   if (t == 0) a.blen[bh] = 0;
 }
 
