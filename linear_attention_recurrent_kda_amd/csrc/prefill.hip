@@ -30,6 +30,7 @@
 //   while the current one computes.
 #include "lq_common.h"
 #include "lq_launch.h"
+#include "lq_rows.h"
 
 namespace lq {
 
@@ -126,7 +127,7 @@ template <int D, bool KDA, bool BF16>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) prefill_blocks_kernel(PrefillArgs a) {
   constexpr int RB = D / 8, CB = D / 16;  // key rows and value columns per thread
   __shared__ float sh_kq[2][2];           // per-wave partial k . q (double-buffered)
-  __shared__ float sh_p[2][2][2][D];      // per-wave column partials of S'^T k and S'^T q
+  __shared__ __align__(16) float sh_p[2][2][2][D];  // per-wave column partials of S'^T k and S'^T q
 
   const int t = threadIdx.x, tj = t & 15, ti = t >> 4, lane = t & 63, wave = t >> 6;
   const int bh = blockIdx.x;
@@ -150,31 +151,38 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
     float kx[RB], qx[RB];
 #pragma unroll
     for (int x = 0; x < RB; ++x) kx[x] = raw_at(cur.k, x), qx[x] = raw_at(cur.q, x);
-    // decay, then the column partials of S'^T k and S'^T q over this thread's rows
-    float pk[CB], pq[CB], kq = 0.f;
+    // decay, then the column partials of S'^T k (pkq[c]) and S'^T q
+    // (pkq[CB + c]) over this thread's rows
+    float pkq[2 * CB], kq = 0.f;
 #pragma unroll
     for (int x = 0; x < RB; ++x) kq = fmaf(kx[x], qx[x], kq);
 #pragma unroll
-    for (int c = 0; c < CB; ++c) pk[c] = pq[c] = 0.f;
+    for (int c = 0; c < 2 * CB; ++c) pkq[c] = 0.f;
 #pragma unroll
     for (int x = 0; x < RB; ++x) {
       const float al = exp_fast(KDA ? cur.g[x] : cur.g[0]);
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
         M[x][c] *= al;
-        pk[c] = fmaf(M[x][c], kx[x], pk[c]);
-        pq[c] = fmaf(M[x][c], qx[x], pq[c]);
+        pkq[c] = fmaf(M[x][c], kx[x], pkq[c]);
+        pkq[CB + c] = fmaf(M[x][c], qx[x], pkq[CB + c]);
       }
     }
-    // sums over key rows: the wave's four row groups, then the two waves
-#pragma unroll
-    for (int c = 0; c < CB; ++c) pk[c] = rows_sum(pk[c]), pq[c] = rows_sum(pq[c]);
-    kq = rows_sum(kq);
-    if (lane < 16) {
-      st<CB>(&sh_p[par][wave][0][j0], pk);
-      st<CB>(&sh_p[par][wave][1][j0], pq);
-      if (lane == 0) sh_kq[par][wave] = kq;
+    // sums over key rows: the wave's four row groups with the work split
+    // (lane row g ends with 2CB/4 consecutive sums: of S'^T k for g < 2, of
+    // S'^T q for g >= 2), then the two waves through LDS
+    {
+      constexpr int NV = 2 * CB / 4;
+      float tot[NV];
+      rows_sum_split<2 * CB>(pkq, tot);
+      const int g = lane >> 4;
+      float* dst = &sh_p[par][wave][g >> 1][j0 + (g & 1) * NV];
+      if constexpr (NV == 4) *reinterpret_cast<float4*>(dst) = make_float4(tot[0], tot[1], tot[2], tot[3]);
+      else if constexpr (NV == 2) *reinterpret_cast<float2*>(dst) = make_float2(tot[0], tot[1]);
+      else *dst = tot[0];
     }
+    kq = rows_sum(kq);
+    if (lane == 0) sh_kq[par][wave] = kq;
     __syncthreads();
     const float kqs = sh_kq[par][0] + sh_kq[par][1];
     float u[CB], o[CB];
