@@ -146,6 +146,10 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   Tok<RB, CB, KDA, BF16> cur, nxt;
   if (a.n_tokens > 0) load_tok<D, KDA, BF16>(a, 0, bh, i0, j0, cur);
   int par = 0;
+  // GDN: the state is S = gam * M, one scale per head, so a token's decay is
+  // one multiply of gam instead of one per element; M is rescaled to S only
+  // when gam falls below 2^-32 (and at the end)
+  float gam = 1.f;
   for (int tt = 0; tt < a.n_tokens; ++tt) {
     if (tt + 1 < a.n_tokens) load_tok<D, KDA, BF16>(a, tt + 1, bh, i0, j0, nxt);
     float kx[RB], qx[RB];
@@ -158,12 +162,25 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
     for (int x = 0; x < RB; ++x) kq = fmaf(kx[x], qx[x], kq);
 #pragma unroll
     for (int c = 0; c < 2 * CB; ++c) pkq[c] = 0.f;
+    if constexpr (!KDA) {
+      gam *= exp_fast(cur.g[0]);
+      if (!(gam >= 0x1p-32f)) {  // the same for every thread of the head
+#pragma unroll
+        for (int x = 0; x < RB; ++x)
+#pragma unroll
+          for (int c = 0; c < CB; ++c) M[x][c] *= gam;
+        gam = 1.f;
+      }
+    }
 #pragma unroll
     for (int x = 0; x < RB; ++x) {
-      const float al = exp_fast(KDA ? cur.g[x] : cur.g[0]);
+      if constexpr (KDA) {
+        const float al = exp_fast(cur.g[x]);
+#pragma unroll
+        for (int c = 0; c < CB; ++c) M[x][c] *= al;
+      }
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        M[x][c] *= al;
         pkq[c] = fmaf(M[x][c], kx[x], pkq[c]);
         pkq[CB + c] = fmaf(M[x][c], qx[x], pkq[CB + c]);
       }
@@ -189,15 +206,20 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
       const int j = j0 + c;
-      const float yk = sh_p[par][0][0][j] + sh_p[par][1][0][j];
-      const float yq = sh_p[par][0][1][j] + sh_p[par][1][1][j];
+      const float yk = gam * (sh_p[par][0][0][j] + sh_p[par][1][0][j]);
+      const float yq = gam * (sh_p[par][0][1][j] + sh_p[par][1][1][j]);
       u[c] = cur.beta * (raw_at(cur.v, c) - yk);
       o[c] = fmaf(kqs, u[c], yq);
     }
+    // S += k u^T, i.e. M += k (u / gam)^T
+    float um[CB];
+    const float ig = KDA ? 1.f : __builtin_amdgcn_rcpf(gam);
+#pragma unroll
+    for (int c = 0; c < CB; ++c) um[c] = KDA ? u[c] : u[c] * ig;
 #pragma unroll
     for (int x = 0; x < RB; ++x)
 #pragma unroll
-      for (int c = 0; c < CB; ++c) M[x][c] = fmaf(kx[x], u[c], M[x][c]);
+      for (int c = 0; c < CB; ++c) M[x][c] = fmaf(kx[x], um[c], M[x][c]);
     if (ti == 0) st<CB>(a.o + (size_t(tt) * a.n_heads + bh) * D + j0, o);
     par ^= 1;
     cur = nxt;
@@ -207,7 +229,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   for (int c = 0; c < CB; ++c) {
     float col[RB];
 #pragma unroll
-    for (int x = 0; x < RB; ++x) col[x] = M[x][c];
+    for (int x = 0; x < RB; ++x) col[x] = KDA ? M[x][c] : M[x][c] * gam;
     st<RB>(a.S + (hD + j0 + c) * D + i0, col);
   }
 }
@@ -288,6 +310,8 @@ __global__ void __launch_bounds__(64) prefill_columns_kernel(PrefillArgs a) {
   };
   float beta_c = 0.f, g_c = 0.f, vj_c = 0.f, e0_c = 0.f, e1_c = 0.f;
   if (n_tok > 0) load_tok(0, beta_c, g_c, vj_c, e0_c, e1_c);
+  // GDN: S = gam * M (one scale per head), rescaled when gam falls below 2^-32
+  float gam = 1.f;
   for (int tt = 0; tt < n_tok; ++tt) {
     const size_t th = th_of(tt);
     const size_t row = th * D;
@@ -309,32 +333,39 @@ __global__ void __launch_bounds__(64) prefill_columns_kernel(PrefillArgs a) {
         s[i & 3] = fmaf(M[i], act_at<BF16>(a.k, row, i), s[i & 3]);
       }
     } else {
-      const float al = expf(g_c);
+      gam *= expf(g_c);
+      if (!(gam >= 0x1p-32f)) {  // the same for every lane
 #pragma unroll
-      for (int i = 0; i < D; ++i) {
-        M[i] *= al;
-        s[i & 3] = fmaf(M[i], act_at<BF16>(a.k, row, i), s[i & 3]);
+        for (int i = 0; i < D; ++i) M[i] *= gam;
+        gam = 1.f;
       }
+#pragma unroll
+      for (int i = 0; i < D; ++i) s[i & 3] = fmaf(M[i], act_at<BF16>(a.k, row, i), s[i & 3]);
     }
-    const float u = col ? beta_c * (vj_c - ((s[0] + s[1]) + (s[2] + s[3]))) : 0.f;
-    // pass 2: S = S' + k u^T, and o_j = sum_i S[i][j] q_i
+    const float yk = (s[0] + s[1]) + (s[2] + s[3]);
+    const float u = col ? beta_c * (vj_c - (KDA ? yk : gam * yk)) : 0.f;
+    // pass 2: S = S' + k u^T (GDN: M += k (u / gam)^T), and o_j = sum_i S[i][j] q_i
+    const float um = KDA ? u : u * __builtin_amdgcn_rcpf(gam);
     float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      M[i] = fmaf(act_at<BF16>(a.k, row, i), u, M[i]);
+      M[i] = fmaf(act_at<BF16>(a.k, row, i), um, M[i]);
       p[i & 3] = fmaf(M[i], act_at<BF16>(a.q, row, i), p[i & 3]);
     }
     // the next token's loads are complete here, before the output store: a
     // wait at the loop's end then never covers the store
     asm volatile("" ::"v"(touch), "v"(vj_n), "v"(e0_n), "v"(e1_n));
-    if (col) a.o[row + j] = (p[0] + p[1]) + (p[2] + p[3]);
+    const float oj = (p[0] + p[1]) + (p[2] + p[3]);
+    if (col) a.o[row + j] = KDA ? oj : gam * oj;
     beta_c = beta_n, g_c = g_n, vj_c = vj_n, e0_c = e0_n, e1_c = e1_n;
   }
 
   if (col) {
 #pragma unroll
     for (int w = 0; w < D / 4; ++w)
-      reinterpret_cast<float4*>(a.S + (hD + j) * D)[w] = make_float4(M[4 * w], M[4 * w + 1], M[4 * w + 2], M[4 * w + 3]);
+      reinterpret_cast<float4*>(a.S + (hD + j) * D)[w] =
+          KDA ? make_float4(M[4 * w], M[4 * w + 1], M[4 * w + 2], M[4 * w + 3])
+              : make_float4(gam * M[4 * w], gam * M[4 * w + 1], gam * M[4 * w + 2], gam * M[4 * w + 3]);
   }
 }
 

@@ -54,6 +54,40 @@ def test_prefill_matches_exact_recurrence(name, kw):
     assert worst <= 1e-5 and s_err <= 1e-5
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_gdn", dict(batch=2, heads=2, d_k=128, d_v=128)),  # fp32 activations: one thread per column
+    ("qwen_gdn", dict(batch=2)),                              # bf16 activations: 16 x 8 blocks
+    ("tiny_gdn", dict(batch=2, heads=3, act_bf16=True)),      # bf16, d = 32
+])
+def test_prefill_strong_decay(name, kw):
+    """GDN decays 40x the workload's (the state shrinks by 2^-32 within a few
+    dozen tokens) plus one token with g = -200, whose decay underflows fp32 to
+    zero: the kernels keep the scalar decay as one scale per head and fold it
+    into the state whenever it falls below 2^-32, which these prompts cross
+    several times. Same bound as above against the exact recurrence."""
+    wl = W[name].replace(**kw)
+    L = 48
+    dims = runner.dims_for(wl)
+    S0 = wk.initial_states(wl, range(wl.batch))
+    S = runner.states_to_device(S0)
+    raw, _ = _prompt(wl, L)
+    raw["g"] = (raw["g"] * 40.0).astype(np.float32)
+    raw["g"][20] = -200.0
+    toks = gh.flat_steps(raw)
+    dev = runner.upload_tokens(raw, wl.act_bf16)
+    N, d = wl.batch * wl.heads, wl.d_k
+    o = torch.empty((L, N, d), dtype=torch.float32, device="cuda")
+    lqk.prefill(dims, S, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], o)
+    torch.cuda.synchronize()
+    S_ref, outs = lq.prefill(S0.reshape(N, d, d).astype(np.float64), toks)
+    o_gpu = o.cpu().numpy()
+    worst = max(gh.rel_l2(o_gpu[t], outs[t]) for t in range(L))
+    s_err = gh.rel_l2(gh.T(S.cpu().numpy()), S_ref)
+    print(name, kw, "strong decay: prefill max rel L2 o", worst, "state", s_err)
+    assert np.isfinite(o_gpu).all()
+    assert worst <= 1e-5 and s_err <= 1e-5
+
+
 @pytest.mark.parametrize("name,kw,bits", [("qwen_gdn", dict(batch=4), 8), ("kda_int4", dict(batch=2), 4),
                                           ("tiny_gdn", dict(batch=2, heads=3), 6)])
 def test_handoff_encode_and_decode_on(name, kw, bits):
