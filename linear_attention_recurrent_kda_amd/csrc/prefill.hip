@@ -9,25 +9,25 @@
 // Per token, decay first (Gated DeltaNet scalar gate; Kimi Delta Attention
 // per-channel gate):
 //   S' = alpha (.)_rows S,  u = beta (v - S'^T k),  S = S' + k u^T,  o = S^T q
-// (o = S'^T q + (k . q) u). Two kernels, one per activation type, both
-// keeping the state in registers for the whole chunk (read and written once):
+// (o = S'^T q + (k . q) u). Two kernels, both keeping the state in registers
+// for the whole chunk (read and written once):
 //
-// - fp32 activations, prefill_columns_kernel: every value column j evolves on
-//   its own (u_j needs column j of S' and k; o_j column j of S and q), so one
-//   thread owns one column, all d_k key rows, and a token costs it two passes
-//   over its column with no exchange between threads: no LDS, no barrier, no
-//   cross-lane reduction. k, q, beta and the GDN gate are the same for every
-//   thread of a head and arrive through scalar loads as instruction operands;
-//   the KDA per-channel gates are exponentiated two channels per lane and
-//   broadcast with readlane. One wave covers 64 columns of a head.
-// - bf16 activations, prefill_blocks_kernel: through scalar loads a bf16 pair
-//   costs a scalar-unit split per value, which measured slower than sharing
-//   the sums: 128 threads per head on an 8 x 16 grid, each with a block of
-//   D/8 key rows by D/16 value columns; the column partials of S'^T k and
+// - prefill_blocks_kernel (GDN at either activation type, and KDA with bf16
+//   activations): 128 threads per head on an 8 x 16 grid, each with a block
+//   of D/8 key rows by D/16 value columns; the column partials of S'^T k and
 //   S'^T q and the partial k . q are summed over the wave's rows with the
-//   row-swap instructions and over the two waves through LDS, one barrier per
-//   token, double-buffered; the next token's inputs load (as raw bf16 pairs)
-//   while the current one computes.
+//   row-swap instructions (the work split across the rows) and over the two
+//   waves through LDS, one barrier per token, double-buffered; the next
+//   token's inputs load (as raw bf16 pairs or fp32 words) while the current
+//   one computes. GDN keeps the scalar decay as one scale per head.
+// - prefill_columns_kernel (KDA with fp32 activations): every value column j
+//   evolves on its own (u_j needs column j of S' and k; o_j column j of S and
+//   q), so one thread owns one column, all d_k key rows, and a token costs it
+//   two passes over its column with no exchange between threads. k, q and
+//   beta are the same for every thread of a head and arrive through scalar
+//   loads as instruction operands; the per-channel gates are exponentiated
+//   two channels per lane and broadcast with readlane. One wave covers 64
+//   columns of a head. (The blocks kernel spills at this instantiation.)
 #include "lq_common.h"
 #include "lq_launch.h"
 #include "lq_rows.h"
@@ -268,6 +268,7 @@ __device__ __forceinline__ float act_lane(const void* p, size_t idx) {
 
 template <int D, bool KDA, bool BF16>
 __global__ void __launch_bounds__(64) prefill_columns_kernel(PrefillArgs a) {
+  static_assert(KDA, "per-channel decay only: GDN runs the blocks kernel");
   constexpr int WPH = D > 64 ? D / 64 : 1;  // waves per head
   const int lane = threadIdx.x;
   const int bh = blockIdx.x / WPH;
@@ -288,90 +289,68 @@ __global__ void __launch_bounds__(64) prefill_columns_kernel(PrefillArgs a) {
   }
 
   // Inputs of token tt + 1 are loaded while token tt computes: the per-lane v
-  // and gate values into registers, the uniform beta (and GDN gate) into
-  // scalar registers, and one touch per line of its k and q rows, which warms
-  // the cache for that token's scalar loads.
+  // and gate values into registers, the uniform beta into a scalar register,
+  // and one touch per line of its k and q rows, which warms the cache for that
+  // token's scalar loads.
   const int n_tok = a.n_tokens;
   auto th_of = [&](int tt) { return size_t(tt) * a.n_heads + bh; };  // [token][head]
   const int pfi = min(2 * lane, D - 2);  // element of a k / q row this lane touches
   const int jc = min(j, D - 1);          // in-bounds column for the idle lanes' loads
-  const int gc = min(lane, D - 1);       // KDA: this lane's first gate channel
+  const int gc = min(lane, D - 1);       // this lane's first gate channel
   // loads without branches (clamped indices), so that no join forces an early wait
-  auto load_tok = [&](int tt, float& beta, float& g, float& vj, float& e0, float& e1) {
+  auto load_tok = [&](int tt, float& beta, float& vj, float& e0, float& e1) {
     const size_t th = th_of(tt), row = th * D;
     beta = as_const<float>(a.beta)[th];
     vj = act_lane<BF16>(a.v, row + jc);
-    if constexpr (KDA) {
-      e0 = a.g[row + gc];
-      e1 = D > 64 ? a.g[row + 64 + lane] : 0.f;
-    } else {
-      g = as_const<float>(a.g)[th];
-    }
+    e0 = a.g[row + gc];
+    e1 = D > 64 ? a.g[row + 64 + lane] : 0.f;
   };
-  float beta_c = 0.f, g_c = 0.f, vj_c = 0.f, e0_c = 0.f, e1_c = 0.f;
-  if (n_tok > 0) load_tok(0, beta_c, g_c, vj_c, e0_c, e1_c);
-  // GDN: S = gam * M (one scale per head), rescaled when gam falls below 2^-32
-  float gam = 1.f;
+  float beta_c = 0.f, vj_c = 0.f, e0_c = 0.f, e1_c = 0.f;
+  if (n_tok > 0) load_tok(0, beta_c, vj_c, e0_c, e1_c);
   for (int tt = 0; tt < n_tok; ++tt) {
     const size_t th = th_of(tt);
     const size_t row = th * D;
     const int tn = min(tt + 1, n_tok - 1);  // the last token reloads itself
-    float beta_n = 0.f, g_n = 0.f, vj_n = 0.f, e0_n = 0.f, e1_n = 0.f;
-    load_tok(tn, beta_n, g_n, vj_n, e0_n, e1_n);
+    float beta_n = 0.f, vj_n = 0.f, e0_n = 0.f, e1_n = 0.f;
+    load_tok(tn, beta_n, vj_n, e0_n, e1_n);
     const size_t rown = th_of(tn) * D;
     const float touch = act_lane<BF16>(a.k, rown + pfi) + act_lane<BF16>(a.q, rown + pfi);
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the token's arithmetic
-    // pass 1: decay, and u_j = beta (v_j - sum_i S'[i][j] k_i)
+    // pass 1: decay, and u_j = beta (v_j - sum_i S'[i][j] k_i); alpha_i =
+    // exp(g_i), lane l holding channels l and l + 64
     float s[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (KDA) {
-      // alpha_i = exp(g_i): lane l holds channels l and l + 64
-      const float a0 = expf(e0_c), a1 = expf(e1_c);
+    const float a0 = expf(e0_c), a1 = expf(e1_c);
 #pragma unroll
-      for (int i = 0; i < D; ++i) {
-        const float al = as_f(__builtin_amdgcn_readlane(as_u(i < 64 ? a0 : a1), i & 63));
-        M[i] *= al;
-        s[i & 3] = fmaf(M[i], act_at<BF16>(a.k, row, i), s[i & 3]);
-      }
-    } else {
-      gam *= expf(g_c);
-      if (!(gam >= 0x1p-32f)) {  // the same for every lane
-#pragma unroll
-        for (int i = 0; i < D; ++i) M[i] *= gam;
-        gam = 1.f;
-      }
-#pragma unroll
-      for (int i = 0; i < D; ++i) s[i & 3] = fmaf(M[i], act_at<BF16>(a.k, row, i), s[i & 3]);
+    for (int i = 0; i < D; ++i) {
+      const float al = as_f(__builtin_amdgcn_readlane(as_u(i < 64 ? a0 : a1), i & 63));
+      M[i] *= al;
+      s[i & 3] = fmaf(M[i], act_at<BF16>(a.k, row, i), s[i & 3]);
     }
-    const float yk = (s[0] + s[1]) + (s[2] + s[3]);
-    const float u = col ? beta_c * (vj_c - (KDA ? yk : gam * yk)) : 0.f;
-    // pass 2: S = S' + k u^T (GDN: M += k (u / gam)^T), and o_j = sum_i S[i][j] q_i
-    const float um = KDA ? u : u * __builtin_amdgcn_rcpf(gam);
+    const float u = col ? beta_c * (vj_c - ((s[0] + s[1]) + (s[2] + s[3]))) : 0.f;
+    // pass 2: S = S' + k u^T, and o_j = sum_i S[i][j] q_i
     float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      M[i] = fmaf(act_at<BF16>(a.k, row, i), um, M[i]);
+      M[i] = fmaf(act_at<BF16>(a.k, row, i), u, M[i]);
       p[i & 3] = fmaf(M[i], act_at<BF16>(a.q, row, i), p[i & 3]);
     }
     // the next token's loads are complete here, before the output store: a
     // wait at the loop's end then never covers the store
     asm volatile("" ::"v"(touch), "v"(vj_n), "v"(e0_n), "v"(e1_n));
-    const float oj = (p[0] + p[1]) + (p[2] + p[3]);
-    if (col) a.o[row + j] = KDA ? oj : gam * oj;
-    beta_c = beta_n, g_c = g_n, vj_c = vj_n, e0_c = e0_n, e1_c = e1_n;
+    if (col) a.o[row + j] = (p[0] + p[1]) + (p[2] + p[3]);
+    beta_c = beta_n, vj_c = vj_n, e0_c = e0_n, e1_c = e1_n;
   }
 
   if (col) {
 #pragma unroll
     for (int w = 0; w < D / 4; ++w)
-      reinterpret_cast<float4*>(a.S + (hD + j) * D)[w] =
-          KDA ? make_float4(M[4 * w], M[4 * w + 1], M[4 * w + 2], M[4 * w + 3])
-              : make_float4(gam * M[4 * w], gam * M[4 * w + 1], gam * M[4 * w + 2], gam * M[4 * w + 3]);
+      reinterpret_cast<float4*>(a.S + (hD + j) * D)[w] = make_float4(M[4 * w], M[4 * w + 1], M[4 * w + 2], M[4 * w + 3]);
   }
 }
 
 template <int D, bool KDA, bool BF16>
 hipError_t launch(const lq_dims& d, const PrefillArgs& a, hipStream_t stream) {
-  if constexpr (BF16) {
+  if constexpr (BF16 || !KDA) {
     hipLaunchKernelGGL((prefill_blocks_kernel<D, KDA, BF16>), dim3(d.batch * d.heads), dim3(128), 0, stream, a);
   } else {
     constexpr int WPH = D > 64 ? D / 64 : 1;
