@@ -14,10 +14,13 @@
 // RB = D/8 and CB = D/16 (16 x 8 at D = 128). A 16-lane DPP row holds one
 // block row (all tj), so sums over value columns are DPP reductions; sums over
 // key rows combine the four rows of a wave with the gfx950 row-swap
-// instructions and the two waves through LDS. Tall blocks keep the reduction
-// work per power iteration low (16 DPP sums and 8 row sums per 256 FMA), and
-// at D = 128 a thread owns whole 16-channel code groups. Reductions run in a
-// fixed order, so the result is deterministic.
+// instructions, the work split so that each row keeps a quarter of the
+// columns, and the two waves through LDS. Tall blocks keep the reduction work
+// per power iteration low (16 DPP sums and 6 row swaps per 256 FMA), and at
+// D = 128 a thread owns whole 16-channel code groups. The fold of the buffered
+// entries is an fp32 matrix-core update whose output tiles land on these same
+// register blocks. Reductions run in a fixed order, so the result is
+// deterministic.
 #include "lq_common.h"
 #include "lq_launch.h"
 #include "lq_rows.h"
