@@ -234,6 +234,269 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   }
 }
 
+// ---- GDN at d = 128: chunks of 16 tokens on the matrix cores
+//
+// Within a chunk of C tokens with start state S0 and cumulative log-decay
+// G_t (through token t, inclusive), the recurrence unrolls to
+//   (alpha_t S_{t-1})^T k_t = e^{G_t} S0^T k_t + sum_{s<t} e^{G_t-G_s} (k_s.k_t) u_s
+//   o_t = e^{G_t} S0^T q_t + sum_{s<=t} e^{G_t-G_s} (k_s.q_t) u_s
+//   S_C = e^{G_C} S0 + sum_s e^{G_C-G_s} k_s u_s^T
+// so the u_t solve a unit lower-triangular C x C system per value column,
+//   u_t + beta_t sum_{s<t} A_ts u_s = beta_t (v_t - e^{G_t} S0^T k_t),
+// A_ts = e^{G_t-G_s} k_t.k_s. The products K S0, Q S0, K K^T, Q K^T and the
+// rank-C state update are fp32 MFMA contractions (v_mfma_f32_16x16x4f32); the
+// triangular solves and the outputs run on the vector ALU, one thread per
+// value column. It is the same recurrence, reassociated: results agree with
+// the token-by-token form to fp32 rounding.
+//
+// 128 threads, two waves; wave w holds value columns [64w, 64w + 64) of all
+// 128 key rows, in the MFMA accumulator layout: lane (g = lane / 16,
+// c = lane % 16) holds S[16 TR + 4 g + r][64 w + 16 TC + c] in M[TR][TC][r].
+// As the B operand of K S0 those registers need no movement: MFMA (TR, r)
+// contracts over key rows 16 TR + 4 g + r (g = the lane group), and its A
+// operand reads K at the same rows.
+// x of the lane N below inside the 16-lane row, 0 for the row's first N lanes
+template <int N>
+__device__ __forceinline__ float dpp_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) prefill_chunk_kernel(PrefillArgs a) {
+  constexpr int D = 128, C = 16, KS = D + 4;  // KS: padded LDS row (bank spread)
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) float sh_k[C][KS];
+  __shared__ __align__(16) float sh_qu[C][KS];  // q of the chunk, then its u
+  __shared__ __align__(16) float sh_r[2][C][64];  // per wave: v, then beta (v - e^G S0^T k), token-major
+  __shared__ __align__(16) float sh_p[2][C][64];  // per wave: e^G S0^T q
+  __shared__ float sh_a[C][C];                   // beta_t A_ts, s < t
+  __shared__ float sh_b[C][C];                   // e^{G_t-G_s} k_s.q_t, s <= t
+  __shared__ float sh_G[C], sh_beta[C];
+
+  // Lane-derived indices are re-derived in every phase from an opaque copy of
+  // the thread index, so that the compiler forms each phase's addresses there
+  // instead of keeping dozens of them live across the chunk loop.
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  auto lane_id = [] {
+    int x = int(threadIdx.x) & 63;
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  int lane = lane_id(), g = lane >> 4, c = lane & 15;
+  const int bh = blockIdx.x;
+  const size_t hD = size_t(bh) * D;
+  const int NH = a.n_heads, n_tok = a.n_tokens;
+
+  v4f M[8][4];
+#pragma unroll
+  for (int TC = 0; TC < 4; ++TC) {
+    const float* col = a.S + (hD + 64 * w + 16 * TC + c) * D + 4 * g;  // + 16 TR: immediate offsets
+#pragma unroll
+    for (int TR = 0; TR < 8; ++TR) {
+      const float4 x = *reinterpret_cast<const float4*>(col + 16 * TR);
+      M[TR][TC] = v4f{x.x, x.y, x.z, x.w};
+    }
+  }
+
+  for (int c0 = 0; c0 < n_tok; c0 += C) {
+    const int nc = min(C, n_tok - c0);
+    __syncthreads();  // the previous chunk's reads of sh_k / sh_qu are done
+    // ---- stage k and q (fp32, rows past the prompt zero), G and beta
+    {
+      lane = lane_id(), g = lane >> 4, c = lane & 15;
+      const int t = 64 * w + lane;
+      const int tr = t >> 3, ch = (t & 7) * 16;
+      const bool in = tr < nc;
+      const size_t row = (size_t(c0 + (in ? tr : 0)) * NH + bh) * D + ch;
+      float kv[16], qv[16];
+      if constexpr (BF16) {
+        const uint4* pk = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row);
+        const uint4* pq = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + row);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint4 xk = pk[h], xq = pq[h];
+          const uint32_t wk[4] = {xk.x, xk.y, xk.z, xk.w}, wq[4] = {xq.x, xq.y, xq.z, xq.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv[8 * h + 2 * e] = bf16_lo(wk[e]), kv[8 * h + 2 * e + 1] = bf16_hi(wk[e]);
+            qv[8 * h + 2 * e] = bf16_lo(wq[e]), qv[8 * h + 2 * e + 1] = bf16_hi(wq[e]);
+          }
+        }
+      } else {
+        const float4* pk = reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + row);
+        const float4* pq = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + row);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float4 xk = pk[h], xq = pq[h];
+          kv[4 * h] = xk.x, kv[4 * h + 1] = xk.y, kv[4 * h + 2] = xk.z, kv[4 * h + 3] = xk.w;
+          qv[4 * h] = xq.x, qv[4 * h + 1] = xq.y, qv[4 * h + 2] = xq.z, qv[4 * h + 3] = xq.w;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        *reinterpret_cast<float4*>(&sh_k[tr][ch + 4 * h]) =
+            in ? make_float4(kv[4 * h], kv[4 * h + 1], kv[4 * h + 2], kv[4 * h + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(&sh_qu[tr][ch + 4 * h]) =
+            in ? make_float4(qv[4 * h], qv[4 * h + 1], qv[4 * h + 2], qv[4 * h + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      // v goes where the right-hand side will be built: sh_r[wave of the column]
+      float vr[16];
+      if constexpr (BF16) {
+        const uint4* pv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + row);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint4 xv = pv[h];
+          const uint32_t wv[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vr[8 * h + 2 * e] = bf16_lo(wv[e]), vr[8 * h + 2 * e + 1] = bf16_hi(wv[e]);
+        }
+      } else {
+        const float4* pv = reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + row);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float4 xv = pv[h];
+          vr[4 * h] = xv.x, vr[4 * h + 1] = xv.y, vr[4 * h + 2] = xv.z, vr[4 * h + 3] = xv.w;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        *reinterpret_cast<float4*>(&sh_r[ch >> 6][tr][(ch & 63) + 4 * h]) =
+            in ? make_float4(vr[4 * h], vr[4 * h + 1], vr[4 * h + 2], vr[4 * h + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (w == 0) {  // G_t = sum of g_s over s <= t: an inclusive scan over lanes 0-15
+        const bool tin = lane < nc;  // (nc <= 16)
+        const size_t th = size_t(c0 + (tin ? lane : 0)) * NH + bh;
+        float G = tin ? a.g[th] : 0.f;
+        const float bt = tin ? a.beta[th] : 0.f;
+        G += dpp_shr<1>(G);
+        G += dpp_shr<2>(G);
+        G += dpp_shr<4>(G);
+        G += dpp_shr<8>(G);
+        if (lane < C) sh_G[lane] = G, sh_beta[lane] = bt;
+      }
+    }
+    __syncthreads();
+
+    // ---- K S0, then Q S0, for this wave's columns (token 4g + r, column
+    // 64w + 16TC + c), each turned into its LDS form before the next
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      lane = lane_id(), g = lane >> 4, c = lane & 15;
+      float(*src)[KS] = pass == 0 ? sh_k : sh_qu;
+      v4f P[4];
+#pragma unroll
+      for (int TC = 0; TC < 4; ++TC) P[TC] = v4f{0.f, 0.f, 0.f, 0.f};
+      // operands one row block ahead of the products that use them (a fence
+      // per block keeps the loads from piling up further ahead)
+      float ak[4], an[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ak[r] = src[c][4 * g + r];
+#pragma unroll
+      for (int TR = 0; TR < 8; ++TR) {
+        if (TR < 7) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) an[r] = src[c][16 * (TR + 1) + 4 * g + r];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int TC = 0; TC < 4; ++TC) P[TC] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], M[TR][TC][r], P[TC], 0, 0, 0);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ak[r] = an[r];
+      }
+      // right-hand sides beta (v - e^G S0^T k), or the e^G S0^T q terms
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tk = 4 * g + r;
+        const float eG = exp_fast(sh_G[tk]), bt = sh_beta[tk];
+#pragma unroll
+        for (int TC = 0; TC < 4; ++TC) {
+          if (pass == 0) sh_r[w][tk][16 * TC + c] = bt * (sh_r[w][tk][16 * TC + c] - eG * P[TC][r]);
+          else sh_p[w][tk][16 * TC + c] = eG * P[TC][r];
+        }
+      }
+    }
+    // ---- K K^T (wave 0) or Q K^T (wave 1): entry (t = 4g + r, s = c)
+    {
+      lane = lane_id(), g = lane >> 4, c = lane & 15;
+      v4f X = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int kb = 0; kb < D / 4; ++kb) {
+        const float b = sh_k[c][4 * kb + g];
+        const float av = w == 0 ? b : sh_qu[c][4 * kb + g];
+        X = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b, X, 0, 0, 0);
+      }
+      const float Gs = sh_G[c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tk = 4 * g + r;
+        const float f = exp_fast(sh_G[tk] - Gs);
+        if (w == 0) sh_a[tk][c] = c < tk ? sh_beta[tk] * f * X[r] : 0.f;
+        else sh_b[tk][c] = c <= tk ? f * X[r] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // ---- per value column (lane): forward substitution for u, then o
+    {
+      lane = lane_id();
+      const int J = 64 * w + lane;
+      float u[C];
+      // token by token: u_t from the earlier u, then o_t (a fence per token
+      // keeps the uniform coefficient loads from all being hoisted ahead)
+#pragma unroll
+      for (int tk = 0; tk < C; ++tk) {
+        float x = sh_r[w][tk][lane];
+#pragma unroll
+        for (int s2 = 0; s2 < tk; ++s2) x = fmaf(-sh_a[tk][s2], u[s2], x);
+        u[tk] = x;
+        float o = sh_p[w][tk][lane];
+#pragma unroll
+        for (int s2 = 0; s2 <= tk; ++s2) o = fmaf(sh_b[tk][s2], u[s2], o);
+        if (tk < nc) a.o[(size_t(c0 + tk) * NH + bh) * D + J] = o;
+        asm volatile("" ::: "memory");
+      }
+      __syncthreads();  // every wave has read q (in sh_qu) before u overwrites it
+#pragma unroll
+      for (int tk = 0; tk < C; ++tk) sh_qu[tk][J] = u[tk];
+    }
+    __syncthreads();
+
+    // ---- S = e^{G_C} S0 + sum_s e^{G_C - G_s} k_s u_s^T
+    {
+      lane = lane_id(), g = lane >> 4, c = lane & 15;
+      const float GC = sh_G[C - 1], eC = exp_fast(GC);
+#pragma unroll
+      for (int TR = 0; TR < 8; ++TR)
+#pragma unroll
+        for (int TC = 0; TC < 4; ++TC) M[TR][TC] *= eC;
+#pragma unroll
+      for (int kb = 0; kb < C / 4; ++kb) {
+        const int s2 = 4 * kb + g;
+        const float f = exp_fast(GC - sh_G[s2]);
+        float ub[4];
+#pragma unroll
+        for (int TC = 0; TC < 4; ++TC) ub[TC] = sh_qu[s2][64 * w + 16 * TC + c];
+#pragma unroll
+        for (int TR = 0; TR < 8; ++TR) {
+          const float ak = f * sh_k[s2][16 * TR + c];
+#pragma unroll
+          for (int TC = 0; TC < 4; ++TC) M[TR][TC] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, ub[TC], M[TR][TC], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const int lane_o = lane_id();
+#pragma unroll
+  for (int TC = 0; TC < 4; ++TC) {
+    float* col = a.S + (hD + 64 * w + 16 * TC + (lane_o & 15)) * D + 4 * (lane_o >> 4);
+#pragma unroll
+    for (int TR = 0; TR < 8; ++TR)
+      *reinterpret_cast<float4*>(col + 16 * TR) = make_float4(M[TR][TC][0], M[TR][TC][1], M[TR][TC][2], M[TR][TC][3]);
+  }
+}
+
 // ---- fp32 activations: one thread per value column
 
 // Read-only inputs seen through the constant address space: a load at a
@@ -350,7 +613,9 @@ __global__ void __launch_bounds__(64) prefill_columns_kernel(PrefillArgs a) {
 
 template <int D, bool KDA, bool BF16>
 hipError_t launch(const lq_dims& d, const PrefillArgs& a, hipStream_t stream) {
-  if constexpr (BF16 || !KDA) {
+  if constexpr (D == 128 && !KDA) {
+    hipLaunchKernelGGL((prefill_chunk_kernel<BF16>), dim3(d.batch * d.heads), dim3(128), 0, stream, a);
+  } else if constexpr (BF16 || !KDA) {
     hipLaunchKernelGGL((prefill_blocks_kernel<D, KDA, BF16>), dim3(d.batch * d.heads), dim3(128), 0, stream, a);
   } else {
     constexpr int WPH = D > 64 ? D / 64 : 1;
