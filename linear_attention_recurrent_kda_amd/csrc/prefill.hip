@@ -298,75 +298,78 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
     }
   }
 
+  // A chunk's inputs as loaded (thread t: token row t / 8 of the chunk, 16
+  // channels from (t % 8) * 16, of k, q and v; wave 0 lane l < 16: token l's
+  // g and beta). The next chunk's loads are issued once the current one is
+  // staged, so they are in flight during its arithmetic.
+  constexpr int NWD = BF16 ? 8 : 16;  // 32-bit words per 16 values
+  struct Raw {
+    uint32_t k[NWD], q[NWD], v[NWD];
+    float g, beta;
+  };
+  auto fetch = [&](int cc, Raw& x) {
+    const int l = lane_id(), tt = 64 * w + l;
+    const int tok = min(cc + (tt >> 3), n_tok - 1);  // clamped: rows past the prompt are zeroed when staged
+    const size_t off = ((size_t(tok) * NH + bh) * D + (tt & 7) * 16) * (BF16 ? 2 : 4);
+    if constexpr (BF16) {  // 8-byte pieces: the alignment the C ABI requires of bf16 activations
+#pragma unroll
+      for (int h = 0; h < NWD / 2; ++h) {
+        const uint2 xk = *reinterpret_cast<const uint2*>(static_cast<const char*>(a.k) + off + 8 * h);
+        const uint2 xq = *reinterpret_cast<const uint2*>(static_cast<const char*>(a.q) + off + 8 * h);
+        const uint2 xv = *reinterpret_cast<const uint2*>(static_cast<const char*>(a.v) + off + 8 * h);
+        x.k[2 * h] = xk.x, x.k[2 * h + 1] = xk.y;
+        x.q[2 * h] = xq.x, x.q[2 * h + 1] = xq.y;
+        x.v[2 * h] = xv.x, x.v[2 * h + 1] = xv.y;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < NWD / 4; ++h) {
+        const uint4 xk = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + off + 16 * h);
+        const uint4 xq = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + off + 16 * h);
+        const uint4 xv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) + off + 16 * h);
+        x.k[4 * h] = xk.x, x.k[4 * h + 1] = xk.y, x.k[4 * h + 2] = xk.z, x.k[4 * h + 3] = xk.w;
+        x.q[4 * h] = xq.x, x.q[4 * h + 1] = xq.y, x.q[4 * h + 2] = xq.z, x.q[4 * h + 3] = xq.w;
+        x.v[4 * h] = xv.x, x.v[4 * h + 1] = xv.y, x.v[4 * h + 2] = xv.z, x.v[4 * h + 3] = xv.w;
+      }
+    }
+    if (w == 0) {
+      const size_t th = size_t(min(cc + (l & 15), n_tok - 1)) * NH + bh;
+      x.g = a.g[th];
+      x.beta = a.beta[th];
+    }
+  };
+  auto val = [](const uint32_t(&wd)[NWD], int i) {  // element i of 16
+    if constexpr (BF16) return (i & 1) ? bf16_hi(wd[i >> 1]) : bf16_lo(wd[i >> 1]);
+    else return as_f(wd[i]);
+  };
+  Raw cur;
+  if (n_tok > 0) fetch(0, cur);
+
   for (int c0 = 0; c0 < n_tok; c0 += C) {
     const int nc = min(C, n_tok - c0);
-    __syncthreads();  // the previous chunk's reads of sh_k / sh_qu are done
-    // ---- stage k and q (fp32, rows past the prompt zero), G and beta
+    __syncthreads();  // the previous chunk's reads of sh_k, sh_qu and sh_r are done
+    // ---- stage k, q and v (fp32; rows past the prompt zero), G and beta
     {
-      lane = lane_id(), g = lane >> 4, c = lane & 15;
-      const int t = 64 * w + lane;
-      const int tr = t >> 3, ch = (t & 7) * 16;
+      lane = lane_id();
+      const int tt = 64 * w + lane, tr = tt >> 3, ch = (tt & 7) * 16;
       const bool in = tr < nc;
-      const size_t row = (size_t(c0 + (in ? tr : 0)) * NH + bh) * D + ch;
-      float kv[16], qv[16];
-      if constexpr (BF16) {
-        const uint4* pk = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row);
-        const uint4* pq = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + row);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint4 xk = pk[h], xq = pq[h];
-          const uint32_t wk[4] = {xk.x, xk.y, xk.z, xk.w}, wq[4] = {xq.x, xq.y, xq.z, xq.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kv[8 * h + 2 * e] = bf16_lo(wk[e]), kv[8 * h + 2 * e + 1] = bf16_hi(wk[e]);
-            qv[8 * h + 2 * e] = bf16_lo(wq[e]), qv[8 * h + 2 * e + 1] = bf16_hi(wq[e]);
-          }
-        }
-      } else {
-        const float4* pk = reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + row);
-        const float4* pq = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + row);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float4 xk = pk[h], xq = pq[h];
-          kv[4 * h] = xk.x, kv[4 * h + 1] = xk.y, kv[4 * h + 2] = xk.z, kv[4 * h + 3] = xk.w;
-          qv[4 * h] = xq.x, qv[4 * h + 1] = xq.y, qv[4 * h + 2] = xq.z, qv[4 * h + 3] = xq.w;
-        }
-      }
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        *reinterpret_cast<float4*>(&sh_k[tr][ch + 4 * h]) =
-            in ? make_float4(kv[4 * h], kv[4 * h + 1], kv[4 * h + 2], kv[4 * h + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(&sh_qu[tr][ch + 4 * h]) =
-            in ? make_float4(qv[4 * h], qv[4 * h + 1], qv[4 * h + 2], qv[4 * h + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      // v goes where the right-hand side will be built: sh_r[wave of the column]
-      float vr[16];
-      if constexpr (BF16) {
-        const uint4* pv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + row);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint4 xv = pv[h];
-          const uint32_t wv[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vr[8 * h + 2 * e] = bf16_lo(wv[e]), vr[8 * h + 2 * e + 1] = bf16_hi(wv[e]);
+        float4 xk = make_float4(0.f, 0.f, 0.f, 0.f), xq = xk, xv = xk;
+        if (in) {
+          xk = make_float4(val(cur.k, 4 * h), val(cur.k, 4 * h + 1), val(cur.k, 4 * h + 2), val(cur.k, 4 * h + 3));
+          xq = make_float4(val(cur.q, 4 * h), val(cur.q, 4 * h + 1), val(cur.q, 4 * h + 2), val(cur.q, 4 * h + 3));
+          xv = make_float4(val(cur.v, 4 * h), val(cur.v, 4 * h + 1), val(cur.v, 4 * h + 2), val(cur.v, 4 * h + 3));
         }
-      } else {
-        const float4* pv = reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + row);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float4 xv = pv[h];
-          vr[4 * h] = xv.x, vr[4 * h + 1] = xv.y, vr[4 * h + 2] = xv.z, vr[4 * h + 3] = xv.w;
-        }
+        *reinterpret_cast<float4*>(&sh_k[tr][ch + 4 * h]) = xk;
+        *reinterpret_cast<float4*>(&sh_qu[tr][ch + 4 * h]) = xq;
+        // v goes where the right-hand side will be built: sh_r[wave of the column]
+        *reinterpret_cast<float4*>(&sh_r[ch >> 6][tr][(ch & 63) + 4 * h]) = xv;
       }
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        *reinterpret_cast<float4*>(&sh_r[ch >> 6][tr][(ch & 63) + 4 * h]) =
-            in ? make_float4(vr[4 * h], vr[4 * h + 1], vr[4 * h + 2], vr[4 * h + 3]) : make_float4(0.f, 0.f, 0.f, 0.f);
       if (w == 0) {  // G_t = sum of g_s over s <= t: an inclusive scan over lanes 0-15
         const bool tin = lane < nc;  // (nc <= 16)
-        const size_t th = size_t(c0 + (tin ? lane : 0)) * NH + bh;
-        float G = tin ? a.g[th] : 0.f;
-        const float bt = tin ? a.beta[th] : 0.f;
+        float G = tin ? cur.g : 0.f;
+        const float bt = tin ? cur.beta : 0.f;
         G += dpp_shr<1>(G);
         G += dpp_shr<2>(G);
         G += dpp_shr<4>(G);
@@ -374,6 +377,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         if (lane < C) sh_G[lane] = G, sh_beta[lane] = bt;
       }
     }
+    if (c0 + C < n_tok) fetch(c0 + C, cur);
     __syncthreads();
 
     // ---- K S0, then Q S0, for this wave's columns (token 4g + r, column
@@ -456,7 +460,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         if (tk < nc) a.o[(size_t(c0 + tk) * NH + bh) * D + J] = o;
         asm volatile("" ::: "memory");
       }
-      __syncthreads();  // every wave has read q (in sh_qu) before u overwrites it
+      // (q in sh_qu was last read before the previous barrier)
 #pragma unroll
       for (int tk = 0; tk < C; ++tk) sh_qu[tk][J] = u[tk];
     }
