@@ -136,11 +136,22 @@ def test_handoff_encode_and_decode_on(name, kw, bits):
     assert worst <= 1e-5
 
 
-@pytest.mark.parametrize("L", [0, 1, 5])
-def test_prefill_short_and_empty_prompts(L):
+@pytest.mark.parametrize("name,kw,L", [
+    ("tiny_gdn", dict(batch=2, heads=2, kda=True), 0),
+    ("tiny_gdn", dict(batch=2, heads=2, kda=True), 1),
+    ("tiny_gdn", dict(batch=2, heads=2, kda=True), 5),
+    # GDN at d = 128 runs in chunks of 16 tokens: an empty prompt, a part of
+    # one chunk, and two chunks plus a ragged tail, at both activation types
+    ("qwen_gdn", dict(batch=2), 0),
+    ("qwen_gdn", dict(batch=2), 5),
+    ("qwen_gdn", dict(batch=2), 37),
+    ("tiny_gdn", dict(batch=2, heads=2, d_k=128, d_v=128), 37),
+])
+def test_prefill_short_and_empty_prompts(name, kw, L):
     """An empty prompt leaves the state as it is and the handoff is the plain
-    encode; one token and a few tokens match the exact recurrence."""
-    wl = W["tiny_gdn"].replace(batch=2, heads=2, kda=True)
+    encode; one token, a few tokens and ragged lengths match the exact
+    recurrence."""
+    wl = W[name].replace(**kw)
     dims = runner.dims_for(wl)
     N, d = wl.batch * wl.heads, wl.d_k
     S0 = wk.initial_states(wl, range(wl.batch))
