@@ -9,17 +9,20 @@
 // Per token, decay first (Gated DeltaNet scalar gate; Kimi Delta Attention
 // per-channel gate):
 //   S' = alpha (.)_rows S,  u = beta (v - S'^T k),  S = S' + k u^T,  o = S^T q
-// (o = S'^T q + (k . q) u). Two kernels, both keeping the state in registers
-// for the whole chunk (read and written once):
+// (o = S'^T q + (k . q) u). Three kernels, all keeping the state on chip for
+// the whole prompt (read and written once):
 //
-// - prefill_blocks_kernel (GDN at either activation type, and KDA with bf16
-//   activations): 128 threads per head on an 8 x 16 grid, each with a block
-//   of D/8 key rows by D/16 value columns; the column partials of S'^T k and
-//   S'^T q and the partial k . q are summed over the wave's rows with the
-//   row-swap instructions (the work split across the rows) and over the two
-//   waves through LDS, one barrier per token, double-buffered; the next
-//   token's inputs load (as raw bf16 pairs or fp32 words) while the current
-//   one computes. GDN keeps the scalar decay as one scale per head.
+// - prefill_chunk_kernel (GDN at d = 128): chunks of 16 tokens, whose
+//   products and state update run on the matrix cores (described at the
+//   kernel).
+// - prefill_blocks_kernel (GDN at d < 128, and KDA with bf16 activations):
+//   128 threads per head on an 8 x 16 grid, each with a block of D/8 key rows
+//   by D/16 value columns; the column partials of S'^T k and S'^T q and the
+//   partial k . q are summed over the wave's rows with the row-swap
+//   instructions (the work split across the rows) and over the two waves
+//   through LDS, one barrier per token, double-buffered; the next token's
+//   inputs load while the current one computes. GDN keeps the scalar decay as
+//   one scale per head.
 // - prefill_columns_kernel (KDA with fp32 activations): every value column j
 //   evolves on its own (u_j needs column j of S' and k; o_j column j of S and
 //   q), so one thread owns one column, all d_k key rows, and a token costs it
@@ -255,6 +258,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
 // As the B operand of K S0 those registers need no movement: MFMA (TR, r)
 // contracts over key rows 16 TR + 4 g + r (g = the lane group), and its A
 // operand reads K at the same rows.
+
 // x of the lane N below inside the 16-lane row, 0 for the row's first N lanes
 template <int N>
 __device__ __forceinline__ float dpp_shr(float x) {
