@@ -265,7 +265,7 @@ __device__ __forceinline__ float dpp_shr(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
 }
 
-template <bool BF16>
+template <bool BF16, bool KDA>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) prefill_chunk_kernel(PrefillArgs a) {
   constexpr int D = 128, C = 16, KS = D + 4;  // KS: padded LDS row (bank spread)
   typedef float v4f __attribute__((ext_vector_type(4)));
@@ -275,7 +275,8 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   __shared__ __align__(16) float sh_p[2][C][64];  // per wave: e^G S0^T q
   __shared__ float sh_a[C][C];                   // beta_t A_ts, s < t
   __shared__ float sh_b[C][C];                   // e^{G_t-G_s} k_s.q_t, s <= t
-  __shared__ float sh_G[C], sh_beta[C];
+  __shared__ float sh_G[C], sh_beta[C];          // GDN: G_t; beta_t
+  __shared__ __align__(16) float sh_g[KDA ? C : 1][KS];  // KDA: g, then G_t per key channel
 
   // Lane-derived indices are re-derived in every phase from an opaque copy of
   // the thread index, so that the compiler forms each phase's addresses there
@@ -310,6 +311,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   struct Raw {
     uint32_t k[NWD], q[NWD], v[NWD];
     float g, beta;
+    float gv[KDA ? 16 : 1];  // KDA: the gates of the same 16 channels
   };
   auto fetch = [&](int cc, Raw& x) {
     const int l = lane_id(), tt = 64 * w + l;
@@ -336,9 +338,17 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         x.v[4 * h] = xv.x, x.v[4 * h + 1] = xv.y, x.v[4 * h + 2] = xv.z, x.v[4 * h + 3] = xv.w;
       }
     }
+    if constexpr (KDA) {
+      const float4* pg = reinterpret_cast<const float4*>(a.g + (size_t(tok) * NH + bh) * D + (tt & 7) * 16);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float4 xg = pg[h];
+        x.gv[4 * h] = xg.x, x.gv[4 * h + 1] = xg.y, x.gv[4 * h + 2] = xg.z, x.gv[4 * h + 3] = xg.w;
+      }
+    }
     if (w == 0) {
       const size_t th = size_t(min(cc + (l & 15), n_tok - 1)) * NH + bh;
-      x.g = a.g[th];
+      if constexpr (!KDA) x.g = a.g[th];
       x.beta = a.beta[th];
     }
   };
@@ -369,10 +379,14 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         *reinterpret_cast<float4*>(&sh_qu[tr][ch + 4 * h]) = xq;
         // v goes where the right-hand side will be built: sh_r[wave of the column]
         *reinterpret_cast<float4*>(&sh_r[ch >> 6][tr][(ch & 63) + 4 * h]) = xv;
+        if constexpr (KDA)
+          *reinterpret_cast<float4*>(&sh_g[tr][ch + 4 * h]) =
+              in ? make_float4(cur.gv[4 * h], cur.gv[4 * h + 1], cur.gv[4 * h + 2], cur.gv[4 * h + 3])
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
       }
       if (w == 0) {  // G_t = sum of g_s over s <= t: an inclusive scan over lanes 0-15
         const bool tin = lane < nc;  // (nc <= 16)
-        float G = tin ? cur.g : 0.f;
+        float G = (tin && !KDA) ? cur.g : 0.f;
         const float bt = tin ? cur.beta : 0.f;
         G += dpp_shr<1>(G);
         G += dpp_shr<2>(G);
@@ -383,6 +397,16 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
     }
     if (c0 + C < n_tok) fetch(c0 + C, cur);
     __syncthreads();
+    if constexpr (KDA) {  // G_t per key channel: thread i sums its channel over the chunk in place
+      const int i = 64 * w + lane_id();
+      float G = 0.f;
+#pragma unroll
+      for (int tk = 0; tk < C; ++tk) {
+        G += sh_g[tk][i];
+        sh_g[tk][i] = G;
+      }
+      __syncthreads();
+    }
 
     // ---- K S0, then Q S0, for this wave's columns (token 4g + r, column
     // 64w + 16TC + c), each turned into its LDS form before the next
@@ -395,14 +419,16 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
       for (int TC = 0; TC < 4; ++TC) P[TC] = v4f{0.f, 0.f, 0.f, 0.f};
       // operands one row block ahead of the products that use them (a fence
       // per block keeps the loads from piling up further ahead)
+      // (KDA: the operand row is x_t (.) e^{G_t}, the decay through token t)
+      auto opnd = [&](int row) { return KDA ? src[c][row] * exp_fast(sh_g[c][row]) : src[c][row]; };
       float ak[4], an[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ak[r] = src[c][4 * g + r];
+      for (int r = 0; r < 4; ++r) ak[r] = opnd(4 * g + r);
 #pragma unroll
       for (int TR = 0; TR < 8; ++TR) {
         if (TR < 7) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) an[r] = src[c][16 * (TR + 1) + 4 * g + r];
+          for (int r = 0; r < 4; ++r) an[r] = opnd(16 * (TR + 1) + 4 * g + r);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -416,7 +442,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tk = 4 * g + r;
-        const float eG = exp_fast(sh_G[tk]), bt = sh_beta[tk];
+        const float eG = KDA ? 1.f : exp_fast(sh_G[tk]), bt = sh_beta[tk];
 #pragma unroll
         for (int TC = 0; TC < 4; ++TC) {
           if (pass == 0) sh_r[w][tk][16 * TC + c] = bt * (sh_r[w][tk][16 * TC + c] - eG * P[TC][r]);
@@ -424,8 +450,51 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         }
       }
     }
-    // ---- K K^T (wave 0) or Q K^T (wave 1): entry (t = 4g + r, s = c)
-    {
+    // ---- KDA: for the 120 pairs s < t, beta_t sum_i k_t,i k_s,i e^{G_t,i - G_s,i}
+    // and sum_i q_t,i k_s,i e^{G_t,i - G_s,i} (one decay factor serves both),
+    // and for the 16 pairs s = t, q_t . k_t; each summed over the channels by
+    // one thread (items t0 and t0 + 128)
+    if constexpr (KDA) {
+      const int t0 = 64 * w + lane_id();
+      for (int p = t0; p < 136; p += 128) {
+        if (p < 120) {
+          int tk = 1, base = 0;  // p = t (t - 1) / 2 + s
+          for (int t2 = 2; t2 < C; ++t2)
+            if (t2 * (t2 - 1) / 2 <= p) tk = t2, base = t2 * (t2 - 1) / 2;
+          const int s2 = p - base;
+          float ak = 0.f, aq = 0.f;
+#pragma unroll 4
+          for (int i = 0; i < D; i += 4) {
+            const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i]);
+            const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i]);
+            const float4 ks = *reinterpret_cast<const float4*>(&sh_k[s2][i]);
+            const float4 gt = *reinterpret_cast<const float4*>(&sh_g[tk][i]);
+            const float4 gs = *reinterpret_cast<const float4*>(&sh_g[s2][i]);
+            const float e0 = ks.x * exp_fast(gt.x - gs.x), e1 = ks.y * exp_fast(gt.y - gs.y);
+            const float e2 = ks.z * exp_fast(gt.z - gs.z), e3 = ks.w * exp_fast(gt.w - gs.w);
+            ak = fmaf(k4.x, e0, ak), aq = fmaf(q4.x, e0, aq);
+            ak = fmaf(k4.y, e1, ak), aq = fmaf(q4.y, e1, aq);
+            ak = fmaf(k4.z, e2, ak), aq = fmaf(q4.z, e2, aq);
+            ak = fmaf(k4.w, e3, ak), aq = fmaf(q4.w, e3, aq);
+          }
+          sh_a[tk][s2] = sh_beta[tk] * ak;
+          sh_b[tk][s2] = aq;
+        } else {
+          const int tk = p - 120;
+          float aq = 0.f;
+#pragma unroll 4
+          for (int i = 0; i < D; i += 4) {
+            const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i]);
+            const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i]);
+            aq = fmaf(q4.x, k4.x, aq), aq = fmaf(q4.y, k4.y, aq);
+            aq = fmaf(q4.z, k4.z, aq), aq = fmaf(q4.w, k4.w, aq);
+          }
+          sh_b[tk][tk] = aq;
+        }
+      }
+    }
+    // ---- GDN: K K^T (wave 0) or Q K^T (wave 1): entry (t = 4g + r, s = c)
+    if constexpr (!KDA) {
       lane = lane_id(), g = lane >> 4, c = lane & 15;
       v4f X = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
@@ -475,19 +544,29 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
       lane = lane_id(), g = lane >> 4, c = lane & 15;
       const float GC = sh_G[C - 1], eC = exp_fast(GC);
 #pragma unroll
-      for (int TR = 0; TR < 8; ++TR)
+      for (int TR = 0; TR < 8; ++TR) {
+        if constexpr (KDA) {  // row 16 TR + 4 g + r decays by e^{G_C} of its key channel
+          v4f e;
 #pragma unroll
-        for (int TC = 0; TC < 4; ++TC) M[TR][TC] *= eC;
+          for (int r = 0; r < 4; ++r) e[r] = exp_fast(sh_g[C - 1][16 * TR + 4 * g + r]);
+#pragma unroll
+          for (int TC = 0; TC < 4; ++TC) M[TR][TC] *= e;
+        } else {
+#pragma unroll
+          for (int TC = 0; TC < 4; ++TC) M[TR][TC] *= eC;
+        }
+      }
 #pragma unroll
       for (int kb = 0; kb < C / 4; ++kb) {
         const int s2 = 4 * kb + g;
-        const float f = exp_fast(GC - sh_G[s2]);
+        const float f = KDA ? 1.f : exp_fast(GC - sh_G[s2]);
         float ub[4];
 #pragma unroll
         for (int TC = 0; TC < 4; ++TC) ub[TC] = sh_qu[s2][64 * w + 16 * TC + c];
 #pragma unroll
         for (int TR = 0; TR < 8; ++TR) {
-          const float ak = f * sh_k[s2][16 * TR + c];
+          const float ak = KDA ? sh_k[s2][16 * TR + c] * exp_fast(sh_g[C - 1][16 * TR + c] - sh_g[s2][16 * TR + c])
+                               : f * sh_k[s2][16 * TR + c];
 #pragma unroll
           for (int TC = 0; TC < 4; ++TC) M[TR][TC] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, ub[TC], M[TR][TC], 0, 0, 0);
         }
@@ -621,8 +700,8 @@ __global__ void __launch_bounds__(64) prefill_columns_kernel(PrefillArgs a) {
 
 template <int D, bool KDA, bool BF16>
 hipError_t launch(const lq_dims& d, const PrefillArgs& a, hipStream_t stream) {
-  if constexpr (D == 128 && !KDA) {
-    hipLaunchKernelGGL((prefill_chunk_kernel<BF16>), dim3(d.batch * d.heads), dim3(128), 0, stream, a);
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL((prefill_chunk_kernel<BF16, KDA>), dim3(d.batch * d.heads), dim3(128), 0, stream, a);
   } else if constexpr (BF16 || !KDA) {
     hipLaunchKernelGGL((prefill_blocks_kernel<D, KDA, BF16>), dim3(d.batch * d.heads), dim3(128), 0, stream, a);
   } else {

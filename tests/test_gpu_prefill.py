@@ -146,6 +146,9 @@ def test_handoff_encode_and_decode_on(name, kw, bits):
     ("qwen_gdn", dict(batch=2), 5),
     ("qwen_gdn", dict(batch=2), 37),
     ("tiny_gdn", dict(batch=2, heads=2, d_k=128, d_v=128), 37),
+    ("kda_int4", dict(batch=2), 5),     # KDA at d = 128 also runs in chunks
+    ("kda_int4", dict(batch=2), 37),
+    ("kda_int4", dict(batch=2, act_bf16=True), 37),
 ])
 def test_prefill_short_and_empty_prompts(name, kw, L):
     """An empty prompt leaves the state as it is and the handoff is the plain
