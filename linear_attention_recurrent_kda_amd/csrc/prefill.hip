@@ -12,25 +12,24 @@
 // (o = S'^T q + (k . q) u). Three kernels, all keeping the state on chip for
 // the whole prompt (read and written once):
 //
-// - prefill_chunk_kernel (GDN at d = 128): chunks of 16 tokens, whose
+// - prefill_chunk_kernel (d = 128, GDN and KDA): chunks of 16 tokens, whose
 //   products and state update run on the matrix cores (described at the
 //   kernel).
-// - prefill_blocks_kernel (GDN at d < 128, and KDA with bf16 activations):
-//   128 threads per head on an 8 x 16 grid, each with a block of D/8 key rows
-//   by D/16 value columns; the column partials of S'^T k and S'^T q and the
+// - prefill_blocks_kernel (d < 128: GDN, and KDA with bf16 activations): 128
+//   threads per head on an 8 x 16 grid, each with a block of D/8 key rows by
+//   D/16 value columns; the column partials of S'^T k and S'^T q and the
 //   partial k . q are summed over the wave's rows with the row-swap
 //   instructions (the work split across the rows) and over the two waves
 //   through LDS, one barrier per token, double-buffered; the next token's
 //   inputs load while the current one computes. GDN keeps the scalar decay as
 //   one scale per head.
-// - prefill_columns_kernel (KDA with fp32 activations): every value column j
-//   evolves on its own (u_j needs column j of S' and k; o_j column j of S and
-//   q), so one thread owns one column, all d_k key rows, and a token costs it
-//   two passes over its column with no exchange between threads. k, q and
-//   beta are the same for every thread of a head and arrive through scalar
-//   loads as instruction operands; the per-channel gates are exponentiated
-//   two channels per lane and broadcast with readlane. One wave covers 64
-//   columns of a head. (The blocks kernel spills at this instantiation.)
+// - prefill_columns_kernel (d < 128, KDA with fp32 activations): every value
+//   column j evolves on its own (u_j needs column j of S' and k; o_j column j
+//   of S and q), so one thread owns one column, all d_k key rows, and a token
+//   costs it two passes over its column with no exchange between threads. k,
+//   q and beta are the same for every thread of a head and arrive through
+//   scalar loads as instruction operands; the per-channel gates are
+//   exponentiated two channels per lane and broadcast with readlane.
 #include "lq_common.h"
 #include "lq_launch.h"
 #include "lq_rows.h"
