@@ -58,13 +58,16 @@ def test_prefill_matches_exact_recurrence(name, kw):
     ("tiny_gdn", dict(batch=2, heads=2, d_k=128, d_v=128)),  # fp32 activations: one thread per column
     ("qwen_gdn", dict(batch=2)),                              # bf16 activations: 16 x 8 blocks
     ("tiny_gdn", dict(batch=2, heads=3, act_bf16=True)),      # bf16, d = 32
+    ("kda_int4", dict(batch=2)),                              # KDA chunks: per-channel decays
 ])
 def test_prefill_strong_decay(name, kw):
-    """GDN decays 40x the workload's (the state shrinks by 2^-32 within a few
-    dozen tokens) plus one token with g = -200, whose decay underflows fp32 to
-    zero: the kernels keep the scalar decay as one scale per head and fold it
-    into the state whenever it falls below 2^-32, which these prompts cross
-    several times. Same bound as above against the exact recurrence."""
+    """Decays 40x the workload's (the state shrinks by 2^-32 within a few dozen
+    tokens) plus one token with g = -200, whose decay underflows fp32 to zero.
+    The token-by-token GDN kernel keeps the scalar decay as one scale per head
+    and folds it into the state whenever it falls below 2^-32, which these
+    prompts cross several times; the chunk kernels (GDN and KDA at d = 128)
+    take every decay as an exponent <= 0. Same bound as above against the
+    exact recurrence."""
     wl = W[name].replace(**kw)
     L = 48
     dims = runner.dims_for(wl)
