@@ -351,8 +351,8 @@ def run_prefill(wl, bits, n_tokens):
     """Prefill handoff: the exact recurrence over a prompt of n_tokens (fp32 state
     on chip), then the encode into LeapQuant form. Algorithmic work: 7 d^2 flops
     per head-token (decay, the two column sums S'^T k and S'^T q, the rank-one
-    update). GDN at d = 128 runs in chunks on the matrix cores (bound: fp32
-    MFMA); the other cases run token by token on the vector ALU."""
+    update). At d = 128 the prompt runs in chunks on the matrix cores (bound:
+    fp32 MFMA); below that, token by token on the vector ALU."""
     import torch
 
     from linear_attention_recurrent_kda_amd import leapquant as lqk
@@ -381,7 +381,7 @@ def run_prefill(wl, bits, n_tokens):
     pre_us, enc_us = min(runs)
     flops = 7.0 * d * d * N * n_tokens
     tflops = flops / (pre_us * 1e-6) / 1e12
-    mfma = (not wl.kda) and d == 128
+    mfma = d == 128
     bound, peak = ("mfma", FP32_MFMA_PEAK_TFLOPS) if mfma else ("alu", FP32_VECTOR_PEAK_TFLOPS)
     return {"prompt_tokens": n_tokens, "head_tokens_per_s": round(N * n_tokens / (pre_us * 1e-6), 1),
             "prefill_us": round(pre_us, 1), "encode_us": round(enc_us, 1),
