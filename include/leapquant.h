@@ -182,7 +182,9 @@ int gdn_decode_fp32_baseline(const lq_dims* dims, float* S, const void* q, const
    buffer), so that decoding starts from the prompt. The pages quantize the
    state per window of decoded tokens (wink.run article, per-window
    quantization; LeapQuant abstract); the prompt runs at full precision and
-   is quantized once, at the handoff.
+   is quantized once, at the handoff. At d_k = 128 the prompt is evaluated
+   in chunks of 16 tokens (the same recurrence reassociated into matrix
+   products), so results agree with the token-by-token form to fp32 rounding.
    S: fp32 [B*H][d_v][d_k] (transposed), the state before the prompt on
    entry and after it on return. Tokens are time-major: q, k: [n_tokens][B][H]
    [d_k]; v: [n_tokens][B][H][d_v] (fp32 or bf16 per act_dtype); g: fp32
