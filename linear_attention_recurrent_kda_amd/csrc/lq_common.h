@@ -68,9 +68,11 @@ __device__ __forceinline__ uint32_t rows_umax(uint32_t x) {
   return max(uint32_t(q[0]), uint32_t(q[1]));
 }
 
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
+
 // exp(x) as 2^(x log2 e) on the transcendental unit (about 1 ulp of exp2,
 // plus the rounding of the product: relative error ~ |x| 2^-24).
-__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
 // Sum / max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
 // with the gfx950 row-swap instructions. Every lane ends with the same value.

@@ -275,7 +275,9 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   __shared__ float sh_a[C][C];                   // beta_t A_ts, s < t
   __shared__ float sh_b[C][C];                   // e^{G_t-G_s} k_s.q_t, s <= t
   __shared__ float sh_G[C], sh_beta[C];          // GDN: G_t; beta_t
-  __shared__ __align__(16) float sh_g[KDA ? C : 1][KS];  // KDA: g, then G_t per key channel
+  // KDA: g, then G_t per key channel in base-2 units (G_t log2 e), so that
+  // every decay factor e^{G_t - G_s} is a single exp2 of a difference
+  __shared__ __align__(16) float sh_g[KDA ? C : 1][KS];
 
   // Lane-derived indices are re-derived in every phase from an opaque copy of
   // the thread index, so that the compiler forms each phase's addresses there
@@ -401,7 +403,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
       float G = 0.f;
 #pragma unroll
       for (int tk = 0; tk < C; ++tk) {
-        G += sh_g[tk][i];
+        G = fmaf(sh_g[tk][i], kLog2e, G);
         sh_g[tk][i] = G;
       }
       __syncthreads();
@@ -419,7 +421,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
       // operands one row block ahead of the products that use them (a fence
       // per block keeps the loads from piling up further ahead)
       // (KDA: the operand row is x_t (.) e^{G_t}, the decay through token t)
-      auto opnd = [&](int row) { return KDA ? src[c][row] * exp_fast(sh_g[c][row]) : src[c][row]; };
+      auto opnd = [&](int row) { return KDA ? src[c][row] * __builtin_amdgcn_exp2f(sh_g[c][row]) : src[c][row]; };
       float ak[4], an[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ak[r] = opnd(4 * g + r);
@@ -469,12 +471,13 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
             const float4 ks = *reinterpret_cast<const float4*>(&sh_k[s2][i]);
             const float4 gt = *reinterpret_cast<const float4*>(&sh_g[tk][i]);
             const float4 gs = *reinterpret_cast<const float4*>(&sh_g[s2][i]);
-            const float e0 = ks.x * exp_fast(gt.x - gs.x), e1 = ks.y * exp_fast(gt.y - gs.y);
-            const float e2 = ks.z * exp_fast(gt.z - gs.z), e3 = ks.w * exp_fast(gt.w - gs.w);
+            const float e0 = ks.x * __builtin_amdgcn_exp2f(gt.x - gs.x), e1 = ks.y * __builtin_amdgcn_exp2f(gt.y - gs.y);
+            const float e2 = ks.z * __builtin_amdgcn_exp2f(gt.z - gs.z), e3 = ks.w * __builtin_amdgcn_exp2f(gt.w - gs.w);
             ak = fmaf(k4.x, e0, ak), aq = fmaf(q4.x, e0, aq);
             ak = fmaf(k4.y, e1, ak), aq = fmaf(q4.y, e1, aq);
             ak = fmaf(k4.z, e2, ak), aq = fmaf(q4.z, e2, aq);
             ak = fmaf(k4.w, e3, ak), aq = fmaf(q4.w, e3, aq);
+            asm volatile("" ::: "memory");  // one step's LDS reads at a time (register pressure)
           }
           sh_a[tk][s2] = sh_beta[tk] * ak;
           sh_b[tk][s2] = aq;
@@ -547,7 +550,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         if constexpr (KDA) {  // row 16 TR + 4 g + r decays by e^{G_C} of its key channel
           v4f e;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) e[r] = exp_fast(sh_g[C - 1][16 * TR + 4 * g + r]);
+          for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(sh_g[C - 1][16 * TR + 4 * g + r]);
 #pragma unroll
           for (int TC = 0; TC < 4; ++TC) M[TR][TC] *= e;
         } else {
@@ -564,7 +567,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         for (int TC = 0; TC < 4; ++TC) ub[TC] = sh_qu[s2][64 * w + 16 * TC + c];
 #pragma unroll
         for (int TR = 0; TR < 8; ++TR) {
-          const float ak = KDA ? sh_k[s2][16 * TR + c] * exp_fast(sh_g[C - 1][16 * TR + c] - sh_g[s2][16 * TR + c])
+          const float ak = KDA ? sh_k[s2][16 * TR + c] * __builtin_amdgcn_exp2f(sh_g[C - 1][16 * TR + c] - sh_g[s2][16 * TR + c])
                                : f * sh_k[s2][16 * TR + c];
 #pragma unroll
           for (int TC = 0; TC < 4; ++TC) M[TR][TC] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, ub[TC], M[TR][TC], 0, 0, 0);
