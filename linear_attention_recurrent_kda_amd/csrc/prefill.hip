@@ -453,46 +453,46 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
     }
     // ---- KDA: for the 120 pairs s < t, beta_t sum_i k_t,i k_s,i e^{G_t,i - G_s,i}
     // and sum_i q_t,i k_s,i e^{G_t,i - G_s,i} (one decay factor serves both),
-    // and for the 16 pairs s = t, q_t . k_t; each summed over the channels by
-    // one thread (items t0 and t0 + 128)
+    // each summed over the channels by one thread; then the 16 pairs s = t,
+    // q_t . k_t, by all threads: eight lanes per token, 16 channels each
     if constexpr (KDA) {
       const int t0 = 64 * w + lane_id();
-      for (int p = t0; p < 136; p += 128) {
-        if (p < 120) {
-          int tk = 1, base = 0;  // p = t (t - 1) / 2 + s
-          for (int t2 = 2; t2 < C; ++t2)
-            if (t2 * (t2 - 1) / 2 <= p) tk = t2, base = t2 * (t2 - 1) / 2;
-          const int s2 = p - base;
-          float ak = 0.f, aq = 0.f;
+      if (t0 < 120) {
+        int tk = 1, base = 0;  // t0 = t (t - 1) / 2 + s
+        for (int t2 = 2; t2 < C; ++t2)
+          if (t2 * (t2 - 1) / 2 <= t0) tk = t2, base = t2 * (t2 - 1) / 2;
+        const int s2 = t0 - base;
+        float ak = 0.f, aq = 0.f;
 #pragma unroll 4
-          for (int i = 0; i < D; i += 4) {
-            const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i]);
-            const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i]);
-            const float4 ks = *reinterpret_cast<const float4*>(&sh_k[s2][i]);
-            const float4 gt = *reinterpret_cast<const float4*>(&sh_g[tk][i]);
-            const float4 gs = *reinterpret_cast<const float4*>(&sh_g[s2][i]);
-            const float e0 = ks.x * __builtin_amdgcn_exp2f(gt.x - gs.x), e1 = ks.y * __builtin_amdgcn_exp2f(gt.y - gs.y);
-            const float e2 = ks.z * __builtin_amdgcn_exp2f(gt.z - gs.z), e3 = ks.w * __builtin_amdgcn_exp2f(gt.w - gs.w);
-            ak = fmaf(k4.x, e0, ak), aq = fmaf(q4.x, e0, aq);
-            ak = fmaf(k4.y, e1, ak), aq = fmaf(q4.y, e1, aq);
-            ak = fmaf(k4.z, e2, ak), aq = fmaf(q4.z, e2, aq);
-            ak = fmaf(k4.w, e3, ak), aq = fmaf(q4.w, e3, aq);
-            asm volatile("" ::: "memory");  // one step's LDS reads at a time (register pressure)
-          }
-          sh_a[tk][s2] = sh_beta[tk] * ak;
-          sh_b[tk][s2] = aq;
-        } else {
-          const int tk = p - 120;
-          float aq = 0.f;
-#pragma unroll 4
-          for (int i = 0; i < D; i += 4) {
-            const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i]);
-            const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i]);
-            aq = fmaf(q4.x, k4.x, aq), aq = fmaf(q4.y, k4.y, aq);
-            aq = fmaf(q4.z, k4.z, aq), aq = fmaf(q4.w, k4.w, aq);
-          }
-          sh_b[tk][tk] = aq;
+        for (int i = 0; i < D; i += 4) {
+          const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i]);
+          const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i]);
+          const float4 ks = *reinterpret_cast<const float4*>(&sh_k[s2][i]);
+          const float4 gt = *reinterpret_cast<const float4*>(&sh_g[tk][i]);
+          const float4 gs = *reinterpret_cast<const float4*>(&sh_g[s2][i]);
+          const float e0 = ks.x * __builtin_amdgcn_exp2f(gt.x - gs.x), e1 = ks.y * __builtin_amdgcn_exp2f(gt.y - gs.y);
+          const float e2 = ks.z * __builtin_amdgcn_exp2f(gt.z - gs.z), e3 = ks.w * __builtin_amdgcn_exp2f(gt.w - gs.w);
+          ak = fmaf(k4.x, e0, ak), aq = fmaf(q4.x, e0, aq);
+          ak = fmaf(k4.y, e1, ak), aq = fmaf(q4.y, e1, aq);
+          ak = fmaf(k4.z, e2, ak), aq = fmaf(q4.z, e2, aq);
+          ak = fmaf(k4.w, e3, ak), aq = fmaf(q4.w, e3, aq);
+          asm volatile("" ::: "memory");  // one step's LDS reads at a time (register pressure)
         }
+        sh_a[tk][s2] = sh_beta[tk] * ak;
+        sh_b[tk][s2] = aq;
+      }
+      {
+        const int tk = t0 >> 3, i0 = 16 * (t0 & 7);  // lanes 8m..8m+7 of a wave share a token
+        float aq = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i0 + 4 * h]);
+          const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i0 + 4 * h]);
+          aq = fmaf(q4.x, k4.x, aq), aq = fmaf(q4.y, k4.y, aq);
+          aq = fmaf(q4.z, k4.z, aq), aq = fmaf(q4.w, k4.w, aq);
+        }
+        aq = group_sum<8>(aq);
+        if ((t0 & 7) == 0) sh_b[tk][tk] = aq;
       }
     }
     // ---- GDN: K K^T (wave 0) or Q K^T (wave 1): entry (t = 4g + r, s = c)
