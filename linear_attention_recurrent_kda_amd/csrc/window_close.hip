@@ -504,8 +504,11 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     int code[RB];
 #pragma unroll
     for (int x = 0; x < RB; ++x) {
-      const float qv = fminf(fmaxf(rintf(M[x >> 2][bb][x & 3] * inv[bb]), -float(Q)), float(Q));
-      code[x] = int(qv);
+      // M inv + 1.5 2^23 rounds once to the nearest integer, ties to even,
+      // and the low bits of the sum's pattern are that integer in two's
+      // complement. No clamp: |M| is at most its column's maximum, so
+      // |M inv| <= Q (1 + 2^-24) < Q + 1/2.
+      code[x] = int(__float_as_uint(fmaf(M[x >> 2][bb][x & 3], inv[bb], 12582912.f)) - 0x4B400000u);
     }
     if constexpr (BITS == 6) {
       int hi[RB];
