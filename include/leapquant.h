@@ -126,16 +126,20 @@ int lq_state_sizes(const lq_dims* dims, size_t* bytes_out);
    T-step power method with deflation (start vectors from SplitMix64), key-row
    smoothing, symmetric quantisation with per-value-column scales; writes the
    compensators as entries 0..r-1 and empties every buffer (buf_len = 0).
-   Same arithmetic as a window close with no entries. Sources: LeapQuant abstract (compensator tokens, smoothing) and the
-   wink.run article's compensator and smoothing paragraphs.
+   Same arithmetic as a window close with no entries. Sources: LeapQuant
+   abstract (compensator tokens, smoothing) and the wink.run article's
+   compensator and smoothing paragraphs.
    S: fp32 [B*H][d_v][d_k] (element (j, i) = S[i][j], i.e. S transposed).
    dbg_residual: NULL, or fp32 [B*H][d_v][d_k] receiving the residual after
    the compensators are removed and before smoothing/rounding. */
 int leapquant_encode(const lq_dims* dims, const float* S, const lq_state* st,
                      float* dbg_residual, void* stream);
 
-/* One decode token for every head (per-window quantization: the low-bit state
-   stays fixed and the token's update is buffered in fp32). Per head, with
+/* One decode token for every head. Source: the wink.run article, paragraph on
+   per-window quantization (the low-bit state stays frozen for a window and
+   each token's update is kept in a full-precision buffer), and the
+   compensator-token paragraph (compensators are updates of the same shape as
+   a token's, read on the same path); LeapQuant abstract. Per head, with
    G_t = G_{t-1} + g_t (G_{t-1} = G of the last entry, 0 if there is none):
      y^x = c (.) C^T (s (.) exp(G_t) (.) x) + sum_e u_e (k_e . (exp(G_t - G_e) (.) x)),
      u_t = beta_t (v_t - y^k),  o_t = y^q + (k_t . q_t) u_t,
@@ -166,7 +170,10 @@ int leapquant_window_close(const lq_dims* dims, const lq_state* st, const int32_
                            int32_t n_seq, float* dbg_residual, void* stream);
 
 /* FP32-state baseline: one exact decode token of the gated delta rule with the
-   state kept in fp32 (no quantisation), decay first:
+   state kept in fp32 (no quantisation), the full-precision state that the
+   LeapQuant abstract and the wink.run article's results table and speed
+   paragraph compare against (gated delta rule: Gated DeltaNet; per-channel
+   decay: Kimi Delta Attention). Decay first:
      S' = alpha (.)_rows S,  u = beta (v - S'^T k),  S = S' + k u^T,  o = S^T q.
    S: fp32 [B*H][d_v][d_k] (transposed, in/out). Other arguments as
    leapquant_decode_step. Only batch, heads, d_k, d_v, decay_per_channel and
@@ -223,7 +230,11 @@ int leapquant_restore(const lq_dims* dims, const lq_state* st, const int32_t* se
 
 /* Dense window-start state Shat_0 = sum_{e<r} k_e u_e^T + diag(s) C diag(c)
    (compensators plus residual) of every head into S_out: fp32
-   [B*H][d_v][d_k] (transposed). Test helper. */
+   [B*H][d_v][d_k] (transposed). Source: the wink.run article's
+   compensator-token and residual-smoothing paragraphs (the state is the
+   rank-one compensators plus the smoothed, quantized residual). Reads the
+   codes, the scales and entries 0..r-1 only (the buffered entries are not
+   part of Shat_0); writes nothing but S_out. Test helper. */
 int leapquant_dequantize(const lq_dims* dims, const lq_state* st, float* S_out, void* stream);
 
 /* Host-only: sequences whose window ends with decode token `step` (0-based),
