@@ -199,3 +199,60 @@ def g1_check(R_gpu_math: np.ndarray, host: Dict[str, np.ndarray], bits: int, smo
     ulp = np.spacing(np.maximum(np.abs(c_ref), np.float32(1e-38)).astype(np.float32))
     c_ulps = float(np.max(np.abs(c_gpu.astype(np.float64) - c_ref.astype(np.float64)) / ulp))
     return dict(same=same, max_diff=max_diff, s_exact=s_exact, c_ulps=c_ulps)
+
+
+def download_heads(st: lqk.State, dims: lqk.Dims, heads) -> Dict[str, np.ndarray]:
+    """download_state restricted to the listed heads (gathered on the device)."""
+    torch.cuda.synchronize()
+    idx = torch.as_tensor(np.asarray(heads), device="cuda", dtype=torch.long)
+    out = {n: getattr(st, n).index_select(0, idx).cpu().numpy() for n in lqk.STATE_FIELDS if n != "err"}
+    out["C"] = unpack_codes(out["codes"], dims.bits, dims.d)
+    r = dims.n_comp
+    out["comp_k"], out["comp_u"], out["comp_g"] = out["ent_k"][:, :r], out["ent_u"][:, :r], out["ent_g"][:, :r]
+    out["buf_k"], out["buf_u"], out["buf_g"] = out["ent_k"][:, r:], out["ent_u"][:, r:], out["ent_g"][:, r:]
+    return out
+
+
+def run_gpu_closes(wl: wk.Workload, steps: int, check_seqs: Sequence[int], bits=None, on_close=None,
+                   chunk: int = 16):
+    """Free-running HIP path over the full batch, like run_gpu, with a hook at
+    every window close: on_close(t, local, pre, post, R) gets the step, the
+    indices (into the checked heads) of the checked heads that close, their
+    state just before and just after the close, and the residual the close
+    quantized (host arrays, checked heads only; R in the math layout).
+    Returns (outputs of check_seqs [steps][S][H][d], Decoder, error word, the
+    checked heads' state after the initial encode)."""
+    dims = runner.dims_for(wl, bits)
+    win_len, win_off = wk.window_lengths(wl), wk.window_offsets(wl)
+    dec = runner.Decoder(dims, win_len, win_off)
+    S0 = wk.initial_states(wl, range(wl.batch))
+    dec.encode(runner.states_to_device(S0))
+    del S0
+    gheads = heads_of(check_seqs, wl.heads)
+    start = download_heads(dec.state, dims, gheads)
+    dbg = torch.zeros((wl.batch * wl.heads, wl.d_v, wl.d_k), dtype=torch.float32, device="cuda")
+    seq_of = np.asarray(check_seqs)
+    stream = wk.TokenStream(wl)
+    sel = torch.as_tensor(seq_of, device="cuda", dtype=torch.long)
+    outs = torch.empty((steps, len(check_seqs), wl.heads, wl.d_v), dtype=torch.float32, device="cuda")
+    for c0 in range(0, steps, chunk):
+        n = min(chunk, steps - c0)
+        dev = runner.upload_tokens(stream.next(n), wl.act_bf16)
+        for i in range(n):
+            t = c0 + i
+            o = dec.step(dev["q"][i], dev["k"][i], dev["v"][i], dev["g"][i], dev["beta"][i], close=False)
+            outs[t] = o.view(wl.batch, wl.heads, wl.d_v).index_select(0, sel)
+            due = (win_off[seq_of].astype(np.int64) + t + 1) % win_len[seq_of] == 0
+            if dec.closes_at(t) and on_close is not None and np.any(due):
+                local = np.nonzero(np.repeat(due, wl.heads))[0]
+                pre = download_heads(dec.state, dims, gheads[local])
+                dec.close_due(t, dbg)
+                post = download_heads(dec.state, dims, gheads[local])
+                idx = torch.as_tensor(gheads[local], device="cuda", dtype=torch.long)
+                on_close(t, local, pre, post, T(dbg.index_select(0, idx).cpu().numpy()))
+            else:
+                dec.close_due(t)
+        del dev
+    torch.cuda.synchronize()
+    err = int(dec.state.err.item())
+    return outs.cpu().numpy(), dec, err, start

@@ -7,8 +7,11 @@ Protocol (tolerances are the ones the method's target states):
   G2 decomposition: the GPU's compensators plus residual rebuild the dense
      state (the initial state, or the oracle's fold of the GPU's pre-close
      buffers) to <= 1e-6 relative Frobenius.
-  G3 free-running outputs: for every token, relative L2 of o over all heads
-     <= 1e-3 against the oracle's plain definition from the same inputs.
+  G3 outputs: teacher-forced (every window starts from the oracle's
+     encoding), every token <= 1e-3 relative L2 over all checked heads and for
+     each head; free-running, every token and head within the bound that the
+     GPU's and the oracle's window-start states allow (see the test), with
+     every close checked against the oracle's close of the same buffers.
   G4 single step from an oracle-made state uploaded bit-exactly: o_t and u_t
      <= 1e-5 relative.
 Full-size workloads run the whole batch on the GPU; the oracle checks all
@@ -136,6 +139,7 @@ G3_CASES = [
     ("prefix_mix", 8, 64, {}),
     ("qwen_gdn", 6, 64, {}),
     ("kda_int4", 6, 48, {}),
+    ("kda_int4", 4, 48, dict(act_bf16=True)),   # per-channel decay with bf16 activations
 ]
 
 
@@ -145,42 +149,128 @@ def _g3_setup(name, kw):
     return wl, seqs
 
 
+def _per_head(o, ref, d_v):
+    """Relative L2 of each head's output at each step: [steps][heads]."""
+    a = np.asarray(o, np.float64).reshape(o.shape[0], -1, d_v)
+    b = np.asarray(ref, np.float64).reshape(a.shape)
+    return np.linalg.norm(a - b, axis=2) / np.linalg.norm(b, axis=2)
+
+
 @pytest.mark.parametrize("name,bits,steps,kw", G3_CASES)
 def test_outputs_teacher_forced(name, bits, steps, kw):
     """G3, teacher-forced: at every window start the checked heads hold the
-    oracle's encoding; every token's output must then match to 1e-3."""
+    oracle's encoding; every token's output must then match to 1e-3, over all
+    checked heads together and for every head on its own."""
     wl, seqs = _g3_setup(name, kw)
     ref = gh.run_oracle(wl, steps, seqs, bits, record=True)
     o_gpu, _, err = gh.run_gpu(wl, steps, seqs, bits, force=ref)
     assert err == 0
     per_step = [gh.rel_l2(o_gpu[t], ref["o"][t]) for t in range(steps)]
-    print(name, bits, kw, "teacher-forced max rel L2", max(per_step), "at", int(np.argmax(per_step)))
+    head = _per_head(o_gpu, ref["o"], wl.d_v)
+    t_w, h_w = np.unravel_index(np.argmax(head), head.shape)
+    print(name, bits, kw, "teacher-forced max rel L2", max(per_step), "at", int(np.argmax(per_step)),
+          "| worst head", head.max(), "(step", int(t_w), "head", int(h_w), ")")
     assert max(per_step) <= 1e-3
+    assert head.max() <= 1e-3
+
+
+# Relative noise on a close's input (16 fp32 ulps) at which the oracle's own
+# codes are reported beside the GPU's: how many codes the GPU's close sets
+# differently from the oracle's close of the same buffers, against how many
+# the oracle itself sets differently under this noise. Reported, not gated:
+# with a fixed small number of power iterations the fp32 and fp64
+# compensators of a nearly degenerate head can differ enough to move a row of
+# codes, in the GPU and in the noisy oracle alike.
+FLIP_NOISE = 2.0 ** -20
 
 
 @pytest.mark.parametrize("name,bits,steps,kw", G3_CASES)
 def test_outputs_free_running(name, bits, steps, kw):
-    """G3, free-running from the same initial state. Requantisation makes the
-    plain definition sensitive to rounding-size perturbations (a code near a
-    tie flips and the flip persists), so the bound is the larger of 1e-3 and
-    four times the oracle's own spread when every state entering a close is
-    perturbed by a few fp32 ulp (relative 2^-22, the rounding of a fold that
-    sums r + n + 1 terms; max over three noise seeds)."""
+    """G3, free-running from the same initial state, split into the two things
+    the run is made of.
+
+    (a) Windows. Inside a window both sides run the exact recurrence from their
+    own window-start state (the GPU in the buffered form, in fp32). The
+    recurrence is affine in the state, S_t = A_t S_c + B_t, with the same B_t on
+    both sides and A_t a product of (I - beta k k^T) Diag(alpha) factors: decay
+    alpha <= 1 and 0 < beta |k|^2 < 2 give |A_t|_2 <= 1. A window-start
+    difference therefore never grows inside the window, and for every head and
+    token |o_gpu - o_ref| <= |Dec_gpu - Dec_ref|_2 |q_t| + 1e-3 |o_ref|, the
+    window start being the head's last close (or the initial encode) on each
+    side and 1e-3 the output tolerance for the window's own arithmetic.
+    (b) Closes. Every close the GPU makes passes G1 and G2 on its own
+    pre-close buffers: its compensators plus the residual it quantized rebuild
+    the oracle's fold of those buffers within 1e-6, and its codes and scales
+    are the oracle's quantization of that residual (codes >= 99.99% identical,
+    all within one LSB; row scales bit-identical; column scales within 2 ulp).
+    Rounding decisions at near-ties are where the two runs part (a code flip
+    persists, [article] on per-step quantization); (a) and (b) together account
+    for every difference, with no free factor."""
     wl, seqs = _g3_setup(name, kw)
-    o_gpu, _, err = gh.run_gpu(wl, steps, seqs, bits)
+    r, T = wl.n_comp, wl.power_iters
+    ref = gh.run_oracle(wl, steps, seqs, bits, record=True)
+    ref_close = {ev.step: ev for ev in ref["closes"]}
+    rng = np.random.default_rng(5)
+    tally = dict(flips=0, l1=0, noisy_l1=0, codes=0, off_by_more=0, g2=0.0, g1_same=1.0)
+    events = []  # (step, local heads, |Dec_gpu - Dec_ref|_2 of those heads)
+
+    def on_close(t, local, pre, post, R):
+        F = lq.fold_window(lq.decode(gh.encoded_of(pre)), pre["buf_k"], pre["buf_u"], pre["buf_g"],
+                           pre["buf_len"], wl.kda)
+        # (b): G2 and G1 of this close
+        rebuilt = np.einsum("nli,nlj->nij", post["comp_k"].astype(np.float64), post["comp_u"]) + R
+        g2 = float((np.linalg.norm(rebuilt - F, axis=(1, 2)) / np.linalg.norm(F, axis=(1, 2))).max())
+        g1 = gh.g1_check(R, post, bits, wl.smoothing)
+        assert g2 <= 1e-6, (t, g2)
+        assert g1["same"] >= 0.9999 and g1["max_diff"] <= 1 and g1["s_exact"] and g1["c_ulps"] <= 2.0, (t, g1)
+        tally["g2"] = max(tally["g2"], g2)
+        tally["g1_same"] = min(tally["g1_same"], g1["same"])
+        # reported: end-to-end code changes against the oracle's close of the same buffers
+        start = pre["comp_u"] if wl.warm_start else None  # the variant starts from the closing window's
+        e = lq.encode(F, r, T, bits, wl.smoothing, start=start)
+        diff = np.abs(post["C"] - e.codes)
+        tally["flips"] += int(np.count_nonzero(diff))
+        tally["l1"] += int(diff.sum())
+        tally["off_by_more"] += int(np.count_nonzero(diff > 1))
+        tally["codes"] += diff.size
+        en = lq.encode(F * (1.0 + FLIP_NOISE * rng.standard_normal(F.shape)), r, T, bits, wl.smoothing,
+                       start=start)
+        tally["noisy_l1"] += int(np.abs(en.codes - e.codes).sum())
+        # (a): the window-start difference against the free-running oracle's window start
+        ev = ref_close[t]
+        assert np.array_equal(np.sort(ev.heads), np.sort(local))
+        D_ref = lq.decode(ev.enc.take(np.argsort(ev.heads)))
+        D_gpu = lq.decode(gh.encoded_of(post).take(np.argsort(local)))
+        events.append((t, np.sort(local), np.linalg.norm(D_gpu - D_ref, ord=2, axis=(1, 2))))
+
+    o_gpu, _, err, start = gh.run_gpu_closes(wl, steps, seqs, bits, on_close)
     assert err == 0
-    ref = gh.run_oracle(wl, steps, seqs, bits)
-    env_t = np.zeros(steps)
-    for seed in (1, 2, 3):
-        noisy = gh.run_oracle(wl, steps, seqs, bits, rounding_noise=2.0 ** -22, noise_seed=seed)
-        env_t = np.maximum(env_t, [gh.rel_l2(noisy["o"][t], ref["o"][t]) for t in range(steps)])
-    env_t = np.maximum.accumulate(env_t)
+    N, d_v = len(seqs) * wl.heads, wl.d_v
+    # window-start difference in force at each step (a close after step t acts from t + 1)
+    delta = np.linalg.norm(lq.decode(gh.encoded_of(start)) - lq.decode(ref["enc0"]), ord=2, axis=(1, 2))
+    delta_t = np.empty((steps, N))
+    ev_at = {t: (loc, dl) for (t, loc, dl) in events}
+    for t in range(steps):
+        delta_t[t] = delta
+        if t in ev_at:
+            loc, dl = ev_at[t]
+            delta = delta.copy()
+            delta[loc] = dl
+    toks = gh.flat_steps(wk.TokenStream(wl, seqs).next(steps))
+    qn = np.stack([np.linalg.norm(tk["q"], axis=1) for tk in toks])             # [steps][N]
+    og = o_gpu.reshape(steps, N, d_v).astype(np.float64)
+    orf = ref["o"].reshape(steps, N, d_v)
+    dist = np.linalg.norm(og - orf, axis=2)
+    bound = delta_t * qn + 1e-3 * np.linalg.norm(orf, axis=2)
+    head = dist / np.linalg.norm(orf, axis=2)
     err_t = np.array([gh.rel_l2(o_gpu[t], ref["o"][t]) for t in range(steps)])
-    strict = 2 * int(wk.window_lengths(wl).min())
     print(name, bits, kw, "free-running max rel L2", err_t.max(), "at", int(err_t.argmax()),
-          "| noise envelope max", env_t.max(), "| first", strict, "tokens max", err_t[:strict].max())
-    assert err_t[:strict].max() <= max(1e-3, 4 * env_t[strict - 1])
-    assert np.all(err_t <= np.maximum(1e-3, 4 * env_t))
+          "| worst head", head.max(), "| max distance / bound", (dist / bound).max(),
+          "| closes", len(events), "max G2", tally["g2"], "min G1 same", tally["g1_same"],
+          "| end to end: codes changed", tally["flips"], "of", tally["codes"],
+          "(by more than one LSB:", tally["off_by_more"], ") sum |dC|", tally["l1"], "; oracle at noise",
+          FLIP_NOISE, ": sum |dC|", tally["noisy_l1"])
+    assert np.all(dist <= bound)
 
 
 @pytest.mark.parametrize("name,bits,n_tok,close_seqs,kw", [
@@ -279,15 +369,18 @@ def test_power_of_two_scaling_is_exact():
     assert np.array_equal(a["comp_u"] * np.float32(32.0), b["comp_u"])
 
 
-def test_max_window_and_compensators():
-    """w_max = 64 with r = 8: more key rows than one pass of the row groups."""
-    wl = W["tiny_gdn"].replace(batch=2, heads=3, d_k=128, d_v=128, window=64, n_comp=8, steps=70)
+@pytest.mark.parametrize("kda", [False, True])
+def test_max_window_and_compensators(kda):
+    """w_max = 64 with r = 8: more entries than the decode step prefetches (24)
+    and than one fold pass of the close (16), for both decays."""
+    wl = W["tiny_gdn"].replace(batch=2, heads=3, d_k=128, d_v=128, window=64, n_comp=8, steps=70, kda=kda)
     steps = 70
-    o_gpu, _, err = gh.run_gpu(wl, steps, [0, 1])
+    ref = gh.run_oracle(wl, steps, [0, 1], record=True)
+    o_gpu, _, err = gh.run_gpu(wl, steps, [0, 1], force=ref)  # teacher-forced: the arithmetic alone
     assert err == 0
-    ref = gh.run_oracle(wl, steps, [0, 1])
-    worst = max(gh.rel_l2(o_gpu[t], ref["o"][t]) for t in range(steps))
-    assert worst <= 1e-3, worst
+    head = _per_head(o_gpu, ref["o"], wl.d_v)
+    print("kda", kda, "worst head rel L2", head.max())
+    assert head.max() <= 1e-3
 
 
 @pytest.mark.parametrize("d,kda,bits", [(64, False, 8), (64, True, 8), (32, True, 8), (64, False, 6), (64, True, 4),

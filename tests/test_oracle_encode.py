@@ -184,6 +184,22 @@ def test_encode_is_deterministic():
         assert np.array_equal(getattr(e1, f), getattr(e2, f))
 
 
+def test_outlier_ratio_hand_computed():
+    """max|X| / median|X| over all entries of each head, worked by hand.
+    Head 0 (2 x 3): |X| sorted 0.5 1 2 3 4 12, median (2 + 3) / 2 = 2.5,
+    max 12, ratio 4.8. Head 1: |X| sorted 1 1 1 1 1 9, median 1, ratio 9.
+    A mean in place of the median gives 22.5 / 6 = 3.75 -> 3.2 for head 0;
+    a per-row statistic, a statistic over heads or a signed max all differ."""
+    X = np.array([[[1.0, -2.0, 0.5], [3.0, -12.0, 4.0]],
+                  [[1.0, 1.0, -1.0], [-1.0, 9.0, 1.0]]])
+    np.testing.assert_array_equal(lq.outlier_ratio(X), [4.8, 9.0])
+    # an odd entry count: |X| = 1..9 (signs mixed), median 5, max 9
+    Y = (np.arange(1, 10, dtype=np.float64) * np.array([1, -1, 1, 1, -1, 1, -1, 1, 1]))[None].reshape(1, 3, 3)
+    np.testing.assert_array_equal(lq.outlier_ratio(Y), [9.0 / 5.0])
+    # transposing a head does not change its ratio
+    np.testing.assert_array_equal(lq.outlier_ratio(np.swapaxes(X, 1, 2)), [4.8, 9.0])
+
+
 def test_outlier_ratio_drops_through_compensators_and_smoothing():
     """In kind with the pages' outlier-to-median example: planted outlier rows
     and columns are removed by the compensators, smoothing balances the rest."""
