@@ -1,0 +1,327 @@
+// Host model of the device addressing of the decode step and the window close
+// (csrc/decode_step.hip, csrc/window_close.hip): every global load and store,
+// buffer-descriptor range and LDS index those kernels form, written out again
+// on the host and checked, for every thread of the workgroup, against the
+// sizes the C ABI documents (lq_state_sizes) and the kernels' LDS arrays.
+//
+// Checked for d in {32, 64, 128}, 8-, 6- and 4-bit codes, scalar and
+// per-channel decay, fp32 and bf16 activations, r = 0..8 compensators, buffer
+// capacities w_max from 1 to 64 and every buffer length a launch accepts:
+//  - a buffer descriptor's range lies inside its allocation (the hardware
+//    returns zeros past the descriptor, never past the allocation);
+//  - every access that must return data lies inside its descriptor (reads
+//    past a descriptor are allowed only where the kernel relies on the zeros);
+//  - every plain pointer access and every LDS index lies inside its array.
+// Exit status 0 and one summary line when every check holds; the first
+// violation is printed with its configuration and exits with status 1.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+// Planted-mistake switches for the model's own test (defaults are the real
+// sizes): the kappa rows of the decode step's LDS, and slack taken off the
+// entry rows a state holds per head.
+#ifndef MODEL_KAPPA_ROWS
+#define MODEL_KAPPA_ROWS (8 + 64 + 1)
+#endif
+#ifndef MODEL_ENTRY_SLACK
+#define MODEL_ENTRY_SLACK 0
+#endif
+
+namespace {
+
+long long checks = 0;
+
+struct Cfg {
+  int D, BITS, KDA, BF16, r, w_max, n, bh, BH;
+};
+
+void fail(const Cfg& c, const char* what, long long off, long long lo, long long hi, int t) {
+  std::printf("VIOLATION %s: offset %lld not in [%lld, %lld) -- d=%d bits=%d kda=%d bf16=%d r=%d w_max=%d n=%d bh=%d/%d thread=%d\n",
+              what, off, lo, hi, c.D, c.BITS, c.KDA, c.BF16, c.r, c.w_max, c.n, c.bh, c.BH, t);
+  std::exit(1);
+}
+
+// [off, off + size) must lie inside [lo, hi)
+void in(const Cfg& c, const char* what, long long off, long long size, long long lo, long long hi, int t) {
+  ++checks;
+  if (off < lo || off + size > hi) fail(c, what, off, lo, hi, t);
+}
+
+// ---- sizes, as lq_state_sizes (bytes)
+struct Sizes {
+  long long codes, s, c, ek, eu, eg, blen, act_qk, act_v, g, beta, o, head_codes;
+  int NE;
+};
+
+Sizes sizes(const Cfg& c) {
+  Sizes z{};
+  const long long BH = c.BH, D = c.D;
+  z.NE = c.r + c.w_max - MODEL_ENTRY_SLACK;
+  z.head_codes = D * D * c.BITS / 8;
+  z.codes = BH * z.head_codes;
+  z.s = z.c = BH * D * 4;
+  z.ek = z.eu = BH * z.NE * D * 4;
+  z.eg = BH * z.NE * (c.KDA ? D : 1) * 4;
+  z.blen = BH * 4;
+  z.act_qk = z.act_v = BH * D * (c.BF16 ? 2 : 4);
+  z.g = BH * (c.KDA ? D : 1) * 4;
+  z.beta = BH * 4;
+  z.o = BH * D * 4;
+  return z;
+}
+
+// ---------------------------------------------------------------- decode step
+void decode_step(const Cfg& c) {
+  const Sizes z = sizes(c);
+  const int D = c.D, BITS = c.BITS, KDA = c.KDA;
+  // StepShape
+  const int NT = D >= 128 ? 128 : 64, NW = NT / 64, RB = D / 16, RBW = RB / NW, KB = (D + 63) / 64;
+  const int CPL = D / 16, NG = NT / 16, NQ = D / 4, EP = NT / NQ, PRE = 24, KPF = PRE / NG, PFE = PRE / EP;
+  const int CB = D * (BITS == 6 ? 4 : BITS) / 8;
+  const int MAX_ROWS = MODEL_KAPPA_ROWS;
+  const long long act = c.BF16 ? 2 : 4;
+  const long long bh = c.bh, hD = bh * D;
+  const int NE = c.r + c.w_max, E = c.r + c.n;  // the kernel's own row count
+  // descriptors: base offset inside the allocation and size
+  const long long ek0 = bh * NE * D * 4, eu0 = ek0, eg0 = bh * NE * (KDA ? D : 1) * 4;
+  const long long rk_size = (long long)E * D * 4, rg_size = (long long)E * (KDA ? D : 1) * 4;
+  const long long rc0 = bh * z.head_codes, rc_size = z.head_codes;
+  in(c, "codes descriptor", rc0, rc_size, 0, z.codes, -1);
+  in(c, "entry-key descriptor", ek0, rk_size, 0, z.ek, -1);
+  in(c, "entry-value descriptor", eu0, rk_size, 0, z.eu, -1);
+  in(c, "entry-G descriptor", eg0, rg_size, 0, z.eg, -1);
+  in(c, "length load", bh * 4, 4, 0, z.blen, -1);
+  for (int t = 0; t < NT; ++t) {
+    const int lane = t & 63, wave = t >> 6;
+    const bool chan = NT == D || t < D;
+    const int tc = chan ? t : 0;
+    // load_early / load: codes in MFMA operand order
+    for (int rb = 0; rb < RBW; ++rb)
+      for (int kb = 0; kb < KB; ++kb) {
+        const int jl = lane & 15, il = 16 * (lane >> 4);
+        const int j = 16 * (wave * RBW + rb) + jl, i = 64 * kb + il;
+        if (D >= 64 || i < D) {
+          const long long off = (long long)j * CB + (BITS == 8 ? i : i / 2);
+          const long long bytes = BITS == 8 ? 16 : 8;
+          // every code load returns data: inside the head's (hi-plane) bytes
+          in(c, "code load", off, bytes, 0, BITS == 6 ? (long long)D * D / 2 : rc_size, t);
+        }
+      }
+    if (BITS == 6) {
+      const int NJ = D / 16;
+      for (int kb = 0; kb < KB; ++kb) {
+        const int g = 4 * kb + (lane >> 4);
+        if (D >= 64 || 16 * g < D) {
+          const long long off = (long long)D * D / 2 + 4LL * (((lane & 15) * NJ + g) * NJ + wave * RBW);
+          in(c, "6-bit low plane load", off, RBW == 4 ? 16 : 8, (long long)D * D / 2, rc_size, t);
+        }
+      }
+    }
+    in(c, "k/q load", (hD + tc) * act, act, 0, z.act_qk, t);
+    in(c, "v load", (hD + tc) * act, act, 0, z.act_v, t);
+    in(c, "s load", (hD + tc) * 4, 4, 0, z.s, t);
+    in(c, "c load", (hD + tc) * 4, 4, 0, z.c, t);
+    in(c, "g load", KDA ? (hD + tc) * 4 : bh * 4, 4, 0, z.g, t);
+    in(c, "beta load", bh * 4, 4, 0, z.beta, t);
+    // entries: rows e < E hold data and must be inside the descriptor
+    const int grp = t / 16, li = t % 16, i0 = li * CPL, q4 = t % NQ, ph = t / NQ;
+    for (int k = 0; k < KPF; ++k) {
+      const int e = grp + NG * k;
+      if (e < E) {
+        in(c, "entry key row", (long long)(e * D + i0) * 4, CPL * 4, 0, rk_size, t);
+        if (KDA) in(c, "entry G row", (long long)(e * D + i0) * 4, CPL * 4, 0, rg_size, t);
+        else in(c, "entry G", (long long)e * 4, 4, 0, rg_size, t);
+      }
+    }
+    for (int k = 0; k < PFE; ++k) {
+      const int e = ph + EP * k;
+      if (e < E) in(c, "entry value row", (long long)(e * D + 4 * q4) * 4, 16, 0, rk_size, t);
+    }
+    if (E > 0) {  // G of the last entry, plain pointer into the head's entry block
+      if (KDA) in(c, "last G", eg0 + (long long)((E - 1) * D + tc) * 4, 4, eg0, eg0 + (long long)NE * D * 4, t);
+      else in(c, "last G", eg0 + (long long)(E - 1) * 4, 4, eg0, eg0 + (long long)NE * 4, t);
+    }
+    // compute: LDS indices
+    if (chan) {
+      in(c, "lds x", t, 1, 0, D, t);
+      const int kbl = t >> 6, pos = (t & 48) | (BITS == 8 ? (t & 15) : ((t & 1) ? 8 + ((t & 15) >> 1) : ((t & 15) >> 1)));
+      in(c, "lds limb block", kbl, 1, 0, KB, t);
+      in(c, "lds limb position", pos, 1, 0, 64, t);
+    }
+    // key-side dots: every pass of the row groups
+    int e0 = 0;
+    do {
+      for (int k = 0; k < KPF; ++k) {
+        const int e = e0 + grp + NG * k;
+        if (e >= E && e0 + NG * k > 0) {
+          in(c, "lds kappa (zero row)", e, 1, 0, MAX_ROWS, t);
+          continue;
+        }
+        in(c, "lds kappa", e, 1, 0, MAX_ROWS, t);
+        if (e0 > 0) {  // rows past the prefetch, loaded in the pass
+          in(c, "entry key row (pass)", (long long)(e * D + i0) * 4, CPL * 4, 0, rk_size, t);
+          if (KDA) in(c, "entry G row (pass)", (long long)(e * D + i0) * 4, CPL * 4, 0, rg_size, t);
+          else in(c, "entry G (pass)", (long long)e * 4, 4, 0, rg_size, t);
+        }
+      }
+      e0 += NG * KPF;
+    } while (e0 < E);
+    for (int k = 0; k < PFE; ++k) {
+      const int e = ph + EP * k;
+      if (e >= E && k > 0) continue;
+      in(c, "lds kappa read", e, 1, 0, MAX_ROWS, t);
+    }
+    for (int e = ph + EP * PFE; e < E; e += EP) {
+      in(c, "entry value row (loop)", (long long)(e * D + 4 * q4) * 4, 16, 0, rk_size, t);
+      in(c, "lds kappa read (loop)", e, 1, 0, MAX_ROWS, t);
+    }
+    in(c, "lds value partials", (long long)ph * 2 * D + 4 * q4, 4, 0, (long long)EP * 2 * D, t);
+    in(c, "lds limb operand row", lane & 15, 1, 0, 16, t);
+    for (int rb = 0; rb < RBW; ++rb) {
+      if ((lane >> 4) < 2) in(c, "lds readout", 16 * (wave * RBW + rb) + (lane & 15), 1, 0, D, t);
+    }
+    // stores
+    if (chan) {
+      in(c, "o store", (hD + t) * 4, 4, 0, z.o, t);
+      in(c, "appended value", eu0 + (long long)(E * D + t) * 4, 4, eu0, eu0 + (long long)NE * D * 4, t);
+      in(c, "appended key", ek0 + (long long)(E * D + t) * 4, 4, ek0, ek0 + (long long)NE * D * 4, t);
+      if (KDA) in(c, "appended G", eg0 + (long long)(E * D + t) * 4, 4, eg0, eg0 + (long long)NE * D * 4, t);
+      if (t == 0) {
+        if (!KDA) in(c, "appended G", eg0 + (long long)E * 4, 4, eg0, eg0 + (long long)NE * 4, t);
+        in(c, "length store", bh * 4, 4, 0, z.blen, t);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- window close / encode
+void close_kernel(const Cfg& c, bool dense, bool warm) {
+  const Sizes z = sizes(c);
+  const int D = c.D, BITS = c.BITS, KDA = c.KDA, NT = 128;
+  const int RB = D / 8, CB = D / 16, CH = 16, V4 = D / 4, PER = CH * V4 / NT;
+  const long long bh = c.bh, hD = bh * D, erow = bh * (long long)(c.r + c.w_max);
+  const int n = c.n, E = c.r + n, r = c.r;
+  const long long HB = (long long)D * D * BITS / 8;
+  for (int t = 0; t < NT; ++t) {
+    const int tj = t & 15, ti = t >> 4, lane = t & 63, wave = t >> 6;
+    const int i0 = ti * RB, j0 = tj * CB;
+    if (dense) {
+      for (int bb = 0; bb < CB; ++bb) in(c, "dense state load", ((hD + j0 + bb) * D + i0) * 4, RB * 4, 0, (long long)c.BH * D * D * 4, t);
+    } else {
+      in(c, "s load", (hD + i0) * 4, RB * 4, 0, z.s, t);
+      in(c, "c load", (hD + j0) * 4, CB * 4, 0, z.c, t);
+      if (E > 0) {
+        if (KDA) in(c, "last G row", ((erow + E - 1) * D + i0) * 4, RB * 4, 0, z.eg, t);
+        else in(c, "last G", (erow + E - 1) * 4, 4, 0, z.eg, t);
+      }
+      for (int bb = 0; bb < CB; ++bb) {
+        const long long head = bh * HB;
+        if (BITS == 6) {
+          in(c, "6-bit hi codes", head + (long long)(j0 + bb) * (D / 2) + i0 / 2, RB / 2, head, head + (long long)D * D / 2, t);
+          const int NJ = D / 16, j = j0 + bb, g = i0 / 16;
+          const long long w = (long long)D * D / 2 + 4LL * (((j & 15) * NJ + g) * NJ + (j >> 4));
+          in(c, "6-bit lo word", head + w, 4, head + (long long)D * D / 2, head + HB, t);
+        } else {
+          in(c, "codes", head + (long long)(j0 + bb) * (D * BITS / 8) + i0 * BITS / 8, RB * BITS / 8, head, head + HB, t);
+        }
+      }
+      const int c4 = t % V4;
+      if (KDA && E > 0) in(c, "last G quad", ((erow + E - 1) * D + 4 * c4) * 4, 16, 0, z.eg, t);
+      for (int m0 = 0; m0 < E; m0 += CH) {
+        const int cnt = E - m0 < CH ? E - m0 : CH;
+        for (int p = 0; p < PER; ++p) {
+          const int row = (t + NT * p) / V4;
+          in(c, "lds staged row", row, 1, 0, CH, t);
+          if (row < cnt) {
+            const long long g = ((erow + m0 + row) * D + 4 * c4) * 4;
+            in(c, "staged key", g, 16, 0, z.ek, t);
+            in(c, "staged value", g, 16, 0, z.eu, t);
+            if (KDA) in(c, "staged G", g, 16, 0, z.eg, t);
+            else in(c, "staged G", (erow + m0 + row) * 4, 4, 0, z.eg, t);
+          }
+        }
+        const int nkb = (cnt + 3) >> 2;
+        for (int kb = 0; kb < nkb; ++kb) {
+          const int e = 4 * kb + (lane >> 4);
+          in(c, "lds operand entry", e, 1, 0, CH, t);
+          const int a_row = wave * 4 * RB + RB * ((lane & 15) >> 2) + (lane & 3);
+          for (int q = 0; q < RB / 4; ++q) in(c, "lds key operand", a_row + 4 * q, 1, 0, D, t);
+          in(c, "lds value operand", CB * (lane & 15), CB, 0, D, t);
+        }
+      }
+    }
+    for (int l = 0; l < r; ++l) {
+      if (!dense && warm) in(c, "warm start value", ((erow + l) * D + j0) * 4, CB * 4, 0, z.eu, t);
+      const int g = lane >> 4;
+      if (CB == 8) in(c, "lds column partials", j0 + 2 * g, 2, 0, D, t);
+      else if (CB == 4) in(c, "lds column partials", j0 + g, 1, 0, D, t);
+      else in(c, "lds column partials", j0 + (g >> 1), 1, 0, D, t);
+      for (int bb = 0; bb < CB; ++bb) in(c, "lds column read", j0 + bb, 1, 0, D, t);
+      if (tj == 0) in(c, "compensator key store", ((erow + l) * D + i0) * 4, RB * 4, 0, z.ek, t);
+      if (ti == 0) in(c, "compensator value store", ((erow + l) * D + j0) * 4, CB * 4, 0, z.eu, t);
+      if (KDA && tj == 0) in(c, "compensator G store", ((erow + l) * D + i0) * 4, RB * 4, 0, z.eg, t);
+      if (!KDA && t == 0) in(c, "compensator G store", (erow + l) * 4, 4, 0, z.eg, t);
+    }
+    for (int bb = 0; bb < CB; ++bb) in(c, "residual export", ((hD + j0 + bb) * D + i0) * 4, RB * 4, 0, (long long)c.BH * D * D * 4, t);
+    const int NV = CB >= 4 ? CB / 4 : 1;
+    if (CB >= 4) {
+      const int jg = j0 + (lane >> 4) * NV;
+      in(c, "lds column maxima", jg, NV, 0, D, t);
+    } else {
+      for (int bb = 0; bb < CB; ++bb) in(c, "lds column maxima", j0 + bb, 1, 0, D, t);
+    }
+    const long long head = bh * HB;
+    for (int bb = 0; bb < CB; ++bb) {
+      const int j = j0 + bb;
+      if (BITS == 6) {
+        in(c, "6-bit hi code store", head + (long long)j * (D / 2) + i0 / 2, RB / 2, head, head + (long long)D * D / 2, t);
+        const int NJ = D / 16;
+        const long long w = (long long)D * D / 2 + 4LL * (((j & 15) * NJ + i0 / 16) * NJ + (j >> 4));
+        if (ti % (16 / RB) == 0) in(c, "6-bit lo word store", head + w, 4, head + (long long)D * D / 2, head + HB, t);
+      } else {
+        in(c, "code store", head + (long long)j * (D * BITS / 8) + i0 * BITS / 8, RB * BITS / 8, head, head + HB, t);
+      }
+    }
+    if (RB == 16) in(c, "row scale store", (hD + i0 + tj) * 4, 4, 0, z.s, t);
+    else if (tj == 0) in(c, "row scale store", (hD + i0) * 4, RB * 4, 0, z.s, t);
+    if (CB >= 4) {
+      if (wave == 0)
+        for (int m = 0; m < NV; ++m) in(c, "column scale store", (hD + j0 + (lane >> 4) * NV + m) * 4, 4, 0, z.c, t);
+    } else if (ti == 0) {
+      in(c, "column scale store", (hD + j0) * 4, CB * 4, 0, z.c, t);
+    }
+    if (t == 0) in(c, "length store", bh * 4, 4, 0, z.blen, t);
+  }
+}
+
+}  // namespace
+
+int main() {
+  const int dims[] = {32, 64, 128}, bits[] = {8, 6, 4};
+  const int wmaxes[] = {1, 2, 3, 4, 7, 8, 15, 16, 17, 20, 23, 24, 25, 31, 32, 33, 47, 48, 49, 63, 64};
+  const int BH = 3;
+  long long configs = 0;
+  for (int D : dims)
+    for (int BITS : bits)
+      for (int KDA = 0; KDA < 2; ++KDA)
+        for (int r = 0; r <= 8; ++r)
+          for (int w_max : wmaxes)
+            for (int bh = 0; bh < BH; bh += BH - 1) {
+              for (int BF16 = 0; BF16 < 2; ++BF16)
+                for (int n = 0; n < w_max; ++n) {  // decode: buf_len < w_max
+                  decode_step(Cfg{D, BITS, KDA, BF16, r, w_max, n, bh, BH});
+                  ++configs;
+                }
+              for (int n = 0; n <= w_max; ++n)  // close: buf_len <= w_max
+                for (int warm = 0; warm < 2; ++warm) {
+                  close_kernel(Cfg{D, BITS, KDA, 0, r, w_max, n, bh, BH}, false, warm);
+                  ++configs;
+                }
+              close_kernel(Cfg{D, BITS, KDA, 0, r, w_max, 0, bh, BH}, true, false);  // encode
+              ++configs;
+            }
+  std::printf("bounds model: %lld launch configurations, %lld access checks, all inside their buffers\n", configs,
+              checks);
+  return 0;
+}
