@@ -108,7 +108,8 @@ typedef struct lq_state {
   float* ent_k;      /* [B*H][r + w_max][d_k] entry keys (compensator keys are unit vectors) */
   float* ent_u;      /* [B*H][r + w_max][d_v] entry values u_e */
   float* ent_g;      /* [B*H][r + w_max] (GDN) or [B*H][r + w_max][d_k] (KDA): G_e, the
-                        cumulative log-decay since the window start (0 for compensators) */
+                        cumulative log-decay since the window start (0 for compensators;
+                        the KDA kernels take that value and do not read those rows) */
   int32_t* buf_len;  /* [B*H] buffered tokens n per head */
   int32_t* err;      /* [1] device error word (LQ_DEVERR_* bits), may be NULL */
 } lq_state;

@@ -47,21 +47,11 @@ __device__ __forceinline__ void loadN(const float* p, float (&x)[N]) {
   }
 }
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
 // Cache policies of the state loads: the codes (the bulk of the state, read
 // once per step) stream with the non-temporal hint; the entry rows keep the
 // default policy (the non-temporal hint measured slower for them).
 constexpr int CODES_POLICY = 2;
 constexpr int ENTRY_POLICY = 0;
-
-// Raw buffer resource over [base, base + bytes): a load at or past `bytes`
-// returns zeros and moves no data (gfx9 descriptor word 3: 32-bit data format).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
-}
 
 // N consecutive fp32 values (N in 2, 4, 8) at byte offset off of a buffer.
 template <int N>
@@ -213,6 +203,19 @@ struct HeadStep {
     float *ek, *eu, *eg;
   };
 
+  // KDA: the G rows are read only for the n buffered entries. Compensators sit
+  // at window position 0 (G_e = 0), so the G buffer starts at entry r and a
+  // compensator row's offset lies past its end: it reads as zeros and moves
+  // no data.
+  __device__ static __forceinline__ __amdgpu_buffer_rsrc_t g_rsrc(const StepArgs& a, const Ptr& P, int n) {
+    if constexpr (KDA) return buf_rsrc(P.eg + a.r * D, uint32_t(n) * D * 4);
+    else return buf_rsrc(P.eg, uint32_t(a.r + n) * 4);
+  }
+  __device__ static __forceinline__ uint32_t g_off(const StepArgs& a, int e, int i0) {
+    if constexpr (KDA) return e >= a.r ? uint32_t((e - a.r) * D + i0) * 4 : 0x80000000u;
+    else return uint32_t(e) * 4;
+  }
+
   __device__ static __forceinline__ Ptr ptr(const StepArgs& a, int bh) {
     const int NE = a.r + a.w_max;
     return Ptr{size_t(bh) * D, a.ek + size_t(bh) * NE * D, a.eu + size_t(bh) * NE * D,
@@ -261,18 +264,18 @@ struct HeadStep {
     // last entry read as zeros and cost no memory traffic.
     const int E = a.r + n;
     const auto rk = buf_rsrc(P.ek, uint32_t(E) * D * 4), ru = buf_rsrc(P.eu, uint32_t(E) * D * 4);
-    const auto rg = buf_rsrc(P.eg, uint32_t(E) * (KDA ? D : 1) * 4);
+    const auto rg = g_rsrc(a, P, n);
 #pragma unroll
     for (int k = 0; k < KPF; ++k) {
       const int e = grp + NG * k;
       buf_loadN(rk, uint32_t(e * D + i0) * 4, h.kr[k]);
-      if constexpr (KDA) buf_loadN(rg, uint32_t(e * D + i0) * 4, h.gr[k]);  // zero rows for compensators
-      else h.Gm[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, uint32_t(e) * 4, 0, ENTRY_POLICY));
+      if constexpr (KDA) buf_loadN(rg, g_off(a, e, i0), h.gr[k]);  // zero rows for compensators
+      else h.Gm[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, g_off(a, e, 0), 0, ENTRY_POLICY));
     }
 #pragma unroll
     for (int k = 0; k < PFE; ++k) h.uv[k] = buf_load4(ru, uint32_t((ph + EP * k) * D + 4 * q4) * 4);
-    // G_{t-1}: G of the last entry (compensators carry 0), 0 with no entries
-    if constexpr (KDA) h.Gp = E > 0 ? P.eg[(E - 1) * D + tc] : 0.f;
+    // G_{t-1}: G of the last entry; 0 with no buffered token (compensators carry 0)
+    if constexpr (KDA) h.Gp = n > 0 ? P.eg[(E - 1) * D + tc] : 0.f;
     else h.Gp = E > 0 ? P.eg[E - 1] : 0.f;
     // The second half of the codes is issued last: loads complete in issue
     // order, so the entry arithmetic can start while those codes stream in.
@@ -404,7 +407,7 @@ struct HeadStep {
         for (int x = 0; x < CPL; ++x) Gt[x] *= L2E;
       }
       const auto rk = buf_rsrc(P.ek, uint32_t(E) * D * 4);
-      const auto rg = buf_rsrc(P.eg, uint32_t(E) * (KDA ? D : 1) * 4);
+      const auto rg = g_rsrc(a, P, n);
       int e0 = 0;
       do {  // at least one pass, so that kappa of the prefetched rows is always written
 #pragma unroll
@@ -424,8 +427,8 @@ struct HeadStep {
             }
           } else {  // entries beyond the prefetched ones (long windows)
             buf_loadN(rk, uint32_t(e * D + i0) * 4, row);
-            if constexpr (KDA) buf_loadN(rg, uint32_t(e * D + i0) * 4, gm);
-            else gsc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, uint32_t(e) * 4, 0, ENTRY_POLICY));
+            if constexpr (KDA) buf_loadN(rg, g_off(a, e, i0), gm);
+            else gsc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, g_off(a, e, 0), 0, ENTRY_POLICY));
           }
           float dk = 0.f, dq = 0.f;
 #pragma unroll

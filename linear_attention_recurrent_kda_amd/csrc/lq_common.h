@@ -11,6 +11,16 @@ namespace lq {
 __device__ __forceinline__ float as_f(uint32_t x) { return __uint_as_float(x); }
 __device__ __forceinline__ uint32_t as_u(float x) { return __float_as_uint(x); }
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): a load at or past `bytes`
+// returns zeros and moves no data (gfx9 descriptor word 3: 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
 // DPP lane permutations inside a 16-lane row (gfx9 encodings).
 enum : int {
   DPP_QUAD_XOR1 = 0xB1,    // quad_perm [1,0,3,2]

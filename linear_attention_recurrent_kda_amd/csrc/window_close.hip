@@ -87,20 +87,6 @@ __device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t (&w)[(NB 
   else *reinterpret_cast<uint16_t*>(p) = uint16_t(w[0]);
 }
 
-// N codes of one value column (consecutive key channels) at p -> signed ints.
-// 8 bits: one byte each; 4 bits: two's-complement nibbles, even channel low.
-template <int N, int BITS>
-__device__ __forceinline__ void load_codes(const uint8_t* p, int (&c)[N]) {
-  constexpr int NB = N * BITS / 8;
-  uint32_t w[(NB + 3) / 4];
-  load_bytes<NB>(p, w);
-#pragma unroll
-  for (int a = 0; a < N; ++a) {
-    if constexpr (BITS == 8) c[a] = int(int8_t(uint8_t(w[a / 4] >> (8 * (a % 4)))));
-    else c[a] = int(((w[a / 8] >> (4 * (a % 8))) & 0xFu) ^ 0x8u) - 8;
-  }
-}
-
 template <int N, int BITS>
 __device__ __forceinline__ void store_codes(uint8_t* p, const int (&c)[N]) {
   constexpr int NB = N * BITS / 8;
@@ -131,15 +117,39 @@ __device__ __forceinline__ size_t lo_word(int j, int g) {
   return size_t(D * D / 2) + 4 * size_t(((j & 15) * NJ + g) * NJ + (j >> 4));
 }
 
-// N codes of value column j, key channels i0..i0+N-1 (i0 % N == 0, N <= 16).
-template <int N, int D>
-__device__ __forceinline__ void load_codes6(const uint8_t* head, int j, int i0, int (&c)[N]) {
-  int hi[N];
-  load_codes<N, 4>(head + size_t(j) * (D / 2) + i0 / 2, hi);
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(head + lo_word<D>(j, i0 / 16));
+// The codes of N consecutive key channels i0.. of value column j (i0 % N == 0,
+// N <= 16) as loaded words, unpacked to signed ints later: 8 bits one byte
+// each; 4 bits two's-complement nibbles, even channel low; 6 bits the hi
+// nibbles plus the 16-channel group's low-bit word.
+template <int N, int BITS, int D>
+struct CodeWords {
+  static constexpr int NB = N * (BITS == 6 ? 4 : BITS) / 8;  // bytes of the (hi) plane
+  uint32_t w[(NB + 3) / 4];
+  uint32_t lo;
+
+  __device__ __forceinline__ void load(const uint8_t* head, int j, int i0) {
+    if constexpr (BITS == 6) {
+      load_bytes<NB>(head + size_t(j) * (D / 2) + i0 / 2, w);
+      lo = *reinterpret_cast<const uint32_t*>(head + lo_word<D>(j, i0 / 16));
+    } else {
+      load_bytes<NB>(head + size_t(j) * (D * BITS / 8) + i0 * BITS / 8, w);
+      lo = 0u;
+    }
+  }
+
+  __device__ __forceinline__ void unpack(int i0, int (&c)[N]) const {
 #pragma unroll
-  for (int a = 0; a < N; ++a) c[a] = 4 * hi[a] + int((w >> lo_bit((i0 + a) & 15)) & 3u);
-}
+    for (int a = 0; a < N; ++a) {
+      if constexpr (BITS == 8) {
+        c[a] = int(int8_t(uint8_t(w[a / 4] >> (8 * (a % 4)))));
+      } else {
+        const int hi = int(((w[a / 8] >> (4 * (a % 8))) & 0xFu) ^ 0x8u) - 8;
+        if constexpr (BITS == 6) c[a] = 4 * hi + int((lo >> lo_bit((i0 + a) & 15)) & 3u);
+        else c[a] = hi;
+      }
+    }
+  }
+};
 
 __device__ __forceinline__ uint32_t or_swap16(uint32_t x) {  // x | x of lane ^ 16
   auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
@@ -161,14 +171,16 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   constexpr int CB = D / 16;  // value columns per thread
   constexpr int Q = (1 << (BITS - 1)) - 1;  // 127, 31 or 7
   constexpr int HB = D * D * BITS / 8;      // code bytes per head
-  constexpr int CH = 16;                    // entries staged in LDS per fold pass
+  constexpr int CH0 = 32;                   // entries staged in LDS by the first fold pass
+  constexpr int CH1 = 16;                   // ... by each later pass (windows past CH0 entries)
   constexpr int V4 = D / 4;                 // float4 per entry row
-  constexpr int PER = CH * V4 / NT;         // float4 per thread per staged array
-  static_assert(NT % V4 == 0 && PER >= 1 && PER * NT == CH * V4, "staging shape");
-  __shared__ float sh_n[2][2];                // per-wave squared norms (double-buffered)
+  constexpr int PER0 = CH0 * V4 / NT;       // float4 per thread per staged array, first pass
+  constexpr int PER1 = CH1 * V4 / NT;       // ... later passes
+  static_assert(NT % V4 == 0 && PER1 >= 1 && PER1 * NT == CH1 * V4 && PER0 == 2 * PER1, "staging shape");
+  __shared__ float sh_n[2];                   // per-wave squared norms of the final kappa
   __shared__ __align__(16) float sh_c[2][2][D];  // per-wave column partials (double-buffered)
-  __shared__ __align__(16) float sh_k[DENSE ? 1 : CH][D];  // keys scaled by their decay to the window end
-  __shared__ __align__(16) float sh_u[DENSE ? 1 : CH][D];
+  __shared__ __align__(16) float sh_k[DENSE ? 1 : CH0][D];  // keys scaled by their decay to the window end
+  __shared__ __align__(16) float sh_u[DENSE ? 1 : CH0][D];
 
   const int t = threadIdx.x, tj = t & 15, ti = t >> 4, lane = t & 63, wave = t >> 6;
   const int H = a.heads;
@@ -208,36 +220,91 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       return;
     }
     const int E = r + n;
+    // Every load of the fold is issued before the first of them is used, so
+    // that a head waits for memory once: this thread's code words, its scales,
+    // G_n, and the first CH0 entry rows (all of them when r + n <= CH0).
+    const uint8_t* cb = static_cast<const uint8_t*>(a.codes) + size_t(bh) * HB;
+    CodeWords<RB, BITS, D> cw[CB];
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) cw[bb].load(cb, j0 + bb, i0);
     float si[RB], cj[CB], Gn[KDA ? RB : 1];
     loadB<RB>(a.s + hD + i0, si);
     loadB<CB>(a.c + hD + j0, cj);
-    if constexpr (KDA) {
-      if (E > 0) loadB<RB>(a.eg + (erow + E - 1) * D + i0, Gn);
+    if constexpr (KDA) {  // (compensator G rows are 0 by definition and not read)
+      if (n > 0) loadB<RB>(a.eg + (erow + E - 1) * D + i0, Gn);
       else
 #pragma unroll
         for (int x = 0; x < RB; ++x) Gn[x] = 0.f;
     } else {
       Gn[0] = E > 0 ? a.eg[erow + E - 1] : 0.f;
     }
-    const uint8_t* cb = static_cast<const uint8_t*>(a.codes) + size_t(bh) * HB;
-#pragma unroll
-    for (int x = 0; x < RB; ++x) si[x] *= expf(KDA ? Gn[x] : Gn[0]);  // the residual's decay to the window end
-#pragma unroll
-    for (int bb = 0; bb < CB; ++bb) {
-      int code[RB];
-      if constexpr (BITS == 6) load_codes6<RB, D>(cb, j0 + bb, i0, code);
-      else load_codes<RB, BITS>(cb + size_t(j0 + bb) * (D * BITS / 8) + i0 * BITS / 8, code);
-#pragma unroll
-      for (int x = 0; x < RB; ++x) M[x >> 2][bb][x & 3] = (si[x] * float(code[x])) * cj[bb];
-    }
-    // entries, CH at a time: the workgroup stages the rows in LDS with one
-    // round of loads, each key already multiplied by its decay to the window
-    // end; then every thread applies them to its block. A thread stages the
-    // same four key channels of every row it loads (NT is a multiple of V4).
+    // Entry rows go through LDS, each key multiplied by its decay to the
+    // window end; every thread then applies them to its block. A thread
+    // stages the same four key channels of every row it loads (NT is a
+    // multiple of V4). The loads are range-checked buffer loads over this
+    // head's E rows: rows at or past E read as zeros, and (KDA) a
+    // compensator's G row is addressed past the end of the G range, which
+    // starts at entry r.
     const int c4 = t % V4;
     float4 gq = make_float4(0.f, 0.f, 0.f, 0.f);  // KDA: G_n of the staged channels
     if constexpr (KDA) {
-      if (E > 0) gq = *reinterpret_cast<const float4*>(a.eg + (erow + E - 1) * D + 4 * c4);
+      if (n > 0) gq = *reinterpret_cast<const float4*>(a.eg + (erow + E - 1) * D + 4 * c4);
+    }
+    const auto rk = buf_rsrc(a.ek + erow * D, uint32_t(E) * D * 4);
+    const auto ru = buf_rsrc(a.eu + erow * D, uint32_t(E) * D * 4);
+    const auto rg = KDA ? buf_rsrc(a.eg + (erow + r) * D, uint32_t(n) * D * 4) : buf_rsrc(a.eg + erow, uint32_t(E) * 4);
+    auto ld4 = [](__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+      const v4u q = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      return make_float4(as_f(q[0]), as_f(q[1]), as_f(q[2]), as_f(q[3]));
+    };
+    // rows m0 .. m0 + NP * NT / V4 - 1: loads, then (decay, LDS) once they are in
+    float4 kq[PER0], uq[PER0], ge[KDA ? PER0 : 1];
+    float gs[PER0];
+    auto stage_load = [&](auto np, int m0) {
+      constexpr int NP = decltype(np)::value;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int e = m0 + (t + NT * p) / V4;
+        const uint32_t off = uint32_t(e * D + 4 * c4) * 4;
+        kq[p] = ld4(rk, off);
+        uq[p] = ld4(ru, off);
+        if constexpr (KDA) ge[p] = ld4(rg, e >= r ? uint32_t((e - r) * D + 4 * c4) * 4 : 0x80000000u);
+        else gs[p] = as_f(__builtin_amdgcn_raw_buffer_load_b32(rg, uint32_t(e) * 4, 0, 0));
+      }
+    };
+    auto stage_store = [&](auto np, int m0) {
+      constexpr int NP = decltype(np)::value;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int row = (t + NT * p) / V4;
+        const bool in = m0 + row < E;  // rows past E: zeros (no decay factor, which could overflow)
+        float4 k4 = kq[p];
+        if constexpr (KDA) {
+          k4.x *= in ? expf(gq.x - ge[p].x) : 0.f;
+          k4.y *= in ? expf(gq.y - ge[p].y) : 0.f;
+          k4.z *= in ? expf(gq.z - ge[p].z) : 0.f;
+          k4.w *= in ? expf(gq.w - ge[p].w) : 0.f;
+        } else {
+          const float f = in ? expf(Gn[0] - gs[p]) : 0.f;
+          k4.x *= f, k4.y *= f, k4.z *= f, k4.w *= f;
+        }
+        reinterpret_cast<float4*>(&sh_k[row][0])[c4] = k4;
+        reinterpret_cast<float4*>(&sh_u[row][0])[c4] = uq[p];
+      }
+    };
+    stage_load(std::integral_constant<int, PER0>{}, 0);
+    // the first pass's rows go to LDS before the residual is built, which
+    // frees their registers for it
+    stage_store(std::integral_constant<int, PER0>{}, 0);
+    // the residual M = diag(s exp(G_n)) C diag(c), decayed to the window end
+#pragma unroll
+    for (int x = 0; x < RB; ++x) si[x] *= expf(KDA ? Gn[x] : Gn[0]);
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) {
+      int code[RB];
+      cw[bb].unpack(i0, code);
+#pragma unroll
+      for (int x = 0; x < RB; ++x) M[x >> 2][bb][x & 3] = (si[x] * float(code[x])) * cj[bb];
     }
     // The rank-CH update M += K^T U of a pass runs on the matrix cores
     // (v_mfma_f32_16x16x4f32, four entries per instruction). Its 16 x 16
@@ -248,33 +315,11 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     const int e_of_lane = lane >> 4;  // the operands' entry within a block of four
     const int a_row = wave * 4 * RB + RB * ((lane & 15) >> 2) + (lane & 3);  // + 4 a
     const int b_col = CB * (lane & 15);                                      // + bb
-    for (int m0 = 0; m0 < E; m0 += CH) {
-      const int cnt = min(CH, E - m0);
-      __syncthreads();  // the previous pass has consumed the staged rows
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int row = (t + NT * p) / V4;  // covers all CH rows; rows past cnt are zeros
-        float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), uq = kq;
-        if (row < cnt) {
-          const size_t g = (erow + m0 + row) * D + 4 * c4;
-          kq = *reinterpret_cast<const float4*>(a.ek + g);
-          uq = *reinterpret_cast<const float4*>(a.eu + g);
-          if constexpr (KDA) {
-            const float4 ge = *reinterpret_cast<const float4*>(a.eg + g);
-            kq.x *= expf(gq.x - ge.x);
-            kq.y *= expf(gq.y - ge.y);
-            kq.z *= expf(gq.z - ge.z);
-            kq.w *= expf(gq.w - ge.w);
-          } else {
-            const float f = expf(Gn[0] - a.eg[erow + m0 + row]);
-            kq.x *= f, kq.y *= f, kq.z *= f, kq.w *= f;
-          }
-        }
-        reinterpret_cast<float4*>(&sh_k[row][0])[c4] = kq;
-        reinterpret_cast<float4*>(&sh_u[row][0])[c4] = uq;
-      }
-      __syncthreads();
-      const int nkb = (cnt + 3) >> 2;
+    int m0 = 0;
+    while (true) {
+      const int cnt = min(m0 == 0 ? CH0 : CH1, E - m0);
+      __syncthreads();  // the staged rows are in LDS
+      const int nkb = (cnt + 3) >> 2;  // rows from cnt up to 4 nkb are zeros
       for (int kb = 0; kb < nkb; ++kb) {
         const int e = 4 * kb + e_of_lane;
         float ka[RB / 4], ub[CB];
@@ -286,13 +331,23 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
 #pragma unroll
           for (int bb = 0; bb < CB; ++bb) M[q][bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[q], ub[bb], M[q][bb], 0, 0, 0);
       }
+      m0 += m0 == 0 ? CH0 : CH1;
+      if (m0 >= E) break;
+      __syncthreads();  // the pass has consumed the staged rows
+      stage_load(std::integral_constant<int, PER1>{}, m0);
+      stage_store(std::integral_constant<int, PER1>{}, m0);
     }
   }
 
   // ---- compensators: power method with deflation. One barrier per
-  // iteration: kappa = M v is complete inside each 16-lane row; the column
-  // partials of M^T kappa and the squared norm of kappa go to LDS together
-  // (double-buffered, so the next iteration may write while this one is read)
+  // iteration: kappa = M v is complete inside each 16-lane row, and the
+  // column partials of M^T kappa go to LDS (double-buffered, so the next
+  // iteration may write while this one is read). The iteration keeps kappa
+  // and c = M^T kappa unnormalised: v = c / |c| is the same direction as
+  // w / |w| with w = M^T (kappa / |kappa|), and |kappa| is only needed once,
+  // after the last iteration, for the unit key k and its value w = c / |kappa|.
+  // kappa = 0 exactly when c = 0 (|kappa|^2 = v . c), so |c|^2 zero or not
+  // finite flags a degenerate head.
   bool live = true;
   int par = 0;
   for (int l = 0; l < r; ++l) {
@@ -323,20 +378,16 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       const float inv_nv = __builtin_amdgcn_rsqf(p);
 #pragma unroll
       for (int bb = 0; bb < CB; ++bb) v[bb] *= inv_nv;
-      float inv_rk = 0.f;
       for (int it = 0; it < a.T; ++it) {
-        // kappa = M v (sum over value columns: DPP across the 16 tj lanes),
-        // kept in kk; only the last iteration's is scaled to the unit key
-        float pk = 0.f;
+        // kappa = M v (sum over value columns: DPP across the 16 tj lanes)
 #pragma unroll
         for (int x = 0; x < RB; ++x) {
           float s = 0.f;
 #pragma unroll
           for (int bb = 0; bb < CB; ++bb) s = fmaf(M[x >> 2][bb][x & 3], v[bb], s);
           kk[x] = group_sum<16>(s);
-          pk = fmaf(kk[x], kk[x], pk);
         }
-        // M^T kappa (sum over key rows: the wave's four rows, then the two waves)
+        // c = M^T kappa (sum over key rows: the wave's four rows, then the two waves)
         {
           float cs[CB], tot[CB >= 4 ? CB / 4 : 1];
 #pragma unroll
@@ -357,35 +408,46 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
             sh_c[par][wave][j0 + (g >> 1)] = tot[0];  // rows 2m and 2m+1 hold the same total
           }
         }
-        pk = rows_sum(pk);  // the wave's rows; pk was already equal across the 16 tj lanes
-        if (lane == 0) sh_n[par][wave] = pk;
         __syncthreads();
-        const float nk2 = sh_n[par][0] + sh_n[par][1];
-        if (!(nk2 > 0.f) || !isfinite(nk2)) {  // uniform: every thread read the same sums
-          live = false;
-          break;
-        }
-        inv_rk = __builtin_amdgcn_rsqf(nk2);
-        // w = M^T k = (M^T kappa) / |kappa|
-        float pw = 0.f;
+        float pc = 0.f;
 #pragma unroll
         for (int bb = 0; bb < CB; ++bb) {
           const int j = j0 + bb;
-          w[bb] = (sh_c[par][0][j] + sh_c[par][1][j]) * inv_rk;
-          pw = fmaf(w[bb], w[bb], pw);
+          w[bb] = sh_c[par][0][j] + sh_c[par][1][j];  // c, kept for the value
+          pc = fmaf(w[bb], w[bb], pc);
         }
         par ^= 1;
-        pw = group_sum<16>(pw);  // the same total in every row
-        if (!(pw > 0.f) || !isfinite(pw)) {
+        pc = group_sum<16>(pc);  // the same total in every row
+        if (!(pc > 0.f) || !isfinite(pc)) {  // uniform: every thread read the same sums
           live = false;
           break;
         }
-        const float inv_rw = __builtin_amdgcn_rsqf(pw);
+        const float inv_c = __builtin_amdgcn_rsqf(pc);
 #pragma unroll
-        for (int bb = 0; bb < CB; ++bb) v[bb] = w[bb] * inv_rw;
+        for (int bb = 0; bb < CB; ++bb) v[bb] = w[bb] * inv_c;
       }
+      if (live) {
+        // |kappa|^2 of the last iteration: the thread's rows (equal across
+        // the 16 tj lanes), the wave's four rows, then the two waves
+        float pk = 0.f;
 #pragma unroll
-      for (int x = 0; x < RB; ++x) kk[x] *= inv_rk;
+        for (int x = 0; x < RB; ++x) pk = fmaf(kk[x], kk[x], pk);
+        pk = rows_sum(pk);
+        if (lane == 0) sh_n[wave] = pk;
+        __syncthreads();
+        // (the next write of sh_n comes after at least one more iteration
+        // barrier, which both waves reach only after this read)
+        const float nk2 = sh_n[0] + sh_n[1];
+        if (!(nk2 > 0.f) || !isfinite(nk2)) {
+          live = false;
+        } else {
+          const float inv_rk = __builtin_amdgcn_rsqf(nk2);
+#pragma unroll
+          for (int x = 0; x < RB; ++x) kk[x] *= inv_rk;
+#pragma unroll
+          for (int bb = 0; bb < CB; ++bb) w[bb] *= inv_rk;
+        }
+      }
     }
     if (!live) {
 #pragma unroll

@@ -24,6 +24,9 @@
 #ifndef MODEL_KAPPA_ROWS
 #define MODEL_KAPPA_ROWS (8 + 64 + 1)
 #endif
+#ifndef MODEL_G_COMP_OFF  // the decode step's offset for a compensator's G row
+#define MODEL_G_COMP_OFF 0x80000000LL
+#endif
 #ifndef MODEL_ENTRY_SLACK
 #define MODEL_ENTRY_SLACK 0
 #endif
@@ -71,7 +74,35 @@ Sizes sizes(const Cfg& c) {
   return z;
 }
 
+// A range-checked buffer load of `size` bytes at byte offset off of a
+// descriptor over `range` bytes: either wholly inside (it reads memory) or
+// wholly at or past the end (it returns zeros and moves no data), and below
+// 2^32 with the load's size.
+void buffer_load(const Cfg& c, const char* what, long long off, long long size, long long range, int t) {
+  ++checks;
+  if (off + size > (1LL << 32)) fail(c, what, off, 0, 1LL << 32, t);
+  if (off < range && off + size > range) fail(c, what, off, 0, range, t);
+}
+
 // ---------------------------------------------------------------- decode step
+// A G load of entry e < E (the decode step's g_off): GDN one float at 4e;
+// KDA the channels i0.. of row e - r, or, for a compensator row (e < r), an
+// offset past the descriptor's end that stays below 2^32 with the load's
+// 16-byte steps, so the load returns zeros and moves no data.
+void g_row(const Cfg& c, const char* what, int e, int i0, int cpl, long long rg_size, int t) {
+  if (!c.KDA) {
+    in(c, what, (long long)e * 4, 4, 0, rg_size, t);
+    return;
+  }
+  if (e >= c.r) {
+    in(c, what, (long long)((e - c.r) * c.D + i0) * 4, cpl * 4, 0, rg_size, t);
+    return;
+  }
+  const long long off = MODEL_G_COMP_OFF;
+  ++checks;
+  if (off < rg_size || off + cpl * 4 > (1LL << 32)) fail(c, "compensator G offset", off, rg_size, 1LL << 32, t);
+}
+
 void decode_step(const Cfg& c) {
   const Sizes z = sizes(c);
   const int D = c.D, BITS = c.BITS, KDA = c.KDA;
@@ -85,12 +116,16 @@ void decode_step(const Cfg& c) {
   const int NE = c.r + c.w_max, E = c.r + c.n;  // the kernel's own row count
   // descriptors: base offset inside the allocation and size
   const long long ek0 = bh * NE * D * 4, eu0 = ek0, eg0 = bh * NE * (KDA ? D : 1) * 4;
-  const long long rk_size = (long long)E * D * 4, rg_size = (long long)E * (KDA ? D : 1) * 4;
+  const long long rk_size = (long long)E * D * 4;
+  // the G descriptor: KDA starts at entry r and covers the n buffered rows
+  // (compensator rows are addressed past its end and read as zeros)
+  const long long rg0 = KDA ? eg0 + (long long)c.r * D * 4 : eg0;
+  const long long rg_size = KDA ? (long long)c.n * D * 4 : (long long)E * 4;
   const long long rc0 = bh * z.head_codes, rc_size = z.head_codes;
   in(c, "codes descriptor", rc0, rc_size, 0, z.codes, -1);
   in(c, "entry-key descriptor", ek0, rk_size, 0, z.ek, -1);
   in(c, "entry-value descriptor", eu0, rk_size, 0, z.eu, -1);
-  in(c, "entry-G descriptor", eg0, rg_size, 0, z.eg, -1);
+  in(c, "entry-G descriptor", rg0, rg_size, eg0, eg0 + (long long)NE * (KDA ? D : 1) * 4, -1);
   in(c, "length load", bh * 4, 4, 0, z.blen, -1);
   for (int t = 0; t < NT; ++t) {
     const int lane = t & 63, wave = t >> 6;
@@ -130,18 +165,17 @@ void decode_step(const Cfg& c) {
       const int e = grp + NG * k;
       if (e < E) {
         in(c, "entry key row", (long long)(e * D + i0) * 4, CPL * 4, 0, rk_size, t);
-        if (KDA) in(c, "entry G row", (long long)(e * D + i0) * 4, CPL * 4, 0, rg_size, t);
-        else in(c, "entry G", (long long)e * 4, 4, 0, rg_size, t);
+        g_row(c, "entry G row", e, i0, CPL, rg_size, t);
       }
     }
     for (int k = 0; k < PFE; ++k) {
       const int e = ph + EP * k;
       if (e < E) in(c, "entry value row", (long long)(e * D + 4 * q4) * 4, 16, 0, rk_size, t);
     }
-    if (E > 0) {  // G of the last entry, plain pointer into the head's entry block
-      if (KDA) in(c, "last G", eg0 + (long long)((E - 1) * D + tc) * 4, 4, eg0, eg0 + (long long)NE * D * 4, t);
-      else in(c, "last G", eg0 + (long long)(E - 1) * 4, 4, eg0, eg0 + (long long)NE * 4, t);
-    }
+    // G of the last entry, plain pointer into the head's entry block (KDA:
+    // only with a buffered token, compensators carry G = 0)
+    if (KDA && c.n > 0) in(c, "last G", eg0 + (long long)((E - 1) * D + tc) * 4, 4, eg0, eg0 + (long long)NE * D * 4, t);
+    if (!KDA && E > 0) in(c, "last G", eg0 + (long long)(E - 1) * 4, 4, eg0, eg0 + (long long)NE * 4, t);
     // compute: LDS indices
     if (chan) {
       in(c, "lds x", t, 1, 0, D, t);
@@ -161,8 +195,7 @@ void decode_step(const Cfg& c) {
         in(c, "lds kappa", e, 1, 0, MAX_ROWS, t);
         if (e0 > 0) {  // rows past the prefetch, loaded in the pass
           in(c, "entry key row (pass)", (long long)(e * D + i0) * 4, CPL * 4, 0, rk_size, t);
-          if (KDA) in(c, "entry G row (pass)", (long long)(e * D + i0) * 4, CPL * 4, 0, rg_size, t);
-          else in(c, "entry G (pass)", (long long)e * 4, 4, 0, rg_size, t);
+          g_row(c, "entry G row (pass)", e, i0, CPL, rg_size, t);
         }
       }
       e0 += NG * KPF;
@@ -199,7 +232,7 @@ void decode_step(const Cfg& c) {
 void close_kernel(const Cfg& c, bool dense, bool warm) {
   const Sizes z = sizes(c);
   const int D = c.D, BITS = c.BITS, KDA = c.KDA, NT = 128;
-  const int RB = D / 8, CB = D / 16, CH = 16, V4 = D / 4, PER = CH * V4 / NT;
+  const int RB = D / 8, CB = D / 16, CH0 = 32, CH1 = 16, V4 = D / 4, PER0 = CH0 * V4 / NT, PER1 = CH1 * V4 / NT;
   const long long bh = c.bh, hD = bh * D, erow = bh * (long long)(c.r + c.w_max);
   const int n = c.n, E = c.r + n, r = c.r;
   const long long HB = (long long)D * D * BITS / 8;
@@ -211,10 +244,8 @@ void close_kernel(const Cfg& c, bool dense, bool warm) {
     } else {
       in(c, "s load", (hD + i0) * 4, RB * 4, 0, z.s, t);
       in(c, "c load", (hD + j0) * 4, CB * 4, 0, z.c, t);
-      if (E > 0) {
-        if (KDA) in(c, "last G row", ((erow + E - 1) * D + i0) * 4, RB * 4, 0, z.eg, t);
-        else in(c, "last G", (erow + E - 1) * 4, 4, 0, z.eg, t);
-      }
+      if (KDA && n > 0) in(c, "last G row", ((erow + E - 1) * D + i0) * 4, RB * 4, 0, z.eg, t);
+      if (!KDA && E > 0) in(c, "last G", (erow + E - 1) * 4, 4, 0, z.eg, t);
       for (int bb = 0; bb < CB; ++bb) {
         const long long head = bh * HB;
         if (BITS == 6) {
@@ -227,28 +258,39 @@ void close_kernel(const Cfg& c, bool dense, bool warm) {
         }
       }
       const int c4 = t % V4;
-      if (KDA && E > 0) in(c, "last G quad", ((erow + E - 1) * D + 4 * c4) * 4, 16, 0, z.eg, t);
-      for (int m0 = 0; m0 < E; m0 += CH) {
-        const int cnt = E - m0 < CH ? E - m0 : CH;
-        for (int p = 0; p < PER; ++p) {
-          const int row = (t + NT * p) / V4;
-          in(c, "lds staged row", row, 1, 0, CH, t);
-          if (row < cnt) {
-            const long long g = ((erow + m0 + row) * D + 4 * c4) * 4;
-            in(c, "staged key", g, 16, 0, z.ek, t);
-            in(c, "staged value", g, 16, 0, z.eu, t);
-            if (KDA) in(c, "staged G", g, 16, 0, z.eg, t);
-            else in(c, "staged G", (erow + m0 + row) * 4, 4, 0, z.eg, t);
+      if (KDA && n > 0) in(c, "last G quad", ((erow + E - 1) * D + 4 * c4) * 4, 16, 0, z.eg, t);
+      // range-checked row descriptors: keys and values over this head's E
+      // rows; G (KDA) over its n buffered rows from entry r, (GDN) E floats
+      const long long rk0 = erow * D * 4, rk_size = (long long)E * D * 4;
+      const long long rg0 = KDA ? (erow + r) * D * 4 : erow * 4;
+      const long long rg_size = KDA ? (long long)n * D * 4 : (long long)E * 4;
+      in(c, "close key/value descriptor", rk0, rk_size, 0, z.ek, -1);
+      in(c, "close G descriptor", rg0, rg_size, 0, z.eg, -1);
+      // passes: the first stages CH0 rows, each later one CH1
+      for (int m0 = 0; m0 < E || m0 == 0; m0 += m0 == 0 ? CH0 : CH1) {
+        const int ch = m0 == 0 ? CH0 : CH1, np = m0 == 0 ? PER0 : PER1;
+        const int cnt = E - m0 < ch ? E - m0 : ch;
+        for (int p = 0; p < np; ++p) {
+          const int row = (t + NT * p) / V4, e = m0 + row;
+          in(c, "lds staged row", row, 1, 0, ch, t);
+          buffer_load(c, "staged key/value", (long long)(e * D + 4 * c4) * 4, 16, rk_size, t);
+          if (KDA) {
+            const long long off = e >= r ? (long long)((e - r) * D + 4 * c4) * 4 : MODEL_G_COMP_OFF;
+            if (e < r && off < rg_size) fail(c, "compensator G offset (close)", off, rg_size, 1LL << 32, t);
+            buffer_load(c, "staged G", off, 16, rg_size, t);
+          } else {
+            buffer_load(c, "staged G", (long long)e * 4, 4, rg_size, t);
           }
         }
         const int nkb = (cnt + 3) >> 2;
         for (int kb = 0; kb < nkb; ++kb) {
           const int e = 4 * kb + (lane >> 4);
-          in(c, "lds operand entry", e, 1, 0, CH, t);
+          in(c, "lds operand entry", e, 1, 0, ch, t);
           const int a_row = wave * 4 * RB + RB * ((lane & 15) >> 2) + (lane & 3);
           for (int q = 0; q < RB / 4; ++q) in(c, "lds key operand", a_row + 4 * q, 1, 0, D, t);
           in(c, "lds value operand", CB * (lane & 15), CB, 0, D, t);
         }
+        if (m0 + ch >= E) break;
       }
     }
     for (int l = 0; l < r; ++l) {

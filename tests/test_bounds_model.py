@@ -31,7 +31,8 @@ def test_kernel_addressing_stays_inside_every_buffer(tmp_path):
 
 
 @pytest.mark.parametrize("define,what", [("-DMODEL_KAPPA_ROWS=71", "lds kappa"),
-                                         ("-DMODEL_ENTRY_SLACK=1", "")])
+                                         ("-DMODEL_ENTRY_SLACK=1", ""),
+                                         ("-DMODEL_G_COMP_OFF=0", "compensator G offset")])
 def test_planted_mistakes_are_caught(tmp_path, define, what):
     res = _run(tmp_path, define)
     assert res.returncode == 1
