@@ -12,12 +12,13 @@
 // lives in registers: the 8 x 16 thread grid gives thread (ti, tj) the block
 // of key rows [ti*RB, ti*RB+RB) and value columns [tj*CB, tj*CB+CB), with
 // RB = D/8 and CB = D/16 (16 x 8 at D = 128). A 16-lane DPP row holds one
-// block row (all tj), so sums over value columns are DPP reductions; sums over
-// key rows combine the four rows of a wave with the gfx950 row-swap
-// instructions, the work split so that each row keeps a quarter of the
-// columns, and the two waves through LDS. Tall blocks keep the reduction work
-// per power iteration low (16 DPP sums and 6 row swaps per 256 FMA), and at
-// D = 128 a thread owns whole 16-channel code groups. The fold of the buffered
+// block row (all tj), so sums over value columns stay inside the row: DPP
+// reductions, or at D = 128 a transpose through the wave's own LDS (each lane
+// adds up one key row). Sums over key rows combine the four rows of a wave
+// with the gfx950 row-swap instructions, the work split so that each row
+// keeps a quarter of the columns, and the two waves through LDS. Tall blocks
+// keep the reduction work per power iteration low, and at D = 128 a thread
+// owns whole 16-channel code groups. The fold of the buffered
 // entries is an fp32 matrix-core update whose output tiles land on these same
 // register blocks. Reductions run in a fixed order, so the result is
 // deterministic.
@@ -171,16 +172,22 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   constexpr int CB = D / 16;  // value columns per thread
   constexpr int Q = (1 << (BITS - 1)) - 1;  // 127, 31 or 7
   constexpr int HB = D * D * BITS / 8;      // code bytes per head
-  constexpr int CH0 = 32;                   // entries staged in LDS by the first fold pass
+  constexpr int CH0 = D == 128 ? 20 : 32;   // entries staged in LDS by the first fold pass
   constexpr int CH1 = 16;                   // ... by each later pass (windows past CH0 entries)
   constexpr int V4 = D / 4;                 // float4 per entry row
   constexpr int PER0 = CH0 * V4 / NT;       // float4 per thread per staged array, first pass
   constexpr int PER1 = CH1 * V4 / NT;       // ... later passes
-  static_assert(NT % V4 == 0 && PER1 >= 1 && PER1 * NT == CH1 * V4 && PER0 == 2 * PER1, "staging shape");
+  static_assert(NT % V4 == 0 && PER1 >= 1 && PER1 * NT == CH1 * V4 && PER0 * NT == CH0 * V4, "staging shape");
   __shared__ float sh_n[2];                   // per-wave squared norms of the final kappa
   __shared__ __align__(16) float sh_c[2][2][D];  // per-wave column partials (double-buffered)
   __shared__ __align__(16) float sh_k[DENSE ? 1 : CH0][D];  // keys scaled by their decay to the window end
   __shared__ __align__(16) float sh_u[DENSE ? 1 : CH0][D];
+  // D = 128: the row partials of kappa = M v, per 16-lane row [tj][x] (rows
+  // of 20 floats, 16-byte aligned; 336 floats per lane row, so the four lane
+  // rows of a wave start 16 banks apart), and the row totals [ti][x]
+  constexpr int PX = 20, PR = 16 * PX + 16;
+  __shared__ __align__(16) float sh_p[RB == 16 ? 8 * PR : 1];
+  __shared__ __align__(16) float sh_t[RB == 16 ? 8 : 1][16];
 
   const int t = threadIdx.x, tj = t & 15, ti = t >> 4, lane = t & 63, wave = t >> 6;
   const int H = a.heads;
@@ -343,11 +350,11 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   // iteration: kappa = M v is complete inside each 16-lane row, and the
   // column partials of M^T kappa go to LDS (double-buffered, so the next
   // iteration may write while this one is read). The iteration keeps kappa
-  // and c = M^T kappa unnormalised: v = c / |c| is the same direction as
-  // w / |w| with w = M^T (kappa / |kappa|), and |kappa| is only needed once,
-  // after the last iteration, for the unit key k and its value w = c / |kappa|.
-  // kappa = 0 exactly when c = 0 (|kappa|^2 = v . c), so |c|^2 zero or not
-  // finite flags a degenerate head.
+  // and c = M^T kappa unnormalised: the next v is c, of unit direction
+  // c / |c| = w / |w| with w = M^T (kappa / |kappa|), and |kappa| is only
+  // needed once, after the last iteration, for the unit key k and its value
+  // w = c / |kappa|. kappa = 0 exactly when c = 0 (|kappa|^2 = v . c), so
+  // |c|^2 zero or not finite flags a degenerate head.
   bool live = true;
   int par = 0;
   for (int l = 0; l < r; ++l) {
@@ -375,17 +382,48 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
         }
         p = group_sum<16>(p);
       }
-      const float inv_nv = __builtin_amdgcn_rsqf(p);
-#pragma unroll
-      for (int bb = 0; bb < CB; ++bb) v[bb] *= inv_nv;
+      // v stays unnormalised: the unit vector is v sv, and sv multiplies the
+      // row totals of M v instead of every element of v
+      float sv = __builtin_amdgcn_rsqf(p);
       for (int it = 0; it < a.T; ++it) {
-        // kappa = M v (sum over value columns: DPP across the 16 tj lanes)
+        // kappa = (M v) sv: the sum over value columns runs across the 16 tj lanes
+        if constexpr (RB == 16) {
+          // one row per lane: every lane writes its 16 row partials, lane tj
+          // adds up the 16 partials of row i0 + tj, and every lane reads the
+          // 16 totals back. Only this wave's lanes take part, so the wave's
+          // in-order LDS accesses order them (no workgroup barrier).
+          float sx[RB];
 #pragma unroll
-        for (int x = 0; x < RB; ++x) {
-          float s = 0.f;
+          for (int x = 0; x < RB; ++x) {
+            float s = 0.f;
 #pragma unroll
-          for (int bb = 0; bb < CB; ++bb) s = fmaf(M[x >> 2][bb][x & 3], v[bb], s);
-          kk[x] = group_sum<16>(s);
+            for (int bb = 0; bb < CB; ++bb) s = fmaf(M[x >> 2][bb][x & 3], v[bb], s);
+            sx[x] = s;
+          }
+          float* P = &sh_p[ti * PR];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<float4*>(&P[tj * PX + 4 * k]) = make_float4(sx[4 * k], sx[4 * k + 1], sx[4 * k + 2], sx[4 * k + 3]);
+          __builtin_amdgcn_wave_barrier();
+          float tot = 0.f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) tot += P[q * PX + tj];
+          sh_t[ti][tj] = tot * sv;
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float4 t4 = *reinterpret_cast<const float4*>(&sh_t[ti][4 * k]);
+            kk[4 * k] = t4.x, kk[4 * k + 1] = t4.y, kk[4 * k + 2] = t4.z, kk[4 * k + 3] = t4.w;
+          }
+          __builtin_amdgcn_wave_barrier();  // these reads precede the next iteration's writes
+        } else {
+#pragma unroll
+          for (int x = 0; x < RB; ++x) {
+            float s = 0.f;
+#pragma unroll
+            for (int bb = 0; bb < CB; ++bb) s = fmaf(M[x >> 2][bb][x & 3], v[bb], s);
+            kk[x] = group_sum<16>(s) * sv;
+          }
         }
         // c = M^T kappa (sum over key rows: the wave's four rows, then the two waves)
         {
@@ -422,9 +460,9 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
           live = false;
           break;
         }
-        const float inv_c = __builtin_amdgcn_rsqf(pc);
+        sv = __builtin_amdgcn_rsqf(pc);
 #pragma unroll
-        for (int bb = 0; bb < CB; ++bb) v[bb] = w[bb] * inv_c;
+        for (int bb = 0; bb < CB; ++bb) v[bb] = w[bb];
       }
       if (live) {
         // |kappa|^2 of the last iteration: the thread's rows (equal across

@@ -232,7 +232,9 @@ void decode_step(const Cfg& c) {
 void close_kernel(const Cfg& c, bool dense, bool warm) {
   const Sizes z = sizes(c);
   const int D = c.D, BITS = c.BITS, KDA = c.KDA, NT = 128;
-  const int RB = D / 8, CB = D / 16, CH0 = 32, CH1 = 16, V4 = D / 4, PER0 = CH0 * V4 / NT, PER1 = CH1 * V4 / NT;
+  const int RB = D / 8, CB = D / 16, CH0 = D == 128 ? 20 : 32, CH1 = 16, V4 = D / 4;
+  const int PER0 = CH0 * V4 / NT, PER1 = CH1 * V4 / NT, PX = 20, PR = 16 * PX + 16;
+  if (PER0 * NT != CH0 * V4 || PER1 * NT != CH1 * V4) fail(c, "staging shape", PER0, 0, 0, -1);
   const long long bh = c.bh, hD = bh * D, erow = bh * (long long)(c.r + c.w_max);
   const int n = c.n, E = c.r + n, r = c.r;
   const long long HB = (long long)D * D * BITS / 8;
@@ -294,6 +296,12 @@ void close_kernel(const Cfg& c, bool dense, bool warm) {
       }
     }
     for (int l = 0; l < r; ++l) {
+      if (RB == 16) {  // kappa's row partials and totals (D = 128)
+        for (int k = 0; k < 4; ++k) in(c, "lds kappa partials", (long long)ti * PR + tj * PX + 4 * k, 4, 0, 8LL * PR, t);
+        for (int q = 0; q < 16; ++q) in(c, "lds kappa partial read", (long long)ti * PR + q * PX + tj, 1, (long long)ti * PR, (long long)ti * PR + PR, t);
+        in(c, "lds kappa total", (long long)ti * 16 + tj, 1, 0, 8 * 16, t);
+        for (int k = 0; k < 4; ++k) in(c, "lds kappa totals read", (long long)ti * 16 + 4 * k, 4, 0, 8 * 16, t);
+      }
       if (!dense && warm) in(c, "warm start value", ((erow + l) * D + j0) * 4, CB * 4, 0, z.eu, t);
       const int g = lane >> 4;
       if (CB == 8) in(c, "lds column partials", j0 + 2 * g, 2, 0, D, t);
