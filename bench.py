@@ -182,9 +182,10 @@ class Graphs:
     run of decode steps between two close points (every layer's launch for
     each step), one graph per distinct close list (every layer's close)."""
 
-    def __init__(self, dims, states, toks, outs, closes, lqk, torch, kind="leapquant"):
+    def __init__(self, dims, states, toks, outs, closes, lqk, torch, kind="leapquant", ns=None):
         self.dims, self.states, self.toks, self.outs = dims, states, toks, outs
         self.closes, self.lqk, self.torch, self.kind = closes, lqk, torch, kind
+        self.ns = ns  # per step, the tokens each sequence holds (None: the kernel reads them)
         self._ids, self._cg = {}, {}
 
     def _capture(self, fn):
@@ -198,9 +199,14 @@ class Graphs:
 
         def body():
             for t in range(a, b):
+                # every sequence at the same window position: the kernel is told it
+                n = int(self.ns[t][0]) if self.ns is not None and (self.ns[t] == self.ns[t][0]).all() else -1
                 for l, st in enumerate(self.states):
                     x = self.toks[l]
-                    if self.kind == "leapquant":
+                    if self.kind == "leapquant" and n >= 0:
+                        lqk.decode_step_at(dims, st, n, x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t],
+                                           self.outs[l])
+                    elif self.kind == "leapquant":
                         lqk.decode_step(dims, st, x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t],
                                         self.outs[l])
                     else:
@@ -320,7 +326,7 @@ def run_gpu(args, wl, bits):
         err = int(sum(int(st.err.item()) for st in states))
         assert err == 0, f"device error word {err}"
 
-    gr = Graphs(dims, states, toks, outs, closes, lqk, torch)
+    gr = Graphs(dims, states, toks, outs, closes, lqk, torch, ns=ns)
     torch.cuda.synchronize()
     warm_plan, timed_plan = gr.plan(0, Wu), gr.plan(Wu, total)
     torch.cuda.synchronize()
@@ -450,7 +456,7 @@ def run_single_set(args, wl, bits):
     lqk.encode(dims, runner.states_to_device(wk.initial_states(wl, range(wl.batch))), st)
     toks = [wk.device_tokens(wl, total, seed=0)]
     outs = [torch.empty((BH, D), dtype=torch.float32, device="cuda")]
-    gr = Graphs(dims, [st], toks, outs, closes, lqk, torch)
+    gr = Graphs(dims, [st], toks, outs, closes, lqk, torch, ns=ns)
     warm_plan, timed_plan = gr.plan(0, Wu), gr.plan(Wu, total)
     replay(warm_plan, torch, timed=False)
     torch.cuda.synchronize()

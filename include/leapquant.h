@@ -156,6 +156,20 @@ int leapquant_decode_step(const lq_dims* dims, const lq_state* st, const void* q
                           const void* v, const float* g, const float* beta, float* o,
                           void* stream);
 
+/* leapquant_decode_step for a state whose every head holds n buffered tokens,
+   0 <= n < w_max: the caller's window schedule knows the position (every
+   sequence's windows aligned, as when they start together and share W; the
+   wink.run article, per-window quantization). The same step, bit for bit; the
+   kernel needs no head's buffer length before it issues the entry-row loads,
+   so every load goes out in the order the arithmetic uses it. Arguments as
+   leapquant_decode_step. Returns LQ_ERR_CONFIG for n outside [0, w_max). A
+   head whose stored buf_len differs from n is left unchanged (its o is not
+   written) and LQ_DEVERR_BAD_LEN is or-ed into *st->err when err is not
+   NULL. */
+int leapquant_decode_step_at(const lq_dims* dims, const lq_state* st, int32_t n, const void* q,
+                             const void* k, const void* v, const float* g, const float* beta,
+                             float* o, void* stream);
+
 /* Window close for a list of sequences (all heads of each): fold the entries
    into the dense state S = exp(G_n) (.) diag(s) C diag(c) + sum_e exp(G_n - G_e) (.) k_e u_e^T
    (G_n = G of the last entry), re-extract the compensators into entries

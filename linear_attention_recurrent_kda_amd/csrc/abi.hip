@@ -68,6 +68,7 @@ lq::StepArgs step_args(const lq_dims* d, const lq_state* st) {
   a.err = st->err;
   a.r = d->n_comp;
   a.w_max = d->w_max;
+  a.n_at = -1;
   return a;
 }
 
@@ -141,6 +142,25 @@ int leapquant_decode_step(const lq_dims* d, const lq_state* st, const void* q, c
   a.g = g;
   a.beta = beta;
   a.o = o;
+  return launched(lq::launch_decode_step(*d, a, static_cast<hipStream_t>(stream)));
+}
+
+int leapquant_decode_step_at(const lq_dims* d, const lq_state* st, int32_t n, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, float* o, void* stream) {
+  int rc = check_dims(d, true);
+  if (rc) return rc;
+  if (n < 0 || n >= d->w_max) return LQ_ERR_CONFIG;
+  if (empty(d)) return LQ_OK;
+  if ((rc = check_state(d, st, 1))) return rc;
+  if ((rc = check_acts(d, q, k, v, g, beta, o))) return rc;
+  lq::StepArgs a = step_args(d, st);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.n_at = n;
   return launched(lq::launch_decode_step(*d, a, static_cast<hipStream_t>(stream)));
 }
 

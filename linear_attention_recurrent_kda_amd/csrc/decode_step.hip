@@ -225,13 +225,19 @@ struct HeadStep {
   // Loads that do not depend on the buffer length, issued while it is in
   // flight: the first half of the codes, then the per-channel inputs.
   __device__ static __forceinline__ void load_early(const StepArgs& a, int bh, In& h) {
-    const int t = threadIdx.x;
-    const bool chan = NT == D || t < D;
-    const int tc = chan ? t : 0;
     const Ptr P = ptr(a, bh);
     load_codes(a, P, h, 0, RBW / 2);
     if constexpr (BITS == 6) load_lo(a, P, h);
     __builtin_amdgcn_sched_barrier(0);  // keep these codes first in the issue order
+    load_inputs(a, bh, h);
+  }
+
+  // The per-channel inputs: activations, scales, decay, beta.
+  __device__ static __forceinline__ void load_inputs(const StepArgs& a, int bh, In& h) {
+    const int t = threadIdx.x;
+    const bool chan = NT == D || t < D;
+    const int tc = chan ? t : 0;
+    const Ptr P = ptr(a, bh);
     if constexpr (BF16) {
       h.kx_raw = static_cast<const uint16_t*>(a.k)[P.hD + tc];
       h.qx_raw = static_cast<const uint16_t*>(a.q)[P.hD + tc];
@@ -253,6 +259,26 @@ struct HeadStep {
   // The loads that need the buffer length n (0 <= n < w_max): the entries,
   // then the second half of the codes.
   __device__ static __forceinline__ void load(const StepArgs& a, int bh, int n, In& h) {
+    load_entries(a, bh, n, h);
+    // The second half of the codes is issued last: loads complete in issue
+    // order, so the entry arithmetic can start while those codes stream in.
+    load_codes(a, ptr(a, bh), h, RBW / 2, RBW);
+  }
+
+  // Every load of a head whose buffer length n is known at launch, in the
+  // order the arithmetic uses them: the per-channel inputs, the entry rows,
+  // then all the codes.
+  __device__ static __forceinline__ void load_known(const StepArgs& a, int bh, int n, In& h) {
+    load_inputs(a, bh, h);
+    load_entries(a, bh, n, h);
+    __builtin_amdgcn_sched_barrier(0);
+    const Ptr P = ptr(a, bh);
+    load_codes(a, P, h, 0, RBW);
+    if constexpr (BITS == 6) load_lo(a, P, h);
+  }
+
+  // The entry rows (prefetched part) and G of the last entry.
+  __device__ static __forceinline__ void load_entries(const StepArgs& a, int bh, int n, In& h) {
     const int t = threadIdx.x;
     const int grp = t / 16, li = t % 16, i0 = li * CPL;
     const int q4 = t % NQ, ph = t / NQ;
@@ -277,9 +303,6 @@ struct HeadStep {
     // G_{t-1}: G of the last entry; 0 with no buffered token (compensators carry 0)
     if constexpr (KDA) h.Gp = n > 0 ? P.eg[(E - 1) * D + tc] : 0.f;
     else h.Gp = E > 0 ? P.eg[E - 1] : 0.f;
-    // The second half of the codes is issued last: loads complete in issue
-    // order, so the entry arithmetic can start while those codes stream in.
-    load_codes(a, P, h, RBW / 2, RBW);
   }
 
   // Codes of row blocks [lo, hi) in MFMA operand order: lane -> value column
@@ -554,12 +577,28 @@ struct HeadStep {
 // chip at once, every head's loads are in flight from the start, and no
 // workgroup waits for another. (Several heads per workgroup with the next
 // head's loads overlapping the current head's arithmetic measured slower.)
-template <int D, int BITS, bool KDA, bool BF16>
+template <int D, int BITS, bool KDA, bool BF16, bool AT>
 __global__ void __launch_bounds__((StepShape<D, KDA>::NT)) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 4)))
 decode_step_kernel(StepArgs a) {
   using HS = HeadStep<D, BITS, KDA, BF16>;
   __shared__ typename HS::Smem sm;
   const int bh = blockIdx.x;
+  if constexpr (AT) {
+    // Every head's buffer holds a.n_at tokens (the caller's schedule says so):
+    // no load waits for the length, so the loads go out in the order the
+    // arithmetic uses them. The stored length is loaded first and must agree,
+    // before anything is written.
+    const uint32_t n_raw = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(a.blen + bh, 4), 0, 0, 0);
+    const int n = a.n_at;
+    typename HS::In in;
+    HS::load_known(a, bh, n, in);
+    if (int(__builtin_amdgcn_readfirstlane(int(n_raw))) != n) {
+      if (threadIdx.x == 0 && a.err) atomicOr(a.err, LQ_DEVERR_BAD_LEN);
+      return;
+    }
+    HS::compute(a, bh, n, in, sm);
+    return;
+  }
   // The buffer length comes first (every entry address depends on it) and
   // through the vector memory path, whose loads complete in issue order: the
   // wait for it then lets the loads issued after it stay in flight.
@@ -578,8 +617,12 @@ decode_step_kernel(StepArgs a) {
 
 template <int D, int BITS, bool KDA, bool BF16>
 hipError_t launch(const lq_dims& d, const StepArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_step_kernel<D, BITS, KDA, BF16>), dim3(d.batch * d.heads),
-                     dim3((StepShape<D, KDA>::NT)), 0, stream, a);
+  if (a.n_at >= 0)
+    hipLaunchKernelGGL((decode_step_kernel<D, BITS, KDA, BF16, true>), dim3(d.batch * d.heads),
+                       dim3((StepShape<D, KDA>::NT)), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<D, BITS, KDA, BF16, false>), dim3(d.batch * d.heads),
+                       dim3((StepShape<D, KDA>::NT)), 0, stream, a);
   return hipGetLastError();
 }
 

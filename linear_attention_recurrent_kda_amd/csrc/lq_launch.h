@@ -27,6 +27,7 @@ struct StepArgs {
   float* o;
   int r;
   int w_max;
+  int n_at;  // -1: read each head's buffer length; >= 0: every head holds n_at tokens
 };
 
 struct CloseArgs {

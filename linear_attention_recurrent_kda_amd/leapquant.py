@@ -24,7 +24,8 @@ LQ_DEVERR_BUFFER_FULL, LQ_DEVERR_BAD_SEQ, LQ_DEVERR_BAD_LEN = 1, 2, 4
 LQ_STATE_NBUF = 8
 STATE_FIELDS = ("codes", "row_scale", "col_scale", "ent_k", "ent_u", "ent_g", "buf_len", "err")
 
-EXPORTS = ("lq_state_sizes", "leapquant_encode", "leapquant_decode_step", "leapquant_window_close",
+EXPORTS = ("lq_state_sizes", "leapquant_encode", "leapquant_decode_step", "leapquant_decode_step_at",
+           "leapquant_window_close",
            "gdn_decode_fp32_baseline", "leapquant_prefill", "lq_snapshot_bytes", "leapquant_snapshot",
            "leapquant_restore", "leapquant_dequantize", "lq_close_list", "lq_status_string")
 
@@ -50,6 +51,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lq_state_sizes": (ctypes.c_int, [pd, ctypes.POINTER(SZ)]),
         "leapquant_encode": (ctypes.c_int, [pd, P, ps, P, P]),
         "leapquant_decode_step": (ctypes.c_int, [pd, ps, P, P, P, P, P, P, P]),
+        "leapquant_decode_step_at": (ctypes.c_int, [pd, ps, I32, P, P, P, P, P, P, P]),
         "leapquant_window_close": (ctypes.c_int, [pd, ps, P, I32, P, P]),
         "gdn_decode_fp32_baseline": (ctypes.c_int, [pd, P, P, P, P, P, P, P, P]),
         "leapquant_prefill": (ctypes.c_int, [pd, P, I32, P, P, P, P, P, P, ps, P]),
@@ -198,6 +200,14 @@ def decode_step(dims: Dims, st: State, q, k, v, g, beta, o) -> None:
     _check("leapquant_decode_step", _lib.leapquant_decode_step(
         ctypes.byref(cd), ctypes.byref(cs), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
         _stream()))
+
+
+def decode_step_at(dims: Dims, st: State, n: int, q, k, v, g, beta, o) -> None:
+    """decode_step for a state whose every head holds n buffered tokens."""
+    cd, cs = dims.c(), st.c()
+    _check("leapquant_decode_step_at", _lib.leapquant_decode_step_at(
+        ctypes.byref(cd), ctypes.byref(cs), int(n), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(o), _stream()))
 
 
 def window_close(dims: Dims, st: State, seq_ids: Optional[torch.Tensor] = None, n_seq: int = 0,

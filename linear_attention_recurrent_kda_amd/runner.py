@@ -47,6 +47,15 @@ def states_to_device(S_math: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(S).to(device)
 
 
+def buffered_tokens(win_len: np.ndarray, win_off: np.ndarray, t: int) -> np.ndarray:
+    """Per sequence, the tokens its buffer holds before token t (counted from
+    the encode). A sequence starts at offset o inside its first window with an
+    empty buffer, so before its first close it holds t tokens and afterwards
+    (t + o) mod W."""
+    win_len, win_off = np.asarray(win_len, np.int64), np.asarray(win_off, np.int64)
+    return np.where(t + win_off < win_len, t, (t + win_off) % win_len)
+
+
 class Decoder:
     def __init__(self, dims: lqk.Dims, win_len: np.ndarray, win_off: np.ndarray, device="cuda"):
         self.dims = dims
@@ -71,6 +80,21 @@ class Decoder:
     def closes_at(self, t: int) -> int:
         return self._close_n[t % self.period]
 
+    def position(self, t: int) -> int:
+        """Tokens every sequence's buffer holds before token t, when all hold
+        the same number, else -1."""
+        n = buffered_tokens(self.win_len, self.win_off, t)
+        return int(n[0]) if len(n) and np.all(n == n[0]) else -1
+
+    def decode(self, t: int, q, k, v, g, beta, o) -> None:
+        """The decode step of token t: with the position given to the kernel
+        when every sequence is at the same one."""
+        n = self.position(t)
+        if n >= 0:
+            lqk.decode_step_at(self.dims, self.state, n, q, k, v, g, beta, o)
+        else:
+            lqk.decode_step(self.dims, self.state, q, k, v, g, beta, o)
+
     def close_due(self, t: int, dbg: Optional[torch.Tensor] = None) -> int:
         """Close every sequence whose window ends with token t; returns how many."""
         p = t % self.period
@@ -86,7 +110,7 @@ class Decoder:
 
     def step(self, q, k, v, g, beta, o: Optional[torch.Tensor] = None, close: bool = True) -> torch.Tensor:
         o = self.o if o is None else o
-        lqk.decode_step(self.dims, self.state, q, k, v, g, beta, o)
+        self.decode(self.t, q, k, v, g, beta, o)
         if close:
             self.close_due(self.t)
         self.t += 1
@@ -119,8 +143,7 @@ def capture_tokens(decs, inputs, outs, t0: int, t1: int, overlap: bool = True) -
                     cap.wait_event(pending[l])
                     pending[l] = None
                 x = inputs[l]
-                lqk.decode_step(dec.dims, dec.state, x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t],
-                                outs[l])
+                dec.decode(t, x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t], outs[l])
                 if overlap and dec.closes_at(t):
                     ready = torch.cuda.Event()
                     ready.record(cap)

@@ -103,6 +103,8 @@ void g_row(const Cfg& c, const char* what, int e, int i0, int cpl, long long rg_
   if (off < rg_size || off + cpl * 4 > (1LL << 32)) fail(c, "compensator G offset", off, rg_size, 1LL << 32, t);
 }
 
+// (leapquant_decode_step_at takes n from its caller, 0 <= n < w_max checked on
+// the host, and addresses every buffer exactly as below for that n.)
 void decode_step(const Cfg& c) {
   const Sizes z = sizes(c);
   const int D = c.D, BITS = c.BITS, KDA = c.KDA;

@@ -68,10 +68,29 @@ def test_dims_validation(kw, code):
     d = dims(**kw)
     st = state()
     assert step(d, st) == code
+    if "w_max" not in kw:
+        assert step_at(d, st, 3) == code
     assert L.raw_call("leapquant_window_close", ctypes.byref(d), ctypes.byref(st), None, 0, None, None) == code
     assert L.raw_call("leapquant_encode", ctypes.byref(d), FAKE, ctypes.byref(st), None, None) == code
     sizes = (ctypes.c_size_t * L.LQ_STATE_NBUF)()
     assert L.raw_call("lq_state_sizes", ctypes.byref(d), sizes) == code
+
+
+def step_at(d, st, n, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE):
+    return L.raw_call("leapquant_decode_step_at", ctypes.byref(d), ctypes.byref(st), n, q, k, v, g, beta, o, None)
+
+
+def test_decode_step_at_validation():
+    """The position must lie in [0, w_max); the other arguments are checked as
+    for leapquant_decode_step."""
+    d = dims()
+    assert step_at(d, state(), -1) == L.LQ_ERR_CONFIG
+    assert step_at(d, state(), 16) == L.LQ_ERR_CONFIG
+    assert step_at(dims(w_max=32), state(), 40) == L.LQ_ERR_CONFIG
+    assert step_at(d, state(codes=None), 0) == L.LQ_ERR_NULL
+    assert step_at(d, state(), 15, q=None) == L.LQ_ERR_NULL
+    assert step_at(d, state(ent_g=FAKE + 8), 2) == L.LQ_ERR_ALIGN
+    assert step_at(d, state(), 2, o=FAKE + 4) == L.LQ_ERR_ALIGN
 
 
 def test_null_and_alignment_validation():
@@ -192,3 +211,22 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.status_string(code) != "unknown status"
     assert L.status_string(-99) == "unknown status"
+
+
+def test_buffered_tokens_follow_the_close_schedule():
+    """runner.buffered_tokens (the position handed to leapquant_decode_step_at)
+    against a token-by-token count: every sequence starts empty, gains one
+    token per step and empties after each close of its list."""
+    from linear_attention_recurrent_kda_amd import runner
+
+    rng = np.random.default_rng(1)
+    W = np.where(np.arange(24) % 3 == 0, 16, 32).astype(np.int32)
+    off = rng.integers(0, 16, 24).astype(np.int32)
+    n = np.zeros(24, np.int64)
+    for t in range(100):
+        assert np.array_equal(runner.buffered_tokens(W, off, t), n), t
+        n += 1
+        n[L.close_list(W, off, t)] = 0
+    # aligned windows: every sequence at the same position, t mod W
+    W16, zero = np.full(8, 16, np.int32), np.zeros(8, np.int32)
+    assert [int(runner.buffered_tokens(W16, zero, t)[0]) for t in range(40)] == [t % 16 for t in range(40)]

@@ -79,6 +79,78 @@ def test_decode_step_every_instantiation(d, bits, kda, bf16, n_pre):
         np.testing.assert_allclose(host["buf_g"][np.arange(N), n_pre], G_ref, rtol=1e-6, atol=1e-7)
 
 
+def _uploaded_pair(d, bits, kda, bf16, n_pre):
+    """Two device states holding the same oracle-made state with n_pre buffered
+    tokens, and the next token's device inputs."""
+    wl = _wl(d, kda, bf16)
+    seqs = list(range(wl.batch))
+    N = wl.batch * wl.heads
+    dims = runner.dims_for(wl, bits)
+    S0 = wk.initial_states(wl, seqs).reshape(-1, d, d).astype(np.float64)
+    bo = lq.BufferedOracle(S0, np.full(N, 10 ** 6), np.zeros(N), w_max=dims.w_max, r=wl.n_comp,
+                           T=wl.power_iters, bits=bits, smoothing=wl.smoothing, kda=kda)
+    if n_pre:
+        for t in gh.flat_steps(wk.TokenStream(wl, seqs).next(n_pre)):
+            bo.step(t["q"], t["k"], t["v"], t["g"], t["beta"])
+    sts = [lqk.State(dims) for _ in range(2)]
+    for st in sts:
+        gh.upload_state(st, dims, bo.base, bo.buf_k, bo.buf_u, bo.buf_G, bo.n)
+    raw = wk.TokenStream(wl, seqs).next(n_pre + 1)
+    dev = runner.upload_tokens({k: v[n_pre:] for k, v in raw.items()}, bf16)
+    return dims, N, sts, dev
+
+
+@pytest.mark.parametrize("d,bits,kda,bf16,n_pre", [
+    (d, b, k, f, n) for d, b, k, f in itertools.product(DIMS, BITS, (False, True), (False, True)) for n in (0, 26)])
+def test_decode_step_at_matches_decode_step(d, bits, kda, bf16, n_pre):
+    """leapquant_decode_step_at (the position given by the caller) against
+    leapquant_decode_step on the same state and token: every state buffer and
+    the output bit for bit (the same arithmetic; only the load order differs)."""
+    dims, N, (st1, st2), dev = _uploaded_pair(d, bits, kda, bf16, n_pre)
+    o1 = torch.empty((N, d), dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(o1)
+    x = {k: v[0] for k, v in dev.items()}
+    lqk.decode_step(dims, st1, x["q"], x["k"], x["v"], x["g"], x["beta"], o1)
+    lqk.decode_step_at(dims, st2, n_pre, x["q"], x["k"], x["v"], x["g"], x["beta"], o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for f in lqk.STATE_FIELDS:
+        assert torch.equal(getattr(st1, f), getattr(st2, f)), f
+    assert int(st2.err.item()) == 0
+
+
+@pytest.mark.parametrize("kda", (False, True))
+def test_decode_step_at_skips_heads_at_another_position(kda):
+    """A head whose stored buffer length is not the given position is left as
+    it was, its output row unwritten, and LQ_DEVERR_BAD_LEN is set; the other
+    heads step exactly as with leapquant_decode_step."""
+    n_pre = 5
+    dims, N, (st1, st2), dev = _uploaded_pair(128, 8, kda, False, n_pre)
+    st2.buf_len[1] = n_pre - 2  # one head of the first sequence at another (valid) position
+    before = {f: getattr(st2, f).clone() for f in lqk.STATE_FIELDS}
+    o1 = torch.empty((N, 128), dtype=torch.float32, device="cuda")
+    o2 = torch.full_like(o1, 7.0)
+    x = {k: v[0] for k, v in dev.items()}
+    lqk.decode_step(dims, st1, x["q"], x["k"], x["v"], x["g"], x["beta"], o1)  # every head at n_pre
+    lqk.decode_step_at(dims, st2, n_pre, x["q"], x["k"], x["v"], x["g"], x["beta"], o2)
+    torch.cuda.synchronize()
+    assert int(st2.err.item()) == lq_deverr_bad_len()
+    assert torch.all(o2[1] == 7.0)
+    others = [h for h in range(N) if h != 1]
+    assert torch.equal(o2[others], o1[others])
+    for f in ("codes", "row_scale", "col_scale", "ent_k", "ent_u", "ent_g", "buf_len"):
+        a, b, ref = getattr(st2, f), before[f], getattr(st1, f)
+        assert torch.equal(a[1], b[1]), f
+        assert torch.equal(a[others], ref[others]), f
+
+
+def lq_deverr_bad_len():
+    import re
+    import os
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "leapquant.h")).read()
+    return int(re.search(r"#define LQ_DEVERR_BAD_LEN (\d+)", hdr).group(1))
+
+
 def _close_checks(R, post, bits, smoothing, F, heads):
     rebuilt = np.einsum("nli,nlj->nij", post["comp_k"][heads].astype(np.float64), post["comp_u"][heads]) + R
     err = np.linalg.norm(rebuilt - F, axis=(1, 2)) / np.linalg.norm(F, axis=(1, 2))
