@@ -559,12 +559,17 @@ struct HeadStep {
       for (int p = 0; p < EP; ++p) yk += sm.vs[p][0][j], yq += sm.vs[p][1][j];
       const float vj = BF16 ? as_f(h.vj_raw << 16) : as_f(h.vj_raw);
       const float u = h.beta * (vj - yk);
-      a.o[P.hD + j] = fmaf(kqs, u, yq);
-      // the appended entry is read again one step later, after the rest of
-      // the step's state has streamed through: non-temporal stores
-      __builtin_nontemporal_store(u, P.eu + E * D + j);
-      __builtin_nontemporal_store(kx, P.ek + E * D + j);
-      if constexpr (KDA) __builtin_nontemporal_store(Gi, P.eg + E * D + j);
+      // The output and the appended entry go out with the streaming (nt)
+      // policy: the entry is read again one step later, after the rest of the
+      // step's state has streamed through, and o by the next consumer (the
+      // policy measured faster than write-back stores for both).
+      constexpr int STORE_POLICY = 2;
+      __builtin_amdgcn_raw_buffer_store_b32(as_u(fmaf(kqs, u, yq)), buf_rsrc(a.o + P.hD, D * 4), j * 4, 0,
+                                            STORE_POLICY);
+      __builtin_amdgcn_raw_buffer_store_b32(as_u(u), buf_rsrc(P.eu + E * D, D * 4), j * 4, 0, STORE_POLICY);
+      __builtin_amdgcn_raw_buffer_store_b32(as_u(kx), buf_rsrc(P.ek + E * D, D * 4), j * 4, 0, STORE_POLICY);
+      if constexpr (KDA)
+        __builtin_amdgcn_raw_buffer_store_b32(as_u(Gi), buf_rsrc(P.eg + E * D, D * 4), j * 4, 0, STORE_POLICY);
       if (t == 0) {
         if constexpr (!KDA) P.eg[E] = G;
         a.blen[bh] = n + 1;
