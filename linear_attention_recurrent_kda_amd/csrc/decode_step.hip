@@ -17,9 +17,13 @@
 // B operand's columns. The int32 accumulation is exact, so the only rounding
 // is the fixed-point conversion of z (below fp32 accumulation error) and the
 // final fp32 combination. int4 codes need no decode: a nibble masked into a
-// byte's high half is the int8 16*code. Loads are issued in the order they are
-// consumed (each lane group's key rows straight into registers, per-channel
-// inputs, codes); the key-side dots run while the codes arrive.
+// byte's high half is the int8 16*code. When the caller gives the window
+// position, loads are issued in the order they are consumed (per-channel
+// inputs, each lane group's entry rows straight into registers, then the
+// codes); otherwise every entry address waits for the head's buffer length,
+// and half of the codes are issued while it is in flight. Either way the
+// key-side dots run while the last codes arrive. The output and the appended
+// entry are written with streaming stores.
 #include "lq_common.h"
 #include "lq_launch.h"
 
