@@ -94,16 +94,28 @@ __device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t (&w)[(NB 
   else __builtin_nontemporal_store(uint16_t(w[0]), reinterpret_cast<uint16_t*>(p));
 }
 
+// N codes packed little-endian (4 bits: even channel in the low nibble). Only
+// the low BITS bits of each c[a] are read, so bit patterns whose low bits are
+// the two's-complement codes pack as they are: bytes (or nibble pairs) are
+// gathered four at a time with byte permutes.
 template <int N, int BITS>
-__device__ __forceinline__ void store_codes(uint8_t* p, const int (&c)[N]) {
+__device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&c)[N]) {
+  static_assert(BITS == 8 || BITS == 4, "code width");
   constexpr int NB = N * BITS / 8;
+  uint32_t b[NB];  // byte m of the packed codes in the low 8 bits (higher bits ignored)
+#pragma unroll
+  for (int m = 0; m < NB; ++m) b[m] = BITS == 8 ? c[m] : (c[2 * m] & 0xFu) | (c[2 * m + 1] << 4);
   uint32_t w[(NB + 3) / 4];
+  if constexpr (NB >= 4) {
 #pragma unroll
-  for (int q = 0; q < (NB + 3) / 4; ++q) w[q] = 0u;
-#pragma unroll
-  for (int a = 0; a < N; ++a) {
-    if constexpr (BITS == 8) w[a / 4] |= uint32_t(uint8_t(c[a])) << (8 * (a % 4));
-    else w[a / 8] |= (uint32_t(c[a]) & 0xFu) << (4 * (a % 8));
+    for (int q = 0; q < NB / 4; ++q) {
+      const uint32_t lo = __builtin_amdgcn_perm(b[4 * q + 1], b[4 * q], 0x0c0c0400u);  // bytes 0, 1
+      const uint32_t hi = __builtin_amdgcn_perm(b[4 * q + 3], b[4 * q + 2], 0x0c0c0400u);
+      w[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+  } else {
+    static_assert(NB == 2, "code bytes per block column");
+    w[0] = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
   }
   store_bytes<NB>(p, w);
 }
@@ -607,22 +619,23 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
 #pragma unroll
   for (int bb = 0; bb < CB; ++bb) {
     const int j = j0 + bb;
-    int code[RB];
+    uint32_t pat[RB];
 #pragma unroll
     for (int x = 0; x < RB; ++x) {
       // M inv + 1.5 2^23 rounds once to the nearest integer, ties to even,
-      // and the low bits of the sum's pattern are that integer in two's
-      // complement. No clamp: |M| is at most its column's maximum, so
+      // and the low 22 bits of the sum's pattern are that integer in two's
+      // complement (the pattern minus that of 1.5 2^23, whose low 22 bits are
+      // zero). No clamp: |M| is at most its column's maximum, so
       // |M inv| <= Q (1 + 2^-24) < Q + 1/2.
-      code[x] = int(__float_as_uint(fmaf(M[x >> 2][bb][x & 3], inv[bb], 12582912.f)) - 0x4B400000u);
+      pat[x] = __float_as_uint(fmaf(M[x >> 2][bb][x & 3], inv[bb], 12582912.f));
     }
     if constexpr (BITS == 6) {
-      int hi[RB];
+      uint32_t hi[RB];
       uint32_t lo = 0;
 #pragma unroll
       for (int x = 0; x < RB; ++x) {
-        hi[x] = code[x] >> 2;  // arithmetic: floor(code / 4)
-        lo |= uint32_t(code[x] & 3) << lo_bit((i0 + x) & 15);
+        hi[x] = pat[x] >> 2;  // bits 2-5 of the code: floor(code / 4) as a nibble
+        lo |= (pat[x] & 3u) << lo_bit((i0 + x) & 15);
       }
       store_codes<RB, 4>(cb + size_t(j) * (D / 2) + i0 / 2, hi);
       // a 16-channel group's low bits are one word; below D = 128 the threads
@@ -631,7 +644,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       if constexpr (RB <= 4) lo = or_swap32(lo);
       if (ti % (16 / RB) == 0) __builtin_nontemporal_store(lo, reinterpret_cast<uint32_t*>(cb + lo_word<D>(j, i0 / 16)));
     } else {
-      store_codes<RB, BITS>(cb + size_t(j) * (D * BITS / 8) + i0 * BITS / 8, code);
+      store_codes<RB, BITS>(cb + size_t(j) * (D * BITS / 8) + i0 * BITS / 8, pat);
     }
   }
   if constexpr (RB == 16) {
