@@ -278,6 +278,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   // KDA: g, then G_t per key channel in base-2 units (G_t log2 e), so that
   // every decay factor e^{G_t - G_s} is a single exp2 of a difference
   __shared__ __align__(16) float sh_g[KDA ? C : 1][KS];
+  __shared__ __align__(16) float sh_eC[KDA ? D : 1];  // KDA: e^{G_C} per key channel
 
   // Lane-derived indices are re-derived in every phase from an opaque copy of
   // the thread index, so that the compiler forms each phase's addresses there
@@ -407,6 +408,70 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         sh_g[tk][i] = G;
       }
       __syncthreads();
+      // ---- KDA: for the 120 pairs s < t, beta_t sum_i k_t,i k_s,i e^{G_t,i - G_s,i}
+      // and sum_i q_t,i k_s,i e^{G_t,i - G_s,i} (one decay factor serves both),
+      // each summed over the channels by one thread; then the 16 pairs s = t,
+      // q_t . k_t, by all threads: eight lanes per token, 16 channels each
+      {
+        const int t0 = 64 * w + lane_id();
+        if (t0 < 120) {
+          int tk = 1, base = 0;  // t0 = t (t - 1) / 2 + s
+          for (int t2 = 2; t2 < C; ++t2)
+            if (t2 * (t2 - 1) / 2 <= t0) tk = t2, base = t2 * (t2 - 1) / 2;
+          const int s2 = t0 - base;
+          float ak = 0.f, aq = 0.f;
+#pragma unroll 4
+          for (int i = 0; i < D; i += 4) {
+            const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i]);
+            const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i]);
+            const float4 ks = *reinterpret_cast<const float4*>(&sh_k[s2][i]);
+            const float4 gt = *reinterpret_cast<const float4*>(&sh_g[tk][i]);
+            const float4 gs = *reinterpret_cast<const float4*>(&sh_g[s2][i]);
+            const float e0 = ks.x * __builtin_amdgcn_exp2f(gt.x - gs.x), e1 = ks.y * __builtin_amdgcn_exp2f(gt.y - gs.y);
+            const float e2 = ks.z * __builtin_amdgcn_exp2f(gt.z - gs.z), e3 = ks.w * __builtin_amdgcn_exp2f(gt.w - gs.w);
+            ak = fmaf(k4.x, e0, ak), aq = fmaf(q4.x, e0, aq);
+            ak = fmaf(k4.y, e1, ak), aq = fmaf(q4.y, e1, aq);
+            ak = fmaf(k4.z, e2, ak), aq = fmaf(q4.z, e2, aq);
+            ak = fmaf(k4.w, e3, ak), aq = fmaf(q4.w, e3, aq);
+            asm volatile("" ::: "memory");  // one step's LDS reads at a time (register pressure)
+          }
+          sh_a[tk][s2] = sh_beta[tk] * ak;
+          sh_b[tk][s2] = aq;
+        }
+        {
+          const int tk = t0 >> 3, i0 = 16 * (t0 & 7);  // lanes 8m..8m+7 of a wave share a token
+          float aq = 0.f;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i0 + 4 * h]);
+            const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i0 + 4 * h]);
+            aq = fmaf(q4.x, k4.x, aq), aq = fmaf(q4.y, k4.y, aq);
+            aq = fmaf(q4.z, k4.z, aq), aq = fmaf(q4.w, k4.w, aq);
+          }
+          aq = group_sum<8>(aq);
+          if ((t0 & 7) == 0) sh_b[tk][tk] = aq;
+        }
+      }
+      __syncthreads();  // the pair sums' reads of k, q and G are done
+      // Thread i turns channel i of every token into the operands the
+      // matrix-core phases use, in place: k_t e^{G_t} (for K S0) over G,
+      // q_t e^{G_t} (Q S0) over q, and k_t e^{G_C - G_t} (the state update)
+      // over k; e^{G_C} goes to sh_eC. Each factor is computed once per
+      // element instead of once per operand slot of every wave.
+      {
+        const int i = 64 * w + lane_id();
+        const float GC = sh_g[C - 1][i];
+#pragma unroll
+        for (int tk = 0; tk < C; ++tk) {
+          const float G = sh_g[tk][i];
+          const float e = __builtin_amdgcn_exp2f(G);
+          sh_g[tk][i] = sh_k[tk][i] * e;
+          sh_qu[tk][i] = sh_qu[tk][i] * e;
+          sh_k[tk][i] = sh_k[tk][i] * __builtin_amdgcn_exp2f(GC - G);
+        }
+        sh_eC[i] = __builtin_amdgcn_exp2f(GC);
+      }
+      __syncthreads();
     }
 
     // ---- K S0, then Q S0, for this wave's columns (token 4g + r, column
@@ -414,14 +479,14 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       lane = lane_id(), g = lane >> 4, c = lane & 15;
-      float(*src)[KS] = pass == 0 ? sh_k : sh_qu;
+      float(*src)[KS] = pass == 0 ? (KDA ? sh_g : sh_k) : sh_qu;  // (KDA: decayed operands)
       v4f P[4];
 #pragma unroll
       for (int TC = 0; TC < 4; ++TC) P[TC] = v4f{0.f, 0.f, 0.f, 0.f};
       // operands one row block ahead of the products that use them (a fence
       // per block keeps the loads from piling up further ahead)
       // (KDA: the operand row is x_t (.) e^{G_t}, the decay through token t)
-      auto opnd = [&](int row) { return KDA ? src[c][row] * __builtin_amdgcn_exp2f(sh_g[c][row]) : src[c][row]; };
+      auto opnd = [&](int row) { return src[c][row]; };
       float ak[4], an[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ak[r] = opnd(4 * g + r);
@@ -449,50 +514,6 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
           if (pass == 0) sh_r[w][tk][16 * TC + c] = bt * (sh_r[w][tk][16 * TC + c] - eG * P[TC][r]);
           else sh_p[w][tk][16 * TC + c] = eG * P[TC][r];
         }
-      }
-    }
-    // ---- KDA: for the 120 pairs s < t, beta_t sum_i k_t,i k_s,i e^{G_t,i - G_s,i}
-    // and sum_i q_t,i k_s,i e^{G_t,i - G_s,i} (one decay factor serves both),
-    // each summed over the channels by one thread; then the 16 pairs s = t,
-    // q_t . k_t, by all threads: eight lanes per token, 16 channels each
-    if constexpr (KDA) {
-      const int t0 = 64 * w + lane_id();
-      if (t0 < 120) {
-        int tk = 1, base = 0;  // t0 = t (t - 1) / 2 + s
-        for (int t2 = 2; t2 < C; ++t2)
-          if (t2 * (t2 - 1) / 2 <= t0) tk = t2, base = t2 * (t2 - 1) / 2;
-        const int s2 = t0 - base;
-        float ak = 0.f, aq = 0.f;
-#pragma unroll 4
-        for (int i = 0; i < D; i += 4) {
-          const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i]);
-          const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i]);
-          const float4 ks = *reinterpret_cast<const float4*>(&sh_k[s2][i]);
-          const float4 gt = *reinterpret_cast<const float4*>(&sh_g[tk][i]);
-          const float4 gs = *reinterpret_cast<const float4*>(&sh_g[s2][i]);
-          const float e0 = ks.x * __builtin_amdgcn_exp2f(gt.x - gs.x), e1 = ks.y * __builtin_amdgcn_exp2f(gt.y - gs.y);
-          const float e2 = ks.z * __builtin_amdgcn_exp2f(gt.z - gs.z), e3 = ks.w * __builtin_amdgcn_exp2f(gt.w - gs.w);
-          ak = fmaf(k4.x, e0, ak), aq = fmaf(q4.x, e0, aq);
-          ak = fmaf(k4.y, e1, ak), aq = fmaf(q4.y, e1, aq);
-          ak = fmaf(k4.z, e2, ak), aq = fmaf(q4.z, e2, aq);
-          ak = fmaf(k4.w, e3, ak), aq = fmaf(q4.w, e3, aq);
-          asm volatile("" ::: "memory");  // one step's LDS reads at a time (register pressure)
-        }
-        sh_a[tk][s2] = sh_beta[tk] * ak;
-        sh_b[tk][s2] = aq;
-      }
-      {
-        const int tk = t0 >> 3, i0 = 16 * (t0 & 7);  // lanes 8m..8m+7 of a wave share a token
-        float aq = 0.f;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tk][i0 + 4 * h]);
-          const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tk][i0 + 4 * h]);
-          aq = fmaf(q4.x, k4.x, aq), aq = fmaf(q4.y, k4.y, aq);
-          aq = fmaf(q4.z, k4.z, aq), aq = fmaf(q4.w, k4.w, aq);
-        }
-        aq = group_sum<8>(aq);
-        if ((t0 & 7) == 0) sh_b[tk][tk] = aq;
       }
     }
     // ---- GDN: K K^T (wave 0) or Q K^T (wave 1): entry (t = 4g + r, s = c)
@@ -548,9 +569,8 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
 #pragma unroll
       for (int TR = 0; TR < 8; ++TR) {
         if constexpr (KDA) {  // row 16 TR + 4 g + r decays by e^{G_C} of its key channel
-          v4f e;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(sh_g[C - 1][16 * TR + 4 * g + r]);
+          const float4 e4 = *reinterpret_cast<const float4*>(&sh_eC[16 * TR + 4 * g]);
+          const v4f e = v4f{e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
           for (int TC = 0; TC < 4; ++TC) M[TR][TC] *= e;
         } else {
@@ -567,8 +587,8 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         for (int TC = 0; TC < 4; ++TC) ub[TC] = sh_qu[s2][64 * w + 16 * TC + c];
 #pragma unroll
         for (int TR = 0; TR < 8; ++TR) {
-          const float ak = KDA ? sh_k[s2][16 * TR + c] * __builtin_amdgcn_exp2f(sh_g[C - 1][16 * TR + c] - sh_g[s2][16 * TR + c])
-                               : f * sh_k[s2][16 * TR + c];
+          // (KDA: k_s e^{G_C - G_s}, precomputed)
+          const float ak = KDA ? sh_k[s2][16 * TR + c] : f * sh_k[s2][16 * TR + c];
 #pragma unroll
           for (int TC = 0; TC < 4; ++TC) M[TR][TC] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, ub[TC], M[TR][TC], 0, 0, 0);
         }
