@@ -271,7 +271,6 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   __shared__ __align__(16) float sh_k[C][KS];
   __shared__ __align__(16) float sh_qu[C][KS];  // q of the chunk, then its u
   __shared__ __align__(16) float sh_r[2][C][64];  // per wave: v, then beta (v - e^G S0^T k), token-major
-  __shared__ __align__(16) float sh_p[2][C][64];  // per wave: e^G S0^T q
   __shared__ float sh_a[C][C];                   // beta_t A_ts, s < t
   __shared__ float sh_b[C][C];                   // e^{G_t-G_s} k_s.q_t, s <= t
   __shared__ float sh_G[C], sh_beta[C];          // GDN: G_t; beta_t
@@ -279,6 +278,11 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   // every decay factor e^{G_t - G_s} is a single exp2 of a difference
   __shared__ __align__(16) float sh_g[KDA ? C : 1][KS];
   __shared__ __align__(16) float sh_eC[KDA ? D : 1];  // KDA: e^{G_C} per key channel
+  // per wave: e^G S0^T q. KDA keeps it over sh_g, whose last use is the K S0
+  // pass (that keeps the workgroup's LDS within four workgroups per CU)
+  __shared__ __align__(16) float sh_pg[KDA ? 1 : 2 * C * 64];
+  float(*sh_p)[C][64] = reinterpret_cast<float(*)[C][64]>(KDA ? &sh_g[0][0] : sh_pg);
+  static_assert(!KDA || C * KS >= 2 * C * 64, "e^G S0^T q fits over sh_g");
 
   // Lane-derived indices are re-derived in every phase from an opaque copy of
   // the thread index, so that the compiler forms each phase's addresses there
@@ -478,6 +482,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
     // 64w + 16TC + c), each turned into its LDS form before the next
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
+      if (KDA && pass == 1) __syncthreads();  // K S0's reads of sh_g are done before sh_p overwrites it
       lane = lane_id(), g = lane >> 4, c = lane & 15;
       float(*src)[KS] = pass == 0 ? (KDA ? sh_g : sh_k) : sh_qu;  // (KDA: decayed operands)
       v4f P[4];
