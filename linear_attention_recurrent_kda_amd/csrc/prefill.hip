@@ -274,6 +274,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   __shared__ float sh_a[C][C];                   // beta_t A_ts, s < t
   __shared__ float sh_b[C][C];                   // e^{G_t-G_s} k_s.q_t, s <= t
   __shared__ float sh_G[C], sh_beta[C];          // GDN: G_t; beta_t
+  __shared__ int sh_fast[2];                     // KDA: per-wave vote on the chunk's decay range
   // KDA: g, then G_t per key channel in base-2 units (G_t log2 e), so that
   // every decay factor e^{G_t - G_s} is a single exp2 of a difference
   __shared__ __align__(16) float sh_g[KDA ? C : 1][KS];
@@ -403,6 +404,9 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
     }
     if (c0 + C < n_tok) fetch(c0 + C, cur);
     __syncthreads();
+    // KDA: whether every channel's decay over the chunk stays within 2^-64,
+    // so that e^{G_t} and e^{-G_s} are both safe in fp32 (uniform per chunk)
+    bool fast = false;
     if constexpr (KDA) {  // G_t per key channel: thread i sums its channel over the chunk in place
       const int i = 64 * w + lane_id();
       float G = 0.f;
@@ -411,12 +415,17 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         G = fmaf(sh_g[tk][i], kLog2e, G);
         sh_g[tk][i] = G;
       }
+      const int all_ok = __all(G >= -64.f);  // G is G_C here (false for NaN)
+      if (lane_id() == 0) sh_fast[w] = all_ok;
       __syncthreads();
-      // ---- KDA: for the 120 pairs s < t, beta_t sum_i k_t,i k_s,i e^{G_t,i - G_s,i}
-      // and sum_i q_t,i k_s,i e^{G_t,i - G_s,i} (one decay factor serves both),
-      // each summed over the channels by one thread; then the 16 pairs s = t,
+      fast = sh_fast[0] != 0 && sh_fast[1] != 0;
+      // ---- KDA with a wider decay range: for the 120 pairs s < t,
+      // beta_t sum_i k_t,i k_s,i e^{G_t,i - G_s,i} and
+      // sum_i q_t,i k_s,i e^{G_t,i - G_s,i} (one decay factor serves both),
+      // each summed over the channels by one thread with every factor a
+      // single exp2 of a difference (at most 1); then the 16 pairs s = t,
       // q_t . k_t, by all threads: eight lanes per token, 16 channels each
-      {
+      if (!fast) {
         const int t0 = 64 * w + lane_id();
         if (t0 < 120) {
           int tk = 1, base = 0;  // t0 = t (t - 1) / 2 + s
@@ -456,12 +465,15 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
           if ((t0 & 7) == 0) sh_b[tk][tk] = aq;
         }
       }
-      __syncthreads();  // the pair sums' reads of k, q and G are done
+      if (!fast) __syncthreads();  // the pair sums' reads of k, q and G are done
       // Thread i turns channel i of every token into the operands the
       // matrix-core phases use, in place: k_t e^{G_t} (for K S0) over G,
-      // q_t e^{G_t} (Q S0) over q, and k_t e^{G_C - G_t} (the state update)
-      // over k; e^{G_C} goes to sh_eC. Each factor is computed once per
-      // element instead of once per operand slot of every wave.
+      // q_t e^{G_t} (Q S0) over q, and over k either k_t e^{-G_t} (fast: the
+      // pair products' right operand, turned into the state update's by the
+      // solve phase) or k_t e^{G_C - G_t} (the state update's); e^{G_C} goes
+      // to sh_eC. Each
+      // factor is computed once per element instead of once per operand slot
+      // of every wave.
       {
         const int i = 64 * w + lane_id();
         const float GC = sh_g[C - 1][i];
@@ -471,11 +483,35 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
           const float e = __builtin_amdgcn_exp2f(G);
           sh_g[tk][i] = sh_k[tk][i] * e;
           sh_qu[tk][i] = sh_qu[tk][i] * e;
-          sh_k[tk][i] = sh_k[tk][i] * __builtin_amdgcn_exp2f(GC - G);
+          sh_k[tk][i] = sh_k[tk][i] * __builtin_amdgcn_exp2f(fast ? -G : GC - G);
         }
         sh_eC[i] = __builtin_amdgcn_exp2f(GC);
       }
       __syncthreads();
+    }
+
+    // ---- pair coefficients on the matrix cores: K K^T (wave 0) or Q K^T
+    // (wave 1), entry (t = 4g + r, s = c). GDN: the plain rows, then the
+    // scalar decay e^{G_t - G_s}. KDA in the fast case: x_t e^{G_t} against
+    // k_s e^{-G_s}, so the per-channel decay is inside the contraction.
+    if (!KDA || fast) {
+      lane = lane_id(), g = lane >> 4, c = lane & 15;
+      float(*ra)[KS] = w == 0 ? (KDA ? sh_g : sh_k) : sh_qu;
+      v4f X = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int kb = 0; kb < D / 4; ++kb) {
+        const float b = sh_k[c][4 * kb + g];
+        const float av = ra[c][4 * kb + g];
+        X = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b, X, 0, 0, 0);
+      }
+      const float Gs = KDA ? 0.f : sh_G[c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tk = 4 * g + r;
+        const float f = KDA ? 1.f : exp_fast(sh_G[tk] - Gs);
+        if (w == 0) sh_a[tk][c] = c < tk ? sh_beta[tk] * f * X[r] : 0.f;
+        else sh_b[tk][c] = c <= tk ? f * X[r] : 0.f;
+      }
     }
 
     // ---- K S0, then Q S0, for this wave's columns (token 4g + r, column
@@ -521,25 +557,6 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         }
       }
     }
-    // ---- GDN: K K^T (wave 0) or Q K^T (wave 1): entry (t = 4g + r, s = c)
-    if constexpr (!KDA) {
-      lane = lane_id(), g = lane >> 4, c = lane & 15;
-      v4f X = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int kb = 0; kb < D / 4; ++kb) {
-        const float b = sh_k[c][4 * kb + g];
-        const float av = w == 0 ? b : sh_qu[c][4 * kb + g];
-        X = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b, X, 0, 0, 0);
-      }
-      const float Gs = sh_G[c];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tk = 4 * g + r;
-        const float f = exp_fast(sh_G[tk] - Gs);
-        if (w == 0) sh_a[tk][c] = c < tk ? sh_beta[tk] * f * X[r] : 0.f;
-        else sh_b[tk][c] = c <= tk ? f * X[r] : 0.f;
-      }
-    }
     __syncthreads();
 
     // ---- per value column (lane): forward substitution for u, then o
@@ -564,6 +581,11 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
       // (q in sh_qu was last read before the previous barrier)
 #pragma unroll
       for (int tk = 0; tk < C; ++tk) sh_qu[tk][J] = u[tk];
+      if (KDA && fast) {  // key channel J: k_t e^{-G_t} (the pair products' operand) to k_t e^{G_C - G_t}
+        const float e = sh_eC[J];
+#pragma unroll
+        for (int tk = 0; tk < C; ++tk) sh_k[tk][J] *= e;
+      }
     }
     __syncthreads();
 

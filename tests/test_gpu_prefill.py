@@ -91,6 +91,38 @@ def test_prefill_strong_decay(name, kw):
     assert worst <= 1e-5 and s_err <= 1e-5
 
 
+@pytest.mark.parametrize("act_bf16", [False, True])
+@pytest.mark.parametrize("g_tok", [-2.70, -2.85])
+def test_prefill_kda_chunk_decay_edges(g_tok, act_bf16):
+    """KDA chunks at d = 128 where half of the key channels decay by g_tok per
+    token (log alpha): over a 16-token chunk that is 2^-62.3 (g = -2.70) or
+    2^-65.8 (g = -2.85), one on each side of the 2^-64 range within which the
+    chunk's pair coefficients come from the rows x_t e^{G_t} and k_s e^{-G_s}
+    on the matrix cores (past it, from one exponential of a difference per
+    pair and channel). The other channels keep the workload's gates; the
+    prompt ends in a ragged chunk. Same bound against the exact recurrence."""
+    wl = W["kda_int4"].replace(batch=2, act_bf16=act_bf16)
+    L = 40
+    dims = runner.dims_for(wl)
+    S0 = wk.initial_states(wl, range(wl.batch))
+    S = runner.states_to_device(S0)
+    raw, _ = _prompt(wl, L)
+    raw["g"][..., 0::2] = np.float32(g_tok)
+    toks = gh.flat_steps(raw)
+    dev = runner.upload_tokens(raw, wl.act_bf16)
+    N, d = wl.batch * wl.heads, wl.d_k
+    o = torch.empty((L, N, d), dtype=torch.float32, device="cuda")
+    lqk.prefill(dims, S, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], o)
+    torch.cuda.synchronize()
+    S_ref, outs = lq.prefill(S0.reshape(N, d, d).astype(np.float64), toks)
+    o_gpu = o.cpu().numpy()
+    worst = max(gh.rel_l2(o_gpu[t], outs[t]) for t in range(L))
+    s_err = gh.rel_l2(gh.T(S.cpu().numpy()), S_ref)
+    print("KDA decay edge", g_tok, "bf16" if act_bf16 else "fp32", "max rel L2 o", worst, "state", s_err)
+    assert np.isfinite(o_gpu).all()
+    assert worst <= 1e-5 and s_err <= 1e-5
+
+
 @pytest.mark.parametrize("name,kw,bits", [("qwen_gdn", dict(batch=4), 8), ("kda_int4", dict(batch=2), 4),
                                           ("tiny_gdn", dict(batch=2, heads=3), 6)])
 def test_handoff_encode_and_decode_on(name, kw, bits):
