@@ -279,6 +279,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
   // every decay factor e^{G_t - G_s} is a single exp2 of a difference
   __shared__ __align__(16) float sh_g[KDA ? C : 1][KS];
   __shared__ __align__(16) float sh_eC[KDA ? D : 1];  // KDA: e^{G_C} per key channel
+  __shared__ __align__(16) float sh_GC[KDA ? D : 1];  // KDA: G_C per key channel
   // per wave: e^G S0^T q. KDA keeps it over sh_g, whose last use is the K S0
   // pass (that keeps the workgroup's LDS within four workgroups per CU)
   __shared__ __align__(16) float sh_pg[KDA ? 1 : 2 * C * 64];
@@ -415,6 +416,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         G = fmaf(sh_g[tk][i], kLog2e, G);
         sh_g[tk][i] = G;
       }
+      sh_GC[i] = G;
       const int all_ok = __all(G >= -64.f);  // G is G_C here (false for NaN)
       if (lane_id() == 0) sh_fast[w] = all_ok;
       __syncthreads();
@@ -466,26 +468,36 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) p
         }
       }
       if (!fast) __syncthreads();  // the pair sums' reads of k, q and G are done
-      // Thread i turns channel i of every token into the operands the
+      // Each thread turns 16 channels of one token into the operands the
       // matrix-core phases use, in place: k_t e^{G_t} (for K S0) over G,
       // q_t e^{G_t} (Q S0) over q, and over k either k_t e^{-G_t} (fast: the
       // pair products' right operand, turned into the state update's by the
-      // solve phase) or k_t e^{G_C - G_t} (the state update's); e^{G_C} goes
-      // to sh_eC. Each
-      // factor is computed once per element instead of once per operand slot
-      // of every wave.
+      // solve phase) or k_t e^{G_C - G_t} (the state update's); the threads
+      // of token 0 put e^{G_C} in sh_eC. Each factor is computed once per
+      // element instead of once per operand slot of every wave.
       {
-        const int i = 64 * w + lane_id();
-        const float GC = sh_g[C - 1][i];
+        lane = lane_id();
+        const int tt = 64 * w + lane, tr = tt >> 3, ch = (tt & 7) * 16;
 #pragma unroll
-        for (int tk = 0; tk < C; ++tk) {
-          const float G = sh_g[tk][i];
-          const float e = __builtin_amdgcn_exp2f(G);
-          sh_g[tk][i] = sh_k[tk][i] * e;
-          sh_qu[tk][i] = sh_qu[tk][i] * e;
-          sh_k[tk][i] = sh_k[tk][i] * __builtin_amdgcn_exp2f(fast ? -G : GC - G);
+        for (int h = 0; h < 4; ++h) {
+          const int c4 = ch + 4 * h;
+          const float4 G4 = *reinterpret_cast<const float4*>(&sh_g[tr][c4]);
+          const float4 C4 = *reinterpret_cast<const float4*>(&sh_GC[c4]);
+          const float4 k4 = *reinterpret_cast<const float4*>(&sh_k[tr][c4]);
+          const float4 q4 = *reinterpret_cast<const float4*>(&sh_qu[tr][c4]);
+          const float4 e = make_float4(__builtin_amdgcn_exp2f(G4.x), __builtin_amdgcn_exp2f(G4.y),
+                                       __builtin_amdgcn_exp2f(G4.z), __builtin_amdgcn_exp2f(G4.w));
+          const float4 f = make_float4(__builtin_amdgcn_exp2f(fast ? -G4.x : C4.x - G4.x),
+                                       __builtin_amdgcn_exp2f(fast ? -G4.y : C4.y - G4.y),
+                                       __builtin_amdgcn_exp2f(fast ? -G4.z : C4.z - G4.z),
+                                       __builtin_amdgcn_exp2f(fast ? -G4.w : C4.w - G4.w));
+          *reinterpret_cast<float4*>(&sh_g[tr][c4]) = make_float4(k4.x * e.x, k4.y * e.y, k4.z * e.z, k4.w * e.w);
+          *reinterpret_cast<float4*>(&sh_qu[tr][c4]) = make_float4(q4.x * e.x, q4.y * e.y, q4.z * e.z, q4.w * e.w);
+          *reinterpret_cast<float4*>(&sh_k[tr][c4]) = make_float4(k4.x * f.x, k4.y * f.y, k4.z * f.z, k4.w * f.w);
+          if (tr == 0)
+            *reinterpret_cast<float4*>(&sh_eC[c4]) = make_float4(__builtin_amdgcn_exp2f(C4.x), __builtin_amdgcn_exp2f(C4.y),
+                                                                 __builtin_amdgcn_exp2f(C4.z), __builtin_amdgcn_exp2f(C4.w));
         }
-        sh_eC[i] = __builtin_amdgcn_exp2f(GC);
       }
       __syncthreads();
     }
