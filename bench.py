@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--prefill-tokens", type=int, default=256,
                    help="prompt length of the prefill-handoff leg (0: skip)")
     p.add_argument("--no-snapshot", action="store_true", help="skip timing snapshot/restore")
+    p.add_argument("--no-fuse", action="store_true",
+                   help="take a window's last token with a decode launch and then close, instead of in one launch")
     p.add_argument("--no-overlap", action="store_true",
                    help="skip the schedule with window closes overlapping other layers' decodes")
     p.add_argument("--no-stream-reference", action="store_true",
@@ -180,13 +182,26 @@ def positions_text(ns_list):
 class Graphs:
     """HIP graphs of the decode schedule over L layer state sets: one graph per
     run of decode steps between two close points (every layer's launch for
-    each step), one graph per distinct close list (every layer's close)."""
+    each step), one graph per distinct close list (every layer's close). With
+    fuse, a step after which every sequence closes, all at the same window
+    position, is one launch per layer (leapquant_decode_close_at: the token's
+    step inside the close) in a graph of its own, and the decode graph before
+    it ends one step earlier."""
 
-    def __init__(self, dims, states, toks, outs, closes, lqk, torch, kind="leapquant", ns=None):
+    def __init__(self, dims, states, toks, outs, closes, lqk, torch, kind="leapquant", ns=None, fuse=True):
         self.dims, self.states, self.toks, self.outs = dims, states, toks, outs
         self.closes, self.lqk, self.torch, self.kind = closes, lqk, torch, kind
         self.ns = ns  # per step, the tokens each sequence holds (None: the kernel reads them)
-        self._ids, self._cg = {}, {}
+        self.fuse = fuse and kind == "leapquant" and ns is not None
+        self._ids, self._cg, self._fg = {}, {}, {}
+
+    def fused_at(self, t):
+        """The window position of step t when that step is taken inside the
+        close (every sequence closes after it, all at one position), else -1."""
+        if not self.fuse or len(self.closes[t]) != self.dims.batch:
+            return -1
+        n = self.ns[t]
+        return int(n[0]) if (n == n[0]).all() else -1
 
     def _capture(self, fn):
         g = self.torch.cuda.CUDAGraph()
@@ -195,6 +210,9 @@ class Graphs:
         return g
 
     def decode(self, a, b):
+        """The decode graph of steps [a, b) (None when empty)."""
+        if b <= a:
+            return None
         lqk, dims = self.lqk, self.dims
 
         def body():
@@ -215,9 +233,22 @@ class Graphs:
         return self._capture(body)
 
     def close(self, t):
-        """The close graph of the sequences due after step t (None when none or FP32)."""
+        """The close graph of the sequences due after step t (None when none or
+        FP32); with fusion, step t itself inside the close."""
         if self.kind != "leapquant" or not len(self.closes[t]):
             return None
+        n = self.fused_at(t)
+        if n >= 0:
+            if t not in self._fg:
+                lqk, dims = self.lqk, self.dims
+
+                def fused():
+                    for l, st in enumerate(self.states):
+                        x = self.toks[l]
+                        lqk.decode_close_at(dims, st, n, x["q"][t], x["k"][t], x["v"][t], x["g"][t],
+                                            x["beta"][t], self.outs[l])
+                self._fg[t] = self._capture(fused)
+            return self._fg[t]
         key = tuple(int(b) for b in self.closes[t])
         if key not in self._cg:
             if key not in self._ids:
@@ -235,26 +266,32 @@ class Graphs:
         return self._cg[key]
 
     def plan(self, t0, t1):
-        """[(a, b, decode graph, close graph or None)] covering steps [t0, t1)."""
-        return [(a, b, self.decode(a, b), self.close(b - 1)) for (a, b) in segments(self.closes, t0, t1)]
+        """[(a, b, decode graph or None, close graph or None, fused)] covering
+        steps [t0, t1); fused: step b - 1 is taken inside the close graph."""
+        out = []
+        for (a, b) in segments(self.closes, t0, t1):
+            f = self.fused_at(b - 1) >= 0
+            out.append((a, b, self.decode(a, b - 1 if f else b), self.close(b - 1), f))
+        return out
 
 
 def replay(plan, torch, timed):
     """Replay a plan in order; with timed, HIP events (torch's, on the replay
     stream) bracket each decode graph and each close graph."""
     evs = []
-    for (a, b, g_dec, g_close) in plan:
+    for (a, b, g_dec, g_close, fused) in plan:
         if timed:
             e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             e0.record()
-        g_dec.replay()
+        if g_dec is not None:
+            g_dec.replay()
         if timed:
             e1.record()
         if g_close is not None:
             g_close.replay()
         if timed:
             e2.record()
-            evs.append((a, b, e0, e1, e2, g_close is not None))
+            evs.append((a, b, e0, e1, e2, g_close is not None, fused))
     return evs
 
 
@@ -275,8 +312,8 @@ def timed_repeats(plan, tensors, torch, check_err=None, repeats=REPEATS):
         wall = time.perf_counter() - t0
         if check_err is not None:
             check_err()
-        seg = [(a, b, e0.elapsed_time(e1) * 1e3, e1.elapsed_time(e2) * 1e3 if hc else 0.0, hc)
-               for (a, b, e0, e1, e2, hc) in evs]
+        seg = [(a, b, e0.elapsed_time(e1) * 1e3, e1.elapsed_time(e2) * 1e3 if hc else 0.0, hc, fu)
+               for (a, b, e0, e1, e2, hc, fu) in evs]
         runs.append(dict(wall=wall, seg=seg))
     del saved
     return _median_run(runs), sorted(r["wall"] for r in runs)
@@ -307,8 +344,14 @@ def run_gpu(args, wl, bits):
         return L * H * sum(bm.step_bytes(D, wl.n_comp, dims.bits, wl.kda, wl.act_bf16, int(n)) for n in ns[t])
 
     def close_bytes_at(t):
+        if gr.fused_at(t) >= 0:  # the step's token inside the close
+            return L * H * sum(bm.fused_bytes(D, wl.n_comp, dims.bits, wl.kda, wl.act_bf16, int(ns[t][s]))
+                               for s in closes[t])
         return L * H * sum(bm.close_bytes(D, wl.n_comp, dims.bits, wl.kda, wl.act_bf16, int(ns[t][s]) + 1)
                            for s in closes[t])
+
+    def decode_steps(t0, t1):  # the steps in [t0, t1) taken by decode launches
+        return [t for t in range(t0, t1) if gr.fused_at(t) < 0]
 
     # inputs resident in HBM before anything is timed
     S_init = runner.states_to_device(wk.initial_states(wl, range(wl.batch)))
@@ -326,7 +369,7 @@ def run_gpu(args, wl, bits):
         err = int(sum(int(st.err.item()) for st in states))
         assert err == 0, f"device error word {err}"
 
-    gr = Graphs(dims, states, toks, outs, closes, lqk, torch, ns=ns)
+    gr = Graphs(dims, states, toks, outs, closes, lqk, torch, ns=ns, fuse=not args.no_fuse)
     torch.cuda.synchronize()
     warm_plan, timed_plan = gr.plan(0, Wu), gr.plan(Wu, total)
     torch.cuda.synchronize()
@@ -339,9 +382,10 @@ def run_gpu(args, wl, bits):
     # per-kernel averages from the events; algorithmic bytes from the schedule
     dec_us = sum(s[2] for s in run["seg"])
     close_us = sum(s[3] for s in run["seg"])
-    n_dec = sum((b - a) * L for (a, b, *_r) in run["seg"])
+    n_dec = sum((s[1] - s[0] - int(s[5])) * L for s in run["seg"])
     n_close = sum(L for s in run["seg"] if s[4])
-    dec_bytes = sum(step_bytes(t) for t in range(Wu, total))
+    n_fused = sum(L for s in run["seg"] if s[5])
+    dec_bytes = sum(step_bytes(t) for t in decode_steps(Wu, total))
     close_bytes = sum(close_bytes_at(t) for t in range(Wu, total))
     # the events lie inside the wall-clock region, and no figure beats the HBM peak
     assert dec_us + close_us <= wall * 1e6 * 1.02, (dec_us, close_us, wall)
@@ -349,10 +393,10 @@ def run_gpu(args, wl, bits):
     assert dec_bytes / (dec_us * 1e-6) <= HBM_PEAK_GBS * 1e9, "decode bytes above the HBM peak"
     assert L * (dec_us / n_dec) * K <= wall * 1e6 * 1.02
     res = dict(wall=wall, walls=walls, dec_us=dec_us / n_dec, close_us=close_us / max(n_close, 1),
-               n_dec=n_dec, n_close=n_close, dec_bytes=dec_bytes, close_bytes=close_bytes,
+               n_dec=n_dec, n_close=n_close, n_fused=n_fused, dec_bytes=dec_bytes, close_bytes=close_bytes,
                dec_gbs=dec_bytes / (dec_us * 1e-6) / 1e9,
                head_tokens=K * L * BH, state_mb=states[0].nbytes() / 1e6,
-               positions=positions_text([ns[t] for t in range(Wu, total)]))
+               positions=positions_text([ns[t] for t in decode_steps(Wu, total)]))
 
     # Decode launches over whole windows: from a fresh encode, one period of the
     # close schedule runs untimed, then the next period is replayed with the same
@@ -364,11 +408,13 @@ def run_gpu(args, wl, bits):
         replay([p for p in pos_plan if p[0] < period], torch, timed=False)
         evs = replay([p for p in pos_plan if p[0] >= period], torch, timed=True)
         torch.cuda.synchronize()
-        per.append(sum(e0.elapsed_time(e1) * 1e3 for (_, _, e0, e1, _, _) in evs))
+        per.append(sum(e0.elapsed_time(e1) * 1e3 for (_, _, e0, e1, _, _, _) in evs))
     us_period = float(np.median(per))
-    pos_bytes = sum(step_bytes(t) for t in range(period, 2 * period))
-    res["whole_windows"] = dict(steps=period, avg_launch_us=us_period / (period * L),
-                                bytes_per_launch=pos_bytes / (period * L),
+    pos_steps = decode_steps(period, 2 * period)
+    pos_bytes = sum(step_bytes(t) for t in pos_steps)
+    res["whole_windows"] = dict(steps=period, decode_steps=len(pos_steps),
+                                avg_launch_us=us_period / (len(pos_steps) * L),
+                                bytes_per_launch=pos_bytes / (len(pos_steps) * L),
                                 gbs=pos_bytes / (us_period * 1e-6) / 1e9)
     check_err()
     del pos_plan
@@ -456,16 +502,16 @@ def run_single_set(args, wl, bits):
     lqk.encode(dims, runner.states_to_device(wk.initial_states(wl, range(wl.batch))), st)
     toks = [wk.device_tokens(wl, total, seed=0)]
     outs = [torch.empty((BH, D), dtype=torch.float32, device="cuda")]
-    gr = Graphs(dims, [st], toks, outs, closes, lqk, torch, ns=ns)
+    gr = Graphs(dims, [st], toks, outs, closes, lqk, torch, ns=ns, fuse=not args.no_fuse)
     warm_plan, timed_plan = gr.plan(0, Wu), gr.plan(Wu, total)
     replay(warm_plan, torch, timed=False)
     torch.cuda.synchronize()
     run, _ = timed_repeats(timed_plan, [getattr(st, n) for n in lqk.STATE_FIELDS], torch)
     assert int(st.err.item()) == 0
     dec_us = sum(s[2] for s in run["seg"])
-    n_dec = sum(b - a for (a, b, *_r) in run["seg"])
+    n_dec = sum(s[1] - s[0] - int(s[5]) for s in run["seg"])
     dec_bytes = sum(H * sum(bm.step_bytes(D, wl.n_comp, dims.bits, wl.kda, wl.act_bf16, int(n)) for n in ns[t])
-                    for t in range(Wu, total))
+                    for t in range(Wu, total) if gr.fused_at(t) < 0)
     return {"note": "one state set, resident in the last-level cache: a warm figure, not the HBM measurement",
             "value": round(K * BH / run["wall"], 1), "unit": "head-tokens/s",
             "decode_avg_launch_us": round(dec_us / n_dec, 3),
@@ -687,12 +733,16 @@ def main():
             "avg_launch_us": round(r["dec_us"], 3),
             "bytes_per_launch": round(r["dec_bytes"] / max(r["n_dec"], 1)),
             "timed_window_positions": r["positions"],
-            "whole_windows": {"steps": ww["steps"], "avg_launch_us": round(ww["avg_launch_us"], 3),
+            "whole_windows": {"steps": ww["steps"], "decode_steps": ww["decode_steps"],
+                              "avg_launch_us": round(ww["avg_launch_us"], 3),
                               "bytes_per_launch": round(ww["bytes_per_launch"]),
                               "achieved": round(ww["gbs"], 1), "frac": round(ww["gbs"] / HBM_PEAK_GBS, 4)},
         },
         "window_close": {"avg_launch_us": round(r["close_us"], 3), "launches": r["n_close"],
-                         "bytes_per_launch": round(r["close_bytes"] / max(r["n_close"], 1))},
+                         "bytes_per_launch": round(r["close_bytes"] / max(r["n_close"], 1)),
+                         "with_last_token": r["n_fused"],
+                         "note": "launches that also take the window's last token (leapquant_decode_close_at) "
+                                 "are counted in with_last_token; that token has no decode launch"},
         "hbm_gbs_all_in": round((r["dec_bytes"] + r["close_bytes"]) / r["wall"] / 1e9, 1),
     }
     if "overlap_wall" in r:

@@ -184,6 +184,27 @@ int leapquant_decode_step_at(const lq_dims* dims, const lq_state* st, int32_t n,
 int leapquant_window_close(const lq_dims* dims, const lq_state* st, const int32_t* seq_ids,
                            int32_t n_seq, float* dbg_residual, void* stream);
 
+/* The window's last decode token and its window close in one pass, for a
+   state whose every head holds n buffered tokens, 0 <= n < w_max, and whose
+   every sequence closes after this token (aligned windows; the wink.run
+   article, per-window quantization: the state is requantized once per window,
+   after the window's last token). Per head the result is that of
+   leapquant_decode_step_at(n) followed by leapquant_window_close of every
+   sequence, up to fp32 rounding: the token's step is taken on the folded
+   fp32 state instead of the codes plus the buffer, with G_t = G_n + g_t,
+     S = decay of the folded state to G_t,  u_t = beta_t (v_t - S^T k_t),
+     S += k_t u_t^T,  o_t = S^T q_t,
+   and the token is not appended (the close empties the buffer). Then the
+   compensators, smoothing and codes as leapquant_window_close. Arguments as
+   leapquant_decode_step_at (o is written); dbg_residual as
+   leapquant_window_close (NULL, or fp32 [B*H][d_v][d_k]). Returns
+   LQ_ERR_CONFIG for n outside [0, w_max). A head whose stored buf_len differs
+   from n is left unchanged (its o is not written) and LQ_DEVERR_BAD_LEN is
+   or-ed into *st->err when err is not NULL. */
+int leapquant_decode_close_at(const lq_dims* dims, const lq_state* st, int32_t n, const void* q,
+                              const void* k, const void* v, const float* g, const float* beta,
+                              float* o, float* dbg_residual, void* stream);
+
 /* FP32-state baseline: one exact decode token of the gated delta rule with the
    state kept in fp32 (no quantisation), the full-precision state that the
    LeapQuant abstract and the wink.run article's results table and speed

@@ -8,6 +8,8 @@ decode step at window position n (n tokens already buffered):
   + output 4 d_v + buffer append E,        E = 4(d_k + d_v + g_len)
 window close after n tokens:
     read codes + scales + compensators + n*E, write codes + scales + compensators
+the window's last token taken inside its close (n tokens buffered before it):
+    the close over the n buffered rows + activations, decay, beta + output
 FP32-state baseline step:
     state read + write 2*4*d_k*d_v + activations + decay + beta + output
 g_len = 1 for GDN (scalar decay), d_k for KDA (per-key-channel decay).
@@ -32,6 +34,11 @@ def step_bytes(d: int, r: int, bits: int, kda: bool, bf16: bool, n: int) -> int:
 def close_bytes(d: int, r: int, bits: int, kda: bool, bf16: bool, n: int) -> int:
     g_len, E, lowbit, acts = _parts(d, r, bits, kda, bf16)
     return 2 * lowbit + n * E
+
+
+def fused_bytes(d: int, r: int, bits: int, kda: bool, bf16: bool, n: int) -> int:
+    g_len, E, lowbit, acts = _parts(d, r, bits, kda, bf16)
+    return 2 * lowbit + n * E + acts + 4 * d
 
 
 def fp32_step_bytes(d: int, kda: bool, bf16: bool) -> int:

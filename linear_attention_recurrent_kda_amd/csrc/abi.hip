@@ -164,6 +164,28 @@ int leapquant_decode_step_at(const lq_dims* d, const lq_state* st, int32_t n, co
   return launched(lq::launch_decode_step(*d, a, static_cast<hipStream_t>(stream)));
 }
 
+int leapquant_decode_close_at(const lq_dims* d, const lq_state* st, int32_t n, const void* q, const void* k,
+                              const void* v, const float* g, const float* beta, float* o, float* dbg,
+                              void* stream) {
+  int rc = check_dims(d, true);
+  if (rc) return rc;
+  if (n < 0 || n >= d->w_max) return LQ_ERR_CONFIG;
+  if (empty(d)) return LQ_OK;
+  if ((rc = check_state(d, st, 1))) return rc;
+  if ((rc = check_acts(d, q, k, v, g, beta, o))) return rc;
+  if (dbg && !aligned(dbg, 16)) return LQ_ERR_ALIGN;
+  lq::CloseArgs a = close_args(d, st);
+  a.dbg = dbg;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.n_at = n;
+  return launched(lq::launch_close(*d, a, d->batch * d->heads, static_cast<hipStream_t>(stream)));
+}
+
 int leapquant_window_close(const lq_dims* d, const lq_state* st, const int32_t* seq_ids, int32_t n_seq,
                            float* dbg, void* stream) {
   int rc = check_dims(d, true);

@@ -49,6 +49,14 @@ struct CloseArgs {
   int T;
   int smoothing;
   int warm;                // start compensator l from the current entry l's value (close only)
+  // one decode token taken first (NULL q: none): every head holds n_at tokens
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  float* o;
+  int n_at;
 };
 
 struct BaselineArgs {

@@ -184,8 +184,18 @@ __device__ __forceinline__ uint32_t or_swap32(uint32_t x) {  // x | x of lane ^ 
 template <int D>
 __constant__ constexpr StartVectors<8, D> kStart{};
 
-template <int D, int BITS, bool KDA, bool DENSE>
+// ACT: 0 for a plain close (or the dense encode); 1 or 2 when the close
+// first takes one decode token on every head (fp32 or bf16 activations): the
+// window's last token, folded in registers instead of appended.
+template <bool BF16>
+__device__ __forceinline__ float act_at(const void* p, size_t i) {
+  if constexpr (BF16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+  else return static_cast<const float*>(p)[i];
+}
+
+template <int D, int BITS, bool KDA, bool DENSE, int ACT>
 __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
+  static_assert(!(DENSE && ACT), "the dense encode takes no token");
   constexpr int RB = D / 8;   // key rows per thread
   constexpr int CB = D / 16;  // value columns per thread
   constexpr int Q = (1 << (BITS - 1)) - 1;  // 127, 31 or 7
@@ -206,6 +216,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   constexpr int PX = 20, PR = 16 * PX + 16;
   __shared__ __align__(16) float sh_p[RB == 16 ? 8 * PR : 1];
   __shared__ __align__(16) float sh_t[RB == 16 ? 8 : 1][16];
+  __shared__ __align__(16) float sh_tok[ACT ? 3 : 1][D];  // the token's k, q and v
 
   const int t = threadIdx.x, tj = t & 15, ti = t >> 4, lane = t & 63, wave = t >> 6;
   const int H = a.heads;
@@ -240,11 +251,20 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     // over the entries e < r + n (compensators carry G_e = 0); G_n is the G of
     // the last entry (0 when there is none)
     const int n = __builtin_amdgcn_readfirstlane(a.blen[bh]);
-    if (n < 0 || n > a.w_max) {  // corrupted buffer length: leave the head untouched
+    // corrupted buffer length (or, with a token, not the caller's position):
+    // leave the head untouched
+    if (n < 0 || n > a.w_max || (ACT != 0 && n != a.n_at)) {
       if (t == 0 && a.err) atomicOr(a.err, LQ_DEVERR_BAD_LEN);
       return;
     }
     const int E = r + n;
+    if constexpr (ACT != 0) {  // the token's rows, read after the fold (its barriers order them)
+      if (t < D) {
+        sh_tok[0][t] = act_at<ACT == 2>(a.k, hD + t);
+        sh_tok[1][t] = act_at<ACT == 2>(a.q, hD + t);
+        sh_tok[2][t] = act_at<ACT == 2>(a.v, hD + t);
+      }
+    }
     // Every load of the fold is issued before the first of them is used, so
     // that a head waits for memory once: this thread's code words, its scales,
     // G_n, and the first CH0 entry rows (all of them when r + n <= CH0).
@@ -263,6 +283,18 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     } else {
       Gn[0] = E > 0 ? a.eg[erow + E - 1] : 0.f;
     }
+    // with a token, the window ends at its G_t = G_n + g_t: everything is
+    // decayed to it (the decay the step applies before the delta)
+    if constexpr (ACT != 0) {
+      if constexpr (KDA) {
+        float gt[RB];
+        loadB<RB>(a.g + hD + i0, gt);
+#pragma unroll
+        for (int x = 0; x < RB; ++x) Gn[x] += gt[x];
+      } else {
+        Gn[0] += a.g[bh];
+      }
+    }
     // Entry rows go through LDS, each key multiplied by its decay to the
     // window end; every thread then applies them to its block. A thread
     // stages the same four key channels of every row it loads (NT is a
@@ -271,9 +303,13 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     // compensator's G row is addressed past the end of the G range, which
     // starts at entry r.
     const int c4 = t % V4;
-    float4 gq = make_float4(0.f, 0.f, 0.f, 0.f);  // KDA: G_n of the staged channels
+    float4 gq = make_float4(0.f, 0.f, 0.f, 0.f);  // KDA: G_n (or G_t) of the staged channels
     if constexpr (KDA) {
       if (n > 0) gq = *reinterpret_cast<const float4*>(a.eg + (erow + E - 1) * D + 4 * c4);
+      if constexpr (ACT != 0) {
+        const float4 g4 = *reinterpret_cast<const float4*>(a.g + hD + 4 * c4);
+        gq.x += g4.x, gq.y += g4.y, gq.z += g4.z, gq.w += g4.w;
+      }
     }
     const auto rk = buf_rsrc(a.ek + erow * D, uint32_t(E) * D * 4);
     const auto ru = buf_rsrc(a.eu + erow * D, uint32_t(E) * D * 4);
@@ -364,6 +400,57 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     }
   }
 
+  int par = 0;
+  // w = M^T kap for this thread's value columns: the sum over key rows, first
+  // the wave's four rows with the work split (each row swap pairs two
+  // columns, one kept by each half of the lanes), then the two waves through
+  // LDS, double-buffered so that consecutive sums need one barrier each
+  auto colsum = [&](const float(&kap)[RB], float(&w)[CB]) {
+    float cs[CB], tot[CB >= 4 ? CB / 4 : 1];
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) {
+      float s = 0.f;
+#pragma unroll
+      for (int x = 0; x < RB; ++x) s = fmaf(M[x >> 2][bb][x & 3], kap[x], s);
+      cs[bb] = s;
+    }
+    rows_sum_split<CB>(cs, tot);
+    const int g = lane >> 4;
+    static_assert(CB == 8 || CB == 4 || CB == 2, "columns per thread");
+    if constexpr (CB == 8) {
+      *reinterpret_cast<float2*>(&sh_c[par][wave][j0 + 2 * g]) = make_float2(tot[0], tot[1]);
+    } else if constexpr (CB == 4) {
+      sh_c[par][wave][j0 + g] = tot[0];
+    } else {
+      sh_c[par][wave][j0 + (g >> 1)] = tot[0];  // rows 2m and 2m+1 hold the same total
+    }
+    __syncthreads();
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) w[bb] = sh_c[par][0][j0 + bb] + sh_c[par][1][j0 + bb];
+    par ^= 1;
+  };
+
+  // ---- the window's last token (a decode step on the folded state, the
+  // gated delta rule): M is now the state decayed to the token, so
+  // u = beta (v - M^T k), M += k u^T, o = M^T q. The token is not appended:
+  // the close empties the buffer.
+  if constexpr (ACT != 0) {
+    float kr[RB], qr[RB], vv[CB], y[CB], u[CB];
+    loadB<RB>(&sh_tok[0][i0], kr);
+    loadB<RB>(&sh_tok[1][i0], qr);
+    loadB<CB>(&sh_tok[2][j0], vv);
+    const float beta = a.beta[bh];
+    colsum(kr, y);
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) u[bb] = beta * (vv[bb] - y[bb]);
+#pragma unroll
+    for (int x = 0; x < RB; ++x)
+#pragma unroll
+      for (int bb = 0; bb < CB; ++bb) M[x >> 2][bb][x & 3] = fmaf(kr[x], u[bb], M[x >> 2][bb][x & 3]);
+    colsum(qr, y);
+    if (ti == 0) storeB<CB>(a.o + hD + j0, y);
+  }
+
   // ---- compensators: power method with deflation. One barrier per
   // iteration: kappa = M v is complete inside each 16-lane row, and the
   // column partials of M^T kappa go to LDS (double-buffered, so the next
@@ -374,7 +461,6 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   // w = c / |kappa|. kappa = 0 exactly when c = 0 (|kappa|^2 = v . c), so
   // |c|^2 zero or not finite flags a degenerate head.
   bool live = true;
-  int par = 0;
   for (int l = 0; l < r; ++l) {
     float kk[RB], w[CB], v[CB];
 #pragma unroll
@@ -443,36 +529,11 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
             kk[x] = group_sum<16>(s) * sv;
           }
         }
-        // c = M^T kappa (sum over key rows: the wave's four rows, then the two waves)
-        {
-          float cs[CB], tot[CB >= 4 ? CB / 4 : 1];
-#pragma unroll
-          for (int bb = 0; bb < CB; ++bb) {
-            float s = 0.f;
-#pragma unroll
-            for (int x = 0; x < RB; ++x) s = fmaf(M[x >> 2][bb][x & 3], kk[x], s);
-            cs[bb] = s;
-          }
-          rows_sum_split<CB>(cs, tot);
-          const int g = lane >> 4;
-          static_assert(CB == 8 || CB == 4 || CB == 2, "columns per thread");
-          if constexpr (CB == 8) {
-            *reinterpret_cast<float2*>(&sh_c[par][wave][j0 + 2 * g]) = make_float2(tot[0], tot[1]);
-          } else if constexpr (CB == 4) {
-            sh_c[par][wave][j0 + g] = tot[0];
-          } else {
-            sh_c[par][wave][j0 + (g >> 1)] = tot[0];  // rows 2m and 2m+1 hold the same total
-          }
-        }
-        __syncthreads();
+        // c = M^T kappa, kept for the value
+        colsum(kk, w);
         float pc = 0.f;
 #pragma unroll
-        for (int bb = 0; bb < CB; ++bb) {
-          const int j = j0 + bb;
-          w[bb] = sh_c[par][0][j] + sh_c[par][1][j];  // c, kept for the value
-          pc = fmaf(w[bb], w[bb], pc);
-        }
-        par ^= 1;
+        for (int bb = 0; bb < CB; ++bb) pc = fmaf(w[bb], w[bb], pc);
         pc = group_sum<16>(pc);  // the same total in every row
         if (!(pc > 0.f) || !isfinite(pc)) {  // uniform: every thread read the same sums
           live = false;
@@ -663,17 +724,22 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   if (t == 0) a.blen[bh] = 0;
 }
 
-template <int D, int BITS, bool KDA, bool DENSE>
+template <int D, int BITS, bool KDA, bool DENSE, int ACT>
 hipError_t launch(const CloseArgs& a, int n_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((close_kernel<D, BITS, KDA, DENSE>), dim3(n_blocks), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((close_kernel<D, BITS, KDA, DENSE, ACT>), dim3(n_blocks), dim3(NT), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, int BITS, bool KDA>
+hipError_t launch_k(const lq_dims& d, const CloseArgs& a, int nb, hipStream_t s) {
+  if (a.S) return launch<D, BITS, KDA, true, 0>(a, nb, s);
+  if (!a.q) return launch<D, BITS, KDA, false, 0>(a, nb, s);
+  return d.act_dtype == LQ_ACT_BF16 ? launch<D, BITS, KDA, false, 2>(a, nb, s) : launch<D, BITS, KDA, false, 1>(a, nb, s);
 }
 
 template <int D, int BITS>
 hipError_t launch_b(const lq_dims& d, const CloseArgs& a, int nb, hipStream_t s) {
-  if (a.S)
-    return d.decay_per_channel ? launch<D, BITS, true, true>(a, nb, s) : launch<D, BITS, false, true>(a, nb, s);
-  return d.decay_per_channel ? launch<D, BITS, true, false>(a, nb, s) : launch<D, BITS, false, false>(a, nb, s);
+  return d.decay_per_channel ? launch_k<D, BITS, true>(d, a, nb, s) : launch_k<D, BITS, false>(d, a, nb, s);
 }
 
 template <int D>

@@ -25,7 +25,7 @@ LQ_STATE_NBUF = 8
 STATE_FIELDS = ("codes", "row_scale", "col_scale", "ent_k", "ent_u", "ent_g", "buf_len", "err")
 
 EXPORTS = ("lq_state_sizes", "leapquant_encode", "leapquant_decode_step", "leapquant_decode_step_at",
-           "leapquant_window_close",
+           "leapquant_decode_close_at", "leapquant_window_close",
            "gdn_decode_fp32_baseline", "leapquant_prefill", "lq_snapshot_bytes", "leapquant_snapshot",
            "leapquant_restore", "leapquant_dequantize", "lq_close_list", "lq_status_string")
 
@@ -52,6 +52,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "leapquant_encode": (ctypes.c_int, [pd, P, ps, P, P]),
         "leapquant_decode_step": (ctypes.c_int, [pd, ps, P, P, P, P, P, P, P]),
         "leapquant_decode_step_at": (ctypes.c_int, [pd, ps, I32, P, P, P, P, P, P, P]),
+        "leapquant_decode_close_at": (ctypes.c_int, [pd, ps, I32, P, P, P, P, P, P, P, P]),
         "leapquant_window_close": (ctypes.c_int, [pd, ps, P, I32, P, P]),
         "gdn_decode_fp32_baseline": (ctypes.c_int, [pd, P, P, P, P, P, P, P, P]),
         "leapquant_prefill": (ctypes.c_int, [pd, P, I32, P, P, P, P, P, P, ps, P]),
@@ -208,6 +209,16 @@ def decode_step_at(dims: Dims, st: State, n: int, q, k, v, g, beta, o) -> None:
     _check("leapquant_decode_step_at", _lib.leapquant_decode_step_at(
         ctypes.byref(cd), ctypes.byref(cs), int(n), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(o), _stream()))
+
+
+def decode_close_at(dims: Dims, st: State, n: int, q, k, v, g, beta, o,
+                    dbg_residual: Optional[torch.Tensor] = None) -> None:
+    """The window's last token (every head holding n buffered tokens) and the
+    close of every sequence, in one launch."""
+    cd, cs = dims.c(), st.c()
+    _check("leapquant_decode_close_at", _lib.leapquant_decode_close_at(
+        ctypes.byref(cd), ctypes.byref(cs), int(n), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(o), _ptr(dbg_residual), _stream()))
 
 
 def window_close(dims: Dims, st: State, seq_ids: Optional[torch.Tensor] = None, n_seq: int = 0,

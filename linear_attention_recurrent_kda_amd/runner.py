@@ -57,8 +57,15 @@ def buffered_tokens(win_len: np.ndarray, win_off: np.ndarray, t: int) -> np.ndar
 
 
 class Decoder:
-    def __init__(self, dims: lqk.Dims, win_len: np.ndarray, win_off: np.ndarray, device="cuda"):
+    """The decode schedule of one state set: window lengths and offsets per
+    sequence, the close lists they imply, and a token counter. With fuse, a
+    token after which every sequence closes, all at the same window position,
+    is taken inside the close (leapquant_decode_close_at) by step()."""
+
+    def __init__(self, dims: lqk.Dims, win_len: np.ndarray, win_off: np.ndarray, device="cuda",
+                 fuse: bool = True):
         self.dims = dims
+        self.fuse = fuse
         self.state = lqk.State(dims, device)
         self.win_len = np.asarray(win_len, np.int32)
         self.win_off = np.asarray(win_off, np.int32)
@@ -86,6 +93,14 @@ class Decoder:
         n = buffered_tokens(self.win_len, self.win_off, t)
         return int(n[0]) if len(n) and np.all(n == n[0]) else -1
 
+    def fused_at(self, t: int) -> int:
+        """The window position of token t when every sequence closes after it,
+        all at one position (so one launch can take the token and the close),
+        else -1."""
+        if not self.fuse or self.closes_at(t) != self.dims.batch:
+            return -1
+        return self.position(t)
+
     def decode(self, t: int, q, k, v, g, beta, o) -> None:
         """The decode step of token t: with the position given to the kernel
         when every sequence is at the same one."""
@@ -109,10 +124,15 @@ class Decoder:
         return n
 
     def step(self, q, k, v, g, beta, o: Optional[torch.Tensor] = None, close: bool = True) -> torch.Tensor:
+        """Token self.t on every head, then (close) the closes it makes due."""
         o = self.o if o is None else o
-        self.decode(self.t, q, k, v, g, beta, o)
-        if close:
-            self.close_due(self.t)
+        n = self.fused_at(self.t) if close else -1
+        if n >= 0:
+            lqk.decode_close_at(self.dims, self.state, n, q, k, v, g, beta, o)
+        else:
+            self.decode(self.t, q, k, v, g, beta, o)
+            if close:
+                self.close_due(self.t)
         self.t += 1
         return o
 
@@ -120,7 +140,9 @@ class Decoder:
 def capture_tokens(decs, inputs, outs, t0: int, t1: int, overlap: bool = True) -> torch.cuda.CUDAGraph:
     """One HIP graph that advances a stack of layers, each with its own Decoder,
     through tokens t0..t1-1: per token the decode step of every layer in layer
-    order, and the window closes due after it.
+    order, and the window closes due after it (as separate launches: the
+    token's output comes from its decode launch on the capture stream, and
+    only the close, which produces no output, moves to a side stream).
 
     inputs[l]: device token tensors of layer l with a leading token axis (q, k,
     v, g, beta); outs[l]: the output buffer of layer l. overlap=False closes

@@ -1,5 +1,6 @@
 // Host model of the device addressing of the decode step and the window close
-// (csrc/decode_step.hip, csrc/window_close.hip): every global load and store,
+// (csrc/decode_step.hip, csrc/window_close.hip, with or without the window's
+// last token taken inside the close): every global load and store,
 // buffer-descriptor range and LDS index those kernels form, written out again
 // on the host and checked, for every thread of the workgroup, against the
 // sizes the C ABI documents (lq_state_sizes) and the kernels' LDS arrays.
@@ -231,7 +232,7 @@ void decode_step(const Cfg& c) {
 }
 
 // ---------------------------------------------------------------- window close / encode
-void close_kernel(const Cfg& c, bool dense, bool warm) {
+void close_kernel(const Cfg& c, bool dense, bool warm, bool step = false) {
   const Sizes z = sizes(c);
   const int D = c.D, BITS = c.BITS, KDA = c.KDA, NT = 128;
   const int RB = D / 8, CB = D / 16, CH0 = D == 128 ? 20 : 32, CH1 = 16, V4 = D / 4;
@@ -246,6 +247,21 @@ void close_kernel(const Cfg& c, bool dense, bool warm) {
     if (dense) {
       for (int bb = 0; bb < CB; ++bb) in(c, "dense state load", ((hD + j0 + bb) * D + i0) * 4, RB * 4, 0, (long long)c.BH * D * D * 4, t);
     } else {
+      if (step) {  // the token: k, q, v into LDS rows; its decay; beta
+        const int ab = c.BF16 ? 2 : 4;
+        if (t < D) {
+          in(c, "token k/q load", (hD + t) * ab, ab, 0, z.act_qk, t);
+          in(c, "token v load", (hD + t) * ab, ab, 0, z.act_v, t);
+          in(c, "lds token rows", t, 1, 0, D, t);
+        }
+        if (KDA) {
+          in(c, "token decay rows", (hD + i0) * 4, RB * 4, 0, z.g, t);
+          in(c, "token decay quad", (hD + 4 * (t % V4)) * 4, 16, 0, z.g, t);
+        } else {
+          in(c, "token decay", bh * 4, 4, 0, z.g, t);
+        }
+        in(c, "token beta", bh * 4, 4, 0, z.beta, t);
+      }
       in(c, "s load", (hD + i0) * 4, RB * 4, 0, z.s, t);
       in(c, "c load", (hD + j0) * 4, CB * 4, 0, z.c, t);
       if (KDA && n > 0) in(c, "last G row", ((erow + E - 1) * D + i0) * 4, RB * 4, 0, z.eg, t);
@@ -296,6 +312,18 @@ void close_kernel(const Cfg& c, bool dense, bool warm) {
         }
         if (m0 + ch >= E) break;
       }
+    }
+    if (step) {  // u = beta (v - M^T k), o = M^T q: token rows from LDS, column sums, the output
+      in(c, "lds token key/query rows", i0, RB, 0, D, t);
+      in(c, "lds token value row", j0, CB, 0, D, t);
+      const int g = lane >> 4;
+      for (int sum = 0; sum < 2; ++sum) {
+        if (CB == 8) in(c, "lds column partials", j0 + 2 * g, 2, 0, D, t);
+        else if (CB == 4) in(c, "lds column partials", j0 + g, 1, 0, D, t);
+        else in(c, "lds column partials", j0 + (g >> 1), 1, 0, D, t);
+        for (int bb = 0; bb < CB; ++bb) in(c, "lds column read", j0 + bb, 1, 0, D, t);
+      }
+      if (ti == 0) in(c, "token output store", (hD + j0) * 4, CB * 4, 0, z.o, t);
     }
     for (int l = 0; l < r; ++l) {
       if (RB == 16) {  // kappa's row partials and totals (D = 128)
@@ -372,6 +400,11 @@ int main() {
                 }
               close_kernel(Cfg{D, BITS, KDA, 0, r, w_max, 0, bh, BH}, true, false);  // encode
               ++configs;
+              for (int BF16 = 0; BF16 < 2; ++BF16)
+                for (int n = 0; n < w_max; ++n) {  // the window's last token, then the close
+                  close_kernel(Cfg{D, BITS, KDA, BF16, r, w_max, n, bh, BH}, false, false, true);
+                  ++configs;
+                }
             }
   std::printf("bounds model: %lld launch configurations, %lld access checks, all inside their buffers\n", configs,
               checks);

@@ -93,6 +93,28 @@ def test_decode_step_at_validation():
     assert step_at(d, state(), 2, o=FAKE + 4) == L.LQ_ERR_ALIGN
 
 
+def decode_close_at(d, st, n, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, dbg=None):
+    return L.raw_call("leapquant_decode_close_at", ctypes.byref(d), ctypes.byref(st), n, q, k, v, g, beta, o,
+                      dbg, None)
+
+
+def test_decode_close_at_validation():
+    """The window's last token plus its close: the position must lie in
+    [0, w_max); activations, outputs, state and the optional residual are
+    checked as for leapquant_decode_step and leapquant_window_close."""
+    d = dims()
+    assert decode_close_at(d, state(), -1) == L.LQ_ERR_CONFIG
+    assert decode_close_at(d, state(), 16) == L.LQ_ERR_CONFIG
+    assert decode_close_at(dims(bits=5), state(), 15) == L.LQ_ERR_BITS
+    assert decode_close_at(dims(power_iters=0), state(), 15) == L.LQ_ERR_CONFIG
+    assert decode_close_at(d, state(buf_len=None), 15) == L.LQ_ERR_NULL
+    assert decode_close_at(d, state(), 15, beta=None) == L.LQ_ERR_NULL
+    assert decode_close_at(d, state(), 15, o=FAKE + 4) == L.LQ_ERR_ALIGN
+    assert decode_close_at(d, state(), 15, dbg=FAKE + 4) == L.LQ_ERR_ALIGN
+    assert decode_close_at(d, state(ent_u=FAKE + 4), 15) == L.LQ_ERR_ALIGN
+    assert decode_close_at(dims(batch=0), state(), 15) == L.LQ_OK   # nothing to do, nothing launched
+
+
 def test_null_and_alignment_validation():
     d = dims()
     assert L.raw_call("leapquant_decode_step", None, None, None, None, None, None, None, None, None) == L.LQ_ERR_NULL
