@@ -188,9 +188,13 @@ __constant__ constexpr StartVectors<8, D> kStart{};
 // first takes one decode token on every head (fp32 or bf16 activations): the
 // window's last token, folded in registers instead of appended.
 template <bool BF16>
-__device__ __forceinline__ float act_at(const void* p, size_t i) {
-  if constexpr (BF16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
-  else return static_cast<const float*>(p)[i];
+__device__ __forceinline__ uint32_t act_bits(const void* p, size_t i) {  // converted by act_f
+  if constexpr (BF16) return static_cast<const uint16_t*>(p)[i];
+  else return static_cast<const uint32_t*>(p)[i];
+}
+template <bool BF16>
+__device__ __forceinline__ float act_f(uint32_t b) {
+  return __uint_as_float(BF16 ? b << 16 : b);
 }
 
 template <int D, int BITS, bool KDA, bool DENSE, int ACT>
@@ -258,12 +262,17 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       return;
     }
     const int E = r + n;
-    if constexpr (ACT != 0) {  // the token's rows, read after the fold (its barriers order them)
-      if (t < D) {
-        sh_tok[0][t] = act_at<ACT == 2>(a.k, hD + t);
-        sh_tok[1][t] = act_at<ACT == 2>(a.q, hD + t);
-        sh_tok[2][t] = act_at<ACT == 2>(a.v, hD + t);
-      }
+    // the token's k, q and v at channel t: loaded now, put in LDS once the
+    // first staged rows are (so that no wait for them holds back the fold's
+    // loads), read after the fold, whose barriers order them
+    // (as loaded bits, the index clamped rather than branched on, so that
+    // nothing waits for them before the stores)
+    uint32_t tkk = 0u, tkq = 0u, tkv = 0u;
+    if constexpr (ACT != 0) {
+      const size_t it = hD + (t < D ? t : 0);
+      tkk = act_bits<ACT == 2>(a.k, it);
+      tkq = act_bits<ACT == 2>(a.q, it);
+      tkv = act_bits<ACT == 2>(a.v, it);
     }
     // Every load of the fold is issued before the first of them is used, so
     // that a head waits for memory once: this thread's code words, its scales,
@@ -357,6 +366,9 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     // the first pass's rows go to LDS before the residual is built, which
     // frees their registers for it
     stage_store(std::integral_constant<int, PER0>{}, 0);
+    if constexpr (ACT != 0) {
+      if (t < D) sh_tok[0][t] = act_f<ACT == 2>(tkk), sh_tok[1][t] = act_f<ACT == 2>(tkq), sh_tok[2][t] = act_f<ACT == 2>(tkv);
+    }
     // the residual M = diag(s exp(G_n)) C diag(c), decayed to the window end
 #pragma unroll
     for (int x = 0; x < RB; ++x) si[x] *= expf(KDA ? Gn[x] : Gn[0]);
