@@ -242,6 +242,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   // ---- the dense state block M[x][bb] = S[i0 + x][j0 + bb]
   // (four consecutive key rows of one value column form one MFMA accumulator)
   v4f M[RB / 4][CB];
+  int n_stored = 0;  // the head's stored buffer length (close only)
   if constexpr (DENSE) {
 #pragma unroll
     for (int bb = 0; bb < CB; ++bb) {
@@ -254,13 +255,23 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
     // fold: S = exp(G_n) (.) diag(s) C diag(c) + sum_e exp(G_n - G_e) (.) k_e u_e^T
     // over the entries e < r + n (compensators carry G_e = 0); G_n is the G of
     // the last entry (0 when there is none)
-    const int n = __builtin_amdgcn_readfirstlane(a.blen[bh]);
-    // corrupted buffer length (or, with a token, not the caller's position):
-    // leave the head untouched
-    if (n < 0 || n > a.w_max || (ACT != 0 && n != a.n_at)) {
-      if (t == 0 && a.err) atomicOr(a.err, LQ_DEVERR_BAD_LEN);
-      return;
-    }
+    // The buffer length is read first; the code words and scales, which do
+    // not depend on it, go out while it is in flight. Every load of the fold
+    // is issued before the first of them is used, so that a head waits for
+    // memory once: this thread's code words, its scales, G_n, and the first
+    // CH0 entry rows (all of them when r + n <= CH0).
+    n_stored = __builtin_amdgcn_readfirstlane(a.blen[bh]);
+    const uint8_t* cb = static_cast<const uint8_t*>(a.codes) + size_t(bh) * HB;
+    CodeWords<RB, BITS, D> cw[CB];
+#pragma unroll
+    for (int bb = 0; bb < CB; ++bb) cw[bb].load(cb, j0 + bb, i0);
+    __builtin_amdgcn_sched_barrier(0);  // (keeps the length's first use after these loads)
+    // The loads use the stored length clamped to [0, w_max] (with a token,
+    // the caller's position); the stored length itself is checked after the
+    // fold, before anything is written, and a corrupted one (or, with a
+    // token, one that is not the caller's position) leaves the head
+    // untouched. No branch stands between these loads and their use.
+    const int n = ACT != 0 ? a.n_at : min(max(n_stored, 0), a.w_max);
     const int E = r + n;
     // the token's k, q and v at channel t: loaded now, put in LDS once the
     // first staged rows are (so that no wait for them holds back the fold's
@@ -274,13 +285,6 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       tkq = act_bits<ACT == 2>(a.q, it);
       tkv = act_bits<ACT == 2>(a.v, it);
     }
-    // Every load of the fold is issued before the first of them is used, so
-    // that a head waits for memory once: this thread's code words, its scales,
-    // G_n, and the first CH0 entry rows (all of them when r + n <= CH0).
-    const uint8_t* cb = static_cast<const uint8_t*>(a.codes) + size_t(bh) * HB;
-    CodeWords<RB, BITS, D> cw[CB];
-#pragma unroll
-    for (int bb = 0; bb < CB; ++bb) cw[bb].load(cb, j0 + bb, i0);
     float si[RB], cj[CB], Gn[KDA ? RB : 1];
     loadB<RB>(a.s + hD + i0, si);
     loadB<CB>(a.c + hD + j0, cj);
@@ -409,6 +413,11 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       __syncthreads();  // the pass has consumed the staged rows
       stage_load(std::integral_constant<int, PER1>{}, m0);
       stage_store(std::integral_constant<int, PER1>{}, m0);
+    }
+    // (uniform: every thread read the same word)
+    if (ACT != 0 ? n_stored != a.n_at : (n_stored < 0 || n_stored > a.w_max)) {
+      if (t == 0 && a.err) atomicOr(a.err, LQ_DEVERR_BAD_LEN);
+      return;
     }
   }
 
