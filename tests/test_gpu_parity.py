@@ -396,6 +396,33 @@ def test_other_head_dims(d, kda, bits):
     assert max(gh.rel_l2(o_gpu[t], ref["o"][t]) for t in range(40)) <= 1e-3
 
 
+@pytest.mark.parametrize("kda", [False, True])
+def test_close_skips_heads_with_a_corrupted_length(kda):
+    """A head whose stored buffer length lies outside [0, w_max] is left
+    untouched by the close (its fold runs on the length clamped into range,
+    and the check comes before any write) and LQ_DEVERR_BAD_LEN is raised;
+    the other heads close."""
+    wl = W["tiny_gdn"].replace(batch=2, heads=2, window=6, kda=kda)
+    dims = runner.dims_for(wl)
+    dec = runner.Decoder(dims, np.full(wl.batch, wl.w_max), np.zeros(wl.batch, np.int32))
+    dec.encode(runner.states_to_device(wk.initial_states(wl, range(wl.batch))))
+    dev = runner.upload_tokens(wk.TokenStream(wl).next(4), False)
+    for i in range(4):
+        dec.step(dev["q"][i], dev["k"][i], dev["v"][i], dev["g"][i], dev["beta"][i], close=False)
+    st = dec.state
+    st.buf_len[1] = dims.w_max + 3
+    st.buf_len[2] = -1
+    pre = gh.download_state(st, dims)
+    lqk.window_close(dims, st)
+    post = gh.download_state(st, dims)
+    assert int(st.err.item()) & lqk.LQ_DEVERR_BAD_LEN
+    for h in (1, 2):
+        for f in ("codes", "row_scale", "col_scale", "ent_k", "ent_u", "ent_g", "buf_len"):
+            assert np.array_equal(post[f][h], pre[f][h]), (h, f)
+    assert post["buf_len"][0] == 0 and post["buf_len"][3] == 0
+    assert not np.array_equal(post["codes"][0], pre["codes"][0])
+
+
 def test_device_error_flags_and_empty_call():
     wl = W["tiny_gdn"].replace(batch=2, heads=2, window=4)
     dims = runner.dims_for(wl)
