@@ -55,7 +55,10 @@ __device__ __forceinline__ void loadB(const float* p, float (&x)[B]) {
 // The close's writes (codes, scales, compensator rows) use streaming stores:
 // the kernel is bound by its arithmetic, and the next decode step then reads
 // the new state without first evicting it from the caches (write-back stores
-// measured 0.5 us slower on that first step, the close itself unchanged).
+// measured 0.4-0.5 us slower on that first step, the close itself unchanged).
+// The price is write requests: a code row is written half by each wave, and
+// streamed halves often leave the L2 as separate requests (at 4 bits, 29%
+// more bytes written than with write-back stores, within the close's time).
 template <int B>
 __device__ __forceinline__ void storeB(float* p, const float (&x)[B]) {
   typedef float f4 __attribute__((ext_vector_type(4)));
@@ -68,6 +71,40 @@ __device__ __forceinline__ void storeB(float* p, const float (&x)[B]) {
     __builtin_nontemporal_store(f2{x[0], x[1]}, reinterpret_cast<f2*>(p));
   }
 }
+
+// x[B] held alike by the lanes of a group: lane q of the group (q < B / 4)
+// stores float4 q of it, so one instruction writes the group's whole B-float
+// segment and the wave's adjacent segments form whole lines. B = 2: lane 0
+// stores both floats. The caller selects the lanes (q below the count).
+// The elements pass through an empty asm before the lane's choice among them:
+// a choice between elements still in memory would otherwise be folded into a
+// load from a lane-dependent address, which keeps x in scratch memory.
+template <int B>
+__device__ __forceinline__ void storeSplit(float* p, const float (&x)[B], int q) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  if constexpr (B % 4 == 0) {
+    float y[B];
+#pragma unroll
+    for (int e = 0; e < B; ++e) {
+      y[e] = x[e];
+      asm("" : "+v"(y[e]));
+    }
+    f4 v = f4{y[0], y[1], y[2], y[3]};
+#pragma unroll
+    for (int m = 1; m < B / 4; ++m) {
+      const bool take = q == m;
+      v.x = take ? y[4 * m] : v.x;
+      v.y = take ? y[4 * m + 1] : v.y;
+      v.z = take ? y[4 * m + 2] : v.z;
+      v.w = take ? y[4 * m + 3] : v.w;
+    }
+    __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p) + q);
+  } else {
+    storeB<B>(p, x);
+  }
+}
+template <int B>
+constexpr int split_lanes = B % 4 == 0 ? B / 4 : 1;
 
 // NB bytes (2, 4, 8 or 16, naturally aligned) as little-endian 32-bit words.
 template <int NB>
@@ -469,7 +506,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
 #pragma unroll
       for (int bb = 0; bb < CB; ++bb) M[x >> 2][bb][x & 3] = fmaf(kr[x], u[bb], M[x >> 2][bb][x & 3]);
     colsum(qr, y);
-    if (ti == 0) storeB<CB>(a.o + hD + j0, y);
+    if (ti < split_lanes<CB>) storeSplit<CB>(a.o + hD + j0, y, ti);
   }
 
   // ---- compensators: power method with deflation. One barrier per
@@ -594,15 +631,13 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       for (int bb = 0; bb < CB; ++bb) w[bb] = 0.f;
     }
     // compensator l is entry l: a unit key, its value, and G = 0 (window position 0)
-    if (tj == 0) storeB<RB>(a.ek + (erow + l) * D + i0, kk);
-    if (ti == 0) storeB<CB>(a.eu + (erow + l) * D + j0, w);
+    // (kk is alike across a row's 16 tj lanes, w across the 8 ti rows)
+    if (tj < split_lanes<RB>) storeSplit<RB>(a.ek + (erow + l) * D + i0, kk, tj);
+    if (ti < split_lanes<CB>) storeSplit<CB>(a.eu + (erow + l) * D + j0, w, ti);
     if constexpr (KDA) {
-      if (tj == 0) {
-        float z[RB];
-#pragma unroll
-        for (int x = 0; x < RB; ++x) z[x] = 0.f;
-        storeB<RB>(a.eg + (erow + l) * D + i0, z);
-      }
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      static_assert(RB % 4 == 0, "key rows per thread");
+      if (tj < RB / 4) __builtin_nontemporal_store(f4{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f4*>(a.eg + (erow + l) * D + i0) + tj);
     } else if (t == 0) {
       a.eg[erow + l] = 0.f;
     }
@@ -732,7 +767,7 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   if constexpr (RB == 16) {
     a.s[hD + i0 + tj] = sa[0];
   } else {
-    if (tj == 0) storeB<RB>(a.s + hD + i0, sa);
+    if (tj < split_lanes<RB>) storeSplit<RB>(a.s + hD + i0, sa, tj);
   }
   if constexpr (CB >= 4) {
     if (wave == 0) {

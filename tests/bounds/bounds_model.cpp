@@ -52,6 +52,16 @@ void in(const Cfg& c, const char* what, long long off, long long size, long long
   if (off < lo || off + size > hi) fail(c, what, off, lo, hi, t);
 }
 
+// A B-float segment at byte offset seg held alike by a lane group: lane q
+// (q < B/4) stores float4 q; B = 2: lane 0 stores both floats.
+void split_store(const Cfg& c, const char* what, long long seg, int B, int q, long long lo, long long hi, int t) {
+  if (B % 4 == 0) {
+    if (q < B / 4) in(c, what, seg + 16LL * q, 16, lo, hi, t);
+  } else if (q == 0) {
+    in(c, what, seg, 4LL * B, lo, hi, t);
+  }
+}
+
 // ---- sizes, as lq_state_sizes (bytes)
 struct Sizes {
   long long codes, s, c, ek, eu, eg, blen, act_qk, act_v, g, beta, o, head_codes;
@@ -323,7 +333,7 @@ void close_kernel(const Cfg& c, bool dense, bool warm, bool step = false) {
         else in(c, "lds column partials", j0 + (g >> 1), 1, 0, D, t);
         for (int bb = 0; bb < CB; ++bb) in(c, "lds column read", j0 + bb, 1, 0, D, t);
       }
-      if (ti == 0) in(c, "token output store", (hD + j0) * 4, CB * 4, 0, z.o, t);
+      split_store(c, "token output store", (hD + j0) * 4, CB, ti, 0, z.o, t);
     }
     for (int l = 0; l < r; ++l) {
       if (RB == 16) {  // kappa's row partials and totals (D = 128)
@@ -338,9 +348,9 @@ void close_kernel(const Cfg& c, bool dense, bool warm, bool step = false) {
       else if (CB == 4) in(c, "lds column partials", j0 + g, 1, 0, D, t);
       else in(c, "lds column partials", j0 + (g >> 1), 1, 0, D, t);
       for (int bb = 0; bb < CB; ++bb) in(c, "lds column read", j0 + bb, 1, 0, D, t);
-      if (tj == 0) in(c, "compensator key store", ((erow + l) * D + i0) * 4, RB * 4, 0, z.ek, t);
-      if (ti == 0) in(c, "compensator value store", ((erow + l) * D + j0) * 4, CB * 4, 0, z.eu, t);
-      if (KDA && tj == 0) in(c, "compensator G store", ((erow + l) * D + i0) * 4, RB * 4, 0, z.eg, t);
+      split_store(c, "compensator key store", ((erow + l) * D + i0) * 4, RB, tj, 0, z.ek, t);
+      split_store(c, "compensator value store", ((erow + l) * D + j0) * 4, CB, ti, 0, z.eu, t);
+      if (KDA) split_store(c, "compensator G store", ((erow + l) * D + i0) * 4, RB, tj, 0, z.eg, t);
       if (!KDA && t == 0) in(c, "compensator G store", (erow + l) * 4, 4, 0, z.eg, t);
     }
     for (int bb = 0; bb < CB; ++bb) in(c, "residual export", ((hD + j0 + bb) * D + i0) * 4, RB * 4, 0, (long long)c.BH * D * D * 4, t);
@@ -364,7 +374,7 @@ void close_kernel(const Cfg& c, bool dense, bool warm, bool step = false) {
       }
     }
     if (RB == 16) in(c, "row scale store", (hD + i0 + tj) * 4, 4, 0, z.s, t);
-    else if (tj == 0) in(c, "row scale store", (hD + i0) * 4, RB * 4, 0, z.s, t);
+    else split_store(c, "row scale store", (hD + i0) * 4, RB, tj, 0, z.s, t);
     if (CB >= 4) {
       if (wave == 0)
         for (int m = 0; m < NV; ++m) in(c, "column scale store", (hD + j0 + (lane >> 4) * NV + m) * 4, 4, 0, z.c, t);
