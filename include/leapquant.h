@@ -105,7 +105,11 @@ typedef struct lq_state {
                         p = c/2 for even c and 8 + c/2 for odd c. */
   float* row_scale;  /* s [B*H][d_k] key-row smoothing scales */
   float* col_scale;  /* c [B*H][d_v] value-column scales */
-  float* ent_k;      /* [B*H][r + w_max][d_k] entry keys (compensator keys are unit vectors) */
+  float* ent_k;      /* [B*H][r + w_max][d_k] entry keys (compensator keys are unit vectors).
+                        With act_dtype LQ_ACT_BF16 a buffered token's key row (entries r..)
+                        holds its bf16 key k_t, exactly as given, in the row's first
+                        d_k * 2 bytes (little-endian bf16, channel order); the rest of that
+                        row is unused. Compensator rows are fp32 either way. */
   float* ent_u;      /* [B*H][r + w_max][d_v] entry values u_e */
   float* ent_g;      /* [B*H][r + w_max] (GDN) or [B*H][r + w_max][d_k] (KDA): G_e, the
                         cumulative log-decay since the window start (0 for compensators;

@@ -78,6 +78,46 @@ __device__ __forceinline__ float4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t o
   return make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]), __uint_as_float(t[3]));
 }
 
+// Key rows. A compensator's key (entry e < r) is fp32; with bf16 activations
+// a buffered token's key is its bf16 input, held as d_k bf16 values in the
+// first half of its row (exact, and half the bytes). key_load fetches N
+// channels at channel i0 of row e as loaded words (a bf16 row fills the first
+// N/2); key_widen turns them into fp32 where they are used.
+template <bool BF16, int D, int N>
+__device__ __forceinline__ void key_load(__amdgpu_buffer_rsrc_t rk, int e, int r, int i0, float (&x)[N]) {
+  if (BF16 && e >= r) {
+    const uint32_t off = uint32_t(e * D * 4 + i0 * 2);
+    if constexpr (N == 8) {
+      const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, ENTRY_POLICY);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = __uint_as_float(t[c]);
+    } else if constexpr (N == 4) {
+      const v2u t = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, ENTRY_POLICY);
+      x[0] = __uint_as_float(t[0]), x[1] = __uint_as_float(t[1]);
+    } else {
+      static_assert(N == 2, "key channels per lane");
+      x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rk, off, 0, ENTRY_POLICY));
+    }
+#pragma unroll
+    for (int c = N / 2; c < N; ++c) x[c] = 0.f;
+  } else {
+    buf_loadN(rk, uint32_t(e * D + i0) * 4, x);
+  }
+}
+template <bool BF16, int N>
+__device__ __forceinline__ void key_widen(int e, int r, const float (&w)[N], float (&x)[N]) {
+  if (BF16 && e >= r) {
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      const uint32_t b = __float_as_uint(w[c / 2]);
+      x[c] = __uint_as_float((c & 1) ? (b & 0xFFFF0000u) : (b << 16));
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < N; ++c) x[c] = w[c];
+  }
+}
+
 template <int D, bool KDA>
 struct StepShape {
   static constexpr int NT = D >= 128 ? 128 : 64;  // threads per head
@@ -198,7 +238,7 @@ struct HeadStep {
     uint32_t kx_raw, qx_raw;  // q_t, k_t as loaded (bf16 or fp32 bits); converted when used
     uint32_t vj_raw;          // v_t of this thread's value column as loaded (bf16 or fp32 bits)
     float si, cc, gi, beta, gs, Gp;
-    float kr[KPF][CPL], gr[KDA ? KPF : 1][CPL], Gm[KPF];
+    float kr[KPF][CPL], gr[KDA ? KPF : 1][CPL], Gm[KPF];  // kr: key rows as loaded (key_load)
     float4 uv[PFE];
   };
 
@@ -298,7 +338,7 @@ struct HeadStep {
 #pragma unroll
     for (int k = 0; k < KPF; ++k) {
       const int e = grp + NG * k;
-      buf_loadN(rk, uint32_t(e * D + i0) * 4, h.kr[k]);
+      key_load<BF16, D>(rk, e, a.r, i0, h.kr[k]);
       if constexpr (KDA) buf_loadN(rg, g_off(a, e, i0), h.gr[k]);  // zero rows for compensators
       else h.Gm[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, g_off(a, e, 0), 0, ENTRY_POLICY));
     }
@@ -447,13 +487,14 @@ struct HeadStep {
           }
           float row[CPL], gm[CPL], gsc = h.Gm[k];
           if (e0 == 0) {
+            key_widen<BF16>(e, a.r, h.kr[k], row);
 #pragma unroll
-            for (int x = 0; x < CPL; ++x) {
-              row[x] = h.kr[k][x];
+            for (int x = 0; x < CPL; ++x)
               if constexpr (KDA) gm[x] = h.gr[k][x];
-            }
           } else {  // entries beyond the prefetched ones (long windows)
-            buf_loadN(rk, uint32_t(e * D + i0) * 4, row);
+            float w[CPL];
+            key_load<BF16, D>(rk, e, a.r, i0, w);
+            key_widen<BF16>(e, a.r, w, row);
             if constexpr (KDA) buf_loadN(rg, g_off(a, e, i0), gm);
             else gsc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, g_off(a, e, 0), 0, ENTRY_POLICY));
           }
@@ -571,7 +612,10 @@ struct HeadStep {
       __builtin_amdgcn_raw_buffer_store_b32(as_u(fmaf(kqs, u, yq)), buf_rsrc(a.o + P.hD, D * 4), j * 4, 0,
                                             STORE_POLICY);
       __builtin_amdgcn_raw_buffer_store_b32(as_u(u), buf_rsrc(P.eu + E * D, D * 4), j * 4, 0, STORE_POLICY);
-      __builtin_amdgcn_raw_buffer_store_b32(as_u(kx), buf_rsrc(P.ek + E * D, D * 4), j * 4, 0, STORE_POLICY);
+      if constexpr (BF16)  // a token's key row holds its bf16 input (key_load)
+        __builtin_amdgcn_raw_buffer_store_b16(uint16_t(h.kx_raw), buf_rsrc(P.ek + E * D, D * 2), j * 2, 0, STORE_POLICY);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(as_u(kx), buf_rsrc(P.ek + E * D, D * 4), j * 4, 0, STORE_POLICY);
       if constexpr (KDA)
         __builtin_amdgcn_raw_buffer_store_b32(as_u(Gi), buf_rsrc(P.eg + E * D, D * 4), j * 4, 0, STORE_POLICY);
       if (t == 0) {

@@ -234,9 +234,13 @@ __device__ __forceinline__ float act_f(uint32_t b) {
   return __uint_as_float(BF16 ? b << 16 : b);
 }
 
-template <int D, int BITS, bool KDA, bool DENSE, int ACT>
+template <int D, int BITS, bool KDA, bool DENSE, int ACT, bool KB>
 __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   static_assert(!(DENSE && ACT), "the dense encode takes no token");
+  // KB: the buffered tokens' key rows hold bf16 keys (bf16 activations: a
+  // token's key row is its bf16 input in the row's first half; compensator
+  // rows stay fp32); a token of the same width as the buffer
+  static_assert(!(KB && DENSE) && (ACT == 0 || KB == (ACT == 2)), "key row width");
   constexpr int RB = D / 8;   // key rows per thread
   constexpr int CB = D / 16;  // value columns per thread
   constexpr int Q = (1 << (BITS - 1)) - 1;  // 127, 31 or 7
@@ -377,7 +381,12 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
       for (int p = 0; p < NP; ++p) {
         const int e = m0 + (t + NT * p) / V4;
         const uint32_t off = uint32_t(e * D + 4 * c4) * 4;
-        kq[p] = ld4(rk, off);
+        if (KB && e >= r) {  // a token's bf16 key: four channels in 8 bytes
+          const v2u q2 = __builtin_amdgcn_raw_buffer_load_b64(rk, uint32_t(e * D * 4 + 8 * c4), 0, 0);
+          kq[p] = make_float4(as_f(q2[0]), as_f(q2[1]), 0.f, 0.f);
+        } else {
+          kq[p] = ld4(rk, off);
+        }
         uq[p] = ld4(ru, off);
         if constexpr (KDA) ge[p] = ld4(rg, e >= r ? uint32_t((e - r) * D + 4 * c4) * 4 : 0x80000000u);
         else gs[p] = as_f(__builtin_amdgcn_raw_buffer_load_b32(rg, uint32_t(e) * 4, 0, 0));
@@ -390,6 +399,10 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
         const int row = (t + NT * p) / V4;
         const bool in = m0 + row < E;  // rows past E: zeros (no decay factor, which could overflow)
         float4 k4 = kq[p];
+        if (KB && m0 + row >= r) {
+          const uint32_t lo = __float_as_uint(k4.x), hi = __float_as_uint(k4.y);
+          k4 = make_float4(as_f(lo << 16), as_f(lo & 0xFFFF0000u), as_f(hi << 16), as_f(hi & 0xFFFF0000u));
+        }
         if constexpr (KDA) {
           k4.x *= in ? expf(gq.x - ge[p].x) : 0.f;
           k4.y *= in ? expf(gq.y - ge[p].y) : 0.f;
@@ -780,17 +793,18 @@ __global__ void __launch_bounds__(NT) close_kernel(CloseArgs a) {
   if (t == 0) a.blen[bh] = 0;
 }
 
-template <int D, int BITS, bool KDA, bool DENSE, int ACT>
+template <int D, int BITS, bool KDA, bool DENSE, int ACT, bool KB>
 hipError_t launch(const CloseArgs& a, int n_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((close_kernel<D, BITS, KDA, DENSE, ACT>), dim3(n_blocks), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((close_kernel<D, BITS, KDA, DENSE, ACT, KB>), dim3(n_blocks), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int BITS, bool KDA>
 hipError_t launch_k(const lq_dims& d, const CloseArgs& a, int nb, hipStream_t s) {
-  if (a.S) return launch<D, BITS, KDA, true, 0>(a, nb, s);
-  if (!a.q) return launch<D, BITS, KDA, false, 0>(a, nb, s);
-  return d.act_dtype == LQ_ACT_BF16 ? launch<D, BITS, KDA, false, 2>(a, nb, s) : launch<D, BITS, KDA, false, 1>(a, nb, s);
+  if (a.S) return launch<D, BITS, KDA, true, 0, false>(a, nb, s);
+  const bool kb = d.act_dtype == LQ_ACT_BF16;  // buffered keys (and the token) in bf16
+  if (!a.q) return kb ? launch<D, BITS, KDA, false, 0, true>(a, nb, s) : launch<D, BITS, KDA, false, 0, false>(a, nb, s);
+  return kb ? launch<D, BITS, KDA, false, 2, true>(a, nb, s) : launch<D, BITS, KDA, false, 1, false>(a, nb, s);
 }
 
 template <int D, int BITS>

@@ -151,7 +151,9 @@ class State:
         self.codes = torch.zeros((BH, D, D * dims.bits // 8), dtype=torch.int8, device=device)
         self.row_scale = torch.ones((BH, D), **f32)
         self.col_scale = torch.zeros((BH, D), **f32)
-        # entries 0..r-1: compensators; r..r+W-1: buffered tokens
+        # entries 0..r-1: compensators; r..r+W-1: buffered tokens (with bf16
+        # activations a token's key row holds its bf16 key in the row's first
+        # d * 2 bytes; compensator rows are fp32)
         self.ent_k = torch.zeros((BH, r + W, D), **f32)
         self.ent_u = torch.zeros((BH, r + W, D), **f32)
         self.ent_g = torch.zeros((BH, r + W, D) if dims.kda else (BH, r + W), **f32)
@@ -175,6 +177,8 @@ class State:
 
     @property
     def buf_k(self) -> torch.Tensor:
+        """The buffered tokens' key rows as stored (bf16 activations: bf16 keys
+        in each row's first half)."""
         return self.ent_k[:, self.dims.n_comp:]
 
     @property

@@ -95,6 +95,20 @@ void buffer_load(const Cfg& c, const char* what, long long off, long long size, 
   if (off < range && off + size > range) fail(c, what, off, 0, range, t);
 }
 
+// A key-row load of entry e < E at channel i0, n channels: fp32 (compensators,
+// or every row with fp32 activations) or, with bf16 activations, a buffered
+// token's bf16 key in the first half of its row; inside the row and the
+// key descriptor either way.
+void key_row(const Cfg& c, const char* what, int e, int i0, int n, long long rk_size, int t) {
+  const int D = c.D;
+  const bool b16 = c.BF16 && e >= c.r;
+  const long long off = b16 ? (long long)e * D * 4 + i0 * 2 : (long long)(e * D + i0) * 4;
+  const long long size = b16 ? n * 2 : n * 4;
+  const long long row_end = (long long)e * D * 4 + (b16 ? D * 2 : D * 4);
+  in(c, what, off, size, (long long)e * D * 4, row_end, t);
+  in(c, what, off, size, 0, rk_size, t);
+}
+
 // ---------------------------------------------------------------- decode step
 // A G load of entry e < E (the decode step's g_off): GDN one float at 4e;
 // KDA the channels i0.. of row e - r, or, for a compensator row (e < r), an
@@ -177,7 +191,7 @@ void decode_step(const Cfg& c) {
     for (int k = 0; k < KPF; ++k) {
       const int e = grp + NG * k;
       if (e < E) {
-        in(c, "entry key row", (long long)(e * D + i0) * 4, CPL * 4, 0, rk_size, t);
+        key_row(c, "entry key row", e, i0, CPL, rk_size, t);
         g_row(c, "entry G row", e, i0, CPL, rg_size, t);
       }
     }
@@ -207,7 +221,7 @@ void decode_step(const Cfg& c) {
         }
         in(c, "lds kappa", e, 1, 0, MAX_ROWS, t);
         if (e0 > 0) {  // rows past the prefetch, loaded in the pass
-          in(c, "entry key row (pass)", (long long)(e * D + i0) * 4, CPL * 4, 0, rk_size, t);
+          key_row(c, "entry key row (pass)", e, i0, CPL, rk_size, t);
           g_row(c, "entry G row (pass)", e, i0, CPL, rg_size, t);
         }
       }
@@ -231,7 +245,12 @@ void decode_step(const Cfg& c) {
     if (chan) {
       in(c, "o store", (hD + t) * 4, 4, 0, z.o, t);
       in(c, "appended value", eu0 + (long long)(E * D + t) * 4, 4, eu0, eu0 + (long long)NE * D * 4, t);
-      in(c, "appended key", ek0 + (long long)(E * D + t) * 4, 4, ek0, ek0 + (long long)NE * D * 4, t);
+      if (c.BF16) {  // a token's bf16 key in the first half of its row (a D * 2-byte descriptor)
+        in(c, "appended key (bf16)", (long long)t * 2, 2, 0, (long long)D * 2, t);
+        in(c, "appended key row", ek0 + (long long)E * D * 4, (long long)D * 2, ek0, ek0 + (long long)NE * D * 4, t);
+      } else {
+        in(c, "appended key", ek0 + (long long)(E * D + t) * 4, 4, ek0, ek0 + (long long)NE * D * 4, t);
+      }
       if (KDA) in(c, "appended G", eg0 + (long long)(E * D + t) * 4, 4, eg0, eg0 + (long long)NE * D * 4, t);
       if (t == 0) {
         if (!KDA) in(c, "appended G", eg0 + (long long)E * 4, 4, eg0, eg0 + (long long)NE * 4, t);
@@ -303,7 +322,14 @@ void close_kernel(const Cfg& c, bool dense, bool warm, bool step = false) {
         for (int p = 0; p < np; ++p) {
           const int row = (t + NT * p) / V4, e = m0 + row;
           in(c, "lds staged row", row, 1, 0, ch, t);
-          buffer_load(c, "staged key/value", (long long)(e * D + 4 * c4) * 4, 16, rk_size, t);
+          if (c.BF16 && !dense && e >= r) {  // a token's bf16 key: four channels in 8 bytes of the row's first half
+            const long long off = (long long)e * D * 4 + 8 * c4;
+            if (off + 8 > (long long)e * D * 4 + D * 2) fail(c, "staged bf16 key past its half row", off, 0, (long long)e * D * 4 + D * 2, t);
+            buffer_load(c, "staged key (bf16)", off, 8, rk_size, t);
+          } else {
+            buffer_load(c, "staged key", (long long)(e * D + 4 * c4) * 4, 16, rk_size, t);
+          }
+          buffer_load(c, "staged value", (long long)(e * D + 4 * c4) * 4, 16, rk_size, t);
           if (KDA) {
             const long long off = e >= r ? (long long)((e - r) * D + 4 * c4) * 4 : MODEL_G_COMP_OFF;
             if (e < r && off < rg_size) fail(c, "compensator G offset (close)", off, rg_size, 1LL << 32, t);
@@ -403,11 +429,12 @@ int main() {
                   decode_step(Cfg{D, BITS, KDA, BF16, r, w_max, n, bh, BH});
                   ++configs;
                 }
-              for (int n = 0; n <= w_max; ++n)  // close: buf_len <= w_max
-                for (int warm = 0; warm < 2; ++warm) {
-                  close_kernel(Cfg{D, BITS, KDA, 0, r, w_max, n, bh, BH}, false, warm);
-                  ++configs;
-                }
+              for (int BF16 = 0; BF16 < 2; ++BF16)  // (bf16: the buffered keys are bf16)
+                for (int n = 0; n <= w_max; ++n)      // close: buf_len <= w_max
+                  for (int warm = 0; warm < 2; ++warm) {
+                    close_kernel(Cfg{D, BITS, KDA, BF16, r, w_max, n, bh, BH}, false, warm);
+                    ++configs;
+                  }
               close_kernel(Cfg{D, BITS, KDA, 0, r, w_max, 0, bh, BH}, true, false);  // encode
               ++configs;
               for (int BF16 = 0; BF16 < 2; ++BF16)

@@ -78,13 +78,37 @@ def T(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(np.swapaxes(x, -1, -2))
 
 
+def buf_keys_f32(ent_k: np.ndarray, dims: lqk.Dims) -> np.ndarray:
+    """Buffered tokens' keys as fp32 [BH][w_max][d] from the entry key rows. With
+    bf16 activations a token's key row holds its bf16 key in the row's first
+    d * 2 bytes; compensator rows (entries < r) and fp32 rows are fp32."""
+    rows = np.ascontiguousarray(ent_k[:, dims.n_comp:], np.float32)
+    if not dims.bf16:
+        return rows
+    raw = rows.view(np.uint16).reshape(rows.shape[0], rows.shape[1], 2 * dims.d)[:, :, :dims.d]
+    return wk.bf16_to_f32(raw).reshape(rows.shape)
+
+
+def buf_key_rows(buf_k, dims: lqk.Dims) -> np.ndarray:
+    """fp32 buffered keys [BH][w_max][d] -> the entry key rows' contents (bf16
+    activations: the keys must be bf16 values; they fill each row's first half)."""
+    k = np.ascontiguousarray(np.asarray(buf_k, np.float32))
+    if not dims.bf16:
+        return k
+    bits = wk.round_to_bf16(k)
+    assert np.array_equal(wk.bf16_to_f32(bits), k), "buffered keys with bf16 activations must be bf16 values"
+    raw = np.zeros(k.shape[:-1] + (2 * dims.d,), np.uint16)
+    raw[..., :dims.d] = bits
+    return raw.view(np.float32).reshape(k.shape)
+
+
 def download_state(st: lqk.State, dims: lqk.Dims) -> Dict[str, np.ndarray]:
     torch.cuda.synchronize()
     out = {n: getattr(st, n).cpu().numpy() for n in lqk.STATE_FIELDS}
     out["C"] = unpack_codes(out["codes"], dims.bits, dims.d)
     r = dims.n_comp  # entries 0..r-1 are the compensators, the rest the token buffer
     out["comp_k"], out["comp_u"], out["comp_g"] = out["ent_k"][:, :r], out["ent_u"][:, :r], out["ent_g"][:, :r]
-    out["buf_k"], out["buf_u"], out["buf_g"] = out["ent_k"][:, r:], out["ent_u"][:, r:], out["ent_g"][:, r:]
+    out["buf_k"], out["buf_u"], out["buf_g"] = buf_keys_f32(out["ent_k"], dims), out["ent_u"][:, r:], out["ent_g"][:, r:]
     return out
 
 
@@ -108,7 +132,7 @@ def upload_state(st: lqk.State, dims: lqk.Dims, enc: lq.Encoded, buf_k=None, buf
         put(st.comp_u, enc.comp_u)
         st.ent_g[:, :dims.n_comp] = 0.0  # compensators sit at window position 0
     if buf_k is not None:
-        put(st.buf_k, buf_k)
+        put(st.buf_k, buf_key_rows(np.asarray(buf_k, np.float32).reshape(st.buf_k.shape), dims))
         put(st.buf_u, buf_u)
         put(st.buf_g, buf_g)
         st.buf_len.copy_(torch.from_numpy(np.asarray(n, np.int32)))
@@ -209,7 +233,7 @@ def download_heads(st: lqk.State, dims: lqk.Dims, heads) -> Dict[str, np.ndarray
     out["C"] = unpack_codes(out["codes"], dims.bits, dims.d)
     r = dims.n_comp
     out["comp_k"], out["comp_u"], out["comp_g"] = out["ent_k"][:, :r], out["ent_u"][:, :r], out["ent_g"][:, :r]
-    out["buf_k"], out["buf_u"], out["buf_g"] = out["ent_k"][:, r:], out["ent_u"][:, r:], out["ent_g"][:, r:]
+    out["buf_k"], out["buf_u"], out["buf_g"] = buf_keys_f32(out["ent_k"], dims), out["ent_u"][:, r:], out["ent_g"][:, r:]
     return out
 
 
