@@ -56,13 +56,14 @@ def test_fused_bytes_count_the_token_once():
     """The fused launch reads the close's bytes over the n buffered rows plus
     the token's activations and writes its output; against a decode launch
     plus a close of n + 1 rows it saves one pass over the low-bit state, the
-    n buffered rows and the appended row (written and read back)."""
+    n buffered rows and the appended row (written and read back). A buffered
+    token's key is kept at the activation width (bf16 activations: 2 bytes)."""
     d, r = 128, 4
     for bits in (8, 6, 4):
         for kda in (False, True):
             for bf16 in (False, True):
                 for n in (0, 7, 15):
-                    E = 4 * (2 * d + (d if kda else 1))
+                    E = (2 if bf16 else 4) * d + 4 * (d + (d if kda else 1))
                     lowbit = d * d * bits // 8 + 8 * d + 8 * r * d
                     saved = (bm.step_bytes(d, r, bits, kda, bf16, n) + bm.close_bytes(d, r, bits, kda, bf16, n + 1)
                              - bm.fused_bytes(d, r, bits, kda, bf16, n))
