@@ -19,6 +19,7 @@ W = wk.WORKLOADS
 
 CASES = [
     ("qwen_gdn", 8, {}),                                   # bf16 activations
+    ("qwen_gdn", 8, dict(window=32)),                      # bf16 buffered keys over two fold passes
     ("qwen_gdn", 8, dict(act_bf16=False)),
     ("qwen_gdn", 6, {}),
     ("kda_int4", 4, {}),                                   # per-channel decay, fp32 activations

@@ -158,9 +158,11 @@ def _close_checks(R, post, bits, smoothing, F, heads):
     return float(err.max()), g1
 
 
-@pytest.mark.parametrize("d,bits,kda", list(itertools.product(DIMS, BITS, (False, True))))
-def test_close_and_encode_every_instantiation(d, bits, kda):
-    wl = _wl(d, kda, False, batch=4, heads=2)
+@pytest.mark.parametrize("d,bits,kda,bf16", list(itertools.product(DIMS, BITS, (False, True), (False, True))))
+def test_close_and_encode_every_instantiation(d, bits, kda, bf16):
+    # (bf16 activations: the buffered tokens' key rows hold bf16 keys, read by
+    # every fold pass)
+    wl = _wl(d, kda, bf16, batch=4, heads=2)
     dims = runner.dims_for(wl, bits)
     BH = wl.batch * wl.heads
     heads = np.arange(BH)
@@ -171,12 +173,13 @@ def test_close_and_encode_every_instantiation(d, bits, kda):
     dec.encode(runner.states_to_device(S0), dbg)
     post = gh.download_state(dec.state, dims)
     err, g1 = _close_checks(gh.T(dbg.cpu().numpy()), post, bits, wl.smoothing, S0.reshape(-1, d, d), heads)
-    print("encode", d, bits, kda, err, g1)
+    print("encode", d, bits, kda, bf16, err, g1)
     assert err <= 1e-6
     assert g1["same"] >= 0.9999 and g1["max_diff"] <= 1 and g1["s_exact"] and g1["c_ulps"] <= 2.0
-    # 21 tokens, then the close: entries r + 21 = 25 fold in passes of 16 and 9
+    # 21 tokens, then the close: entries r + 21 = 25 (d = 128 stages 20 rows, then 5; d < 128
+    # stages 32 at once)
     n_tok = 21
-    dev = runner.upload_tokens(wk.TokenStream(wl).next(n_tok), False)
+    dev = runner.upload_tokens(wk.TokenStream(wl).next(n_tok), bf16)
     for i in range(n_tok):
         dec.step(dev["q"][i], dev["k"][i], dev["v"][i], dev["g"][i], dev["beta"][i], close=False)
     pre = gh.download_state(dec.state, dims)
@@ -186,7 +189,7 @@ def test_close_and_encode_every_instantiation(d, bits, kda):
     lqk.window_close(dims, dec.state, None, 0, dbg)
     post = gh.download_state(dec.state, dims)
     err, g1 = _close_checks(gh.T(dbg.cpu().numpy()), post, bits, wl.smoothing, F, heads)
-    print("close", d, bits, kda, err, g1)
+    print("close", d, bits, kda, bf16, err, g1)
     assert err <= 1e-6
     assert g1["same"] >= 0.9999 and g1["max_diff"] <= 1 and g1["s_exact"] and g1["c_ulps"] <= 2.0
     assert np.all(post["buf_len"] == 0) and np.all(post["comp_g"] == 0)
