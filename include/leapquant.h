@@ -149,7 +149,8 @@ int leapquant_encode(const lq_dims* dims, const float* S, const lq_state* st,
      y^x = c (.) C^T (s (.) exp(G_t) (.) x) + sum_e u_e (k_e . (exp(G_t - G_e) (.) x)),
      u_t = beta_t (v_t - y^k),  o_t = y^q + (k_t . q_t) u_t,
    with entries e = 0..r+n-1 of the head (compensators included), then appends
-   (k_t, u_t, G_t) as entry r+n and increments buf_len.
+   (k_t, u_t, G_t) as entry r+n (k_t at the activation width, see lq_state.ent_k)
+   and increments buf_len.
    q, k: [B][H][d_k]; v: [B][H][d_v] (fp32 or bf16 per act_dtype);
    g: fp32 [B][H] (GDN) or [B][H][d_k] (KDA), the log-decay (alpha = exp(g));
    beta: fp32 [B][H]; o: fp32 [B][H][d_v] (output).
