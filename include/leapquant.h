@@ -109,7 +109,9 @@ typedef struct lq_state {
                         With act_dtype LQ_ACT_BF16 a buffered token's key row (entries r..)
                         holds its bf16 key k_t, exactly as given, in the row's first
                         d_k * 2 bytes (little-endian bf16, channel order); the rest of that
-                        row is unused. Compensator rows are fp32 either way. */
+                        row is unused. Compensator rows are fp32 either way. A state is
+                        therefore used with one act_dtype while its buffer holds tokens
+                        (at a window boundary the buffer is empty and either may follow). */
   float* ent_u;      /* [B*H][r + w_max][d_v] entry values u_e */
   float* ent_g;      /* [B*H][r + w_max] (GDN) or [B*H][r + w_max][d_k] (KDA): G_e, the
                         cumulative log-decay since the window start (0 for compensators;
