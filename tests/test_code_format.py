@@ -1,6 +1,6 @@
-"""Host-side code layouts (include/leapquant.h, lq_state.codes): the test
-helpers that pack and unpack device code bytes, checked against the layout
-definition written out by hand (CPU only)."""
+"""Host-side layouts (include/leapquant.h: lq_state.codes, and the buffered
+key rows of lq_state.ent_k): the test helpers that pack and unpack device
+bytes, checked against the layout definitions written out by hand (CPU only)."""
 import numpy as np
 import pytest
 
@@ -58,3 +58,44 @@ def test_six_bit_split():
     for code in range(-31, 32):
         hi, lo = code >> 2, code & 3
         assert -8 <= hi <= 7 and 0 <= lo <= 3 and 4 * hi + lo == code
+
+
+# ---- buffered key rows (include/leapquant.h, lq_state.ent_k): with bf16
+# activations a buffered token's row holds its bf16 key in its first d * 2
+# bytes; fp32 rows otherwise
+
+
+def _dims(d, bf16, r=2, w=5):
+    from linear_attention_recurrent_kda_amd import leapquant as lqk
+    return lqk.Dims(batch=1, heads=3, d=d, w_max=w, n_comp=r, bf16=bf16)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_bf16_key_rows_by_definition(d):
+    dims = _dims(d, True)
+    rng = np.random.default_rng(d)
+    bits = rng.integers(0, 1 << 16, size=(3, dims.w_max, d), dtype=np.uint32)
+    bits[(bits & 0x7F80) == 0x7F80] = 0x3F80  # no NaN/Inf patterns
+    k = (bits << 16).view(np.float32)          # bf16 values as fp32
+    rows = gh.buf_key_rows(k, dims)
+    assert rows.shape == k.shape and rows.dtype == np.float32
+    raw = rows.view(np.uint8).reshape(3, dims.w_max, 4 * d)
+    for h in range(3):
+        for e in range(dims.w_max):
+            for c in (0, 1, d // 2, d - 1):
+                b = int(bits[h, e, c])
+                # channel c at bytes 2c, 2c + 1 of the row, little-endian
+                assert raw[h, e, 2 * c] == b & 0xFF and raw[h, e, 2 * c + 1] == b >> 8
+            assert not raw[h, e, 2 * d:].any()     # the row's second half is unused
+    ent = np.zeros((3, dims.n_comp + dims.w_max, d), np.float32)
+    ent[:, :dims.n_comp] = 0.25                  # compensator rows stay fp32
+    ent[:, dims.n_comp:] = rows
+    back = gh.buf_keys_f32(ent, dims)
+    assert np.array_equal(back.view(np.uint32), k.view(np.uint32))
+
+
+def test_key_rows_fp32_and_bf16_values_only():
+    k = np.linspace(-1, 1, 3 * 5 * 32, dtype=np.float32).reshape(3, 5, 32)
+    assert np.array_equal(gh.buf_key_rows(k, _dims(32, False)), k)  # fp32 activations: rows as they are
+    with pytest.raises(AssertionError):
+        gh.buf_key_rows(k + np.float32(1e-3), _dims(32, True))      # not bf16 values
