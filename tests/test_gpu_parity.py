@@ -140,6 +140,7 @@ G3_CASES = [
     ("qwen_gdn", 6, 64, {}),
     ("kda_int4", 6, 48, {}),
     ("kda_int4", 4, 48, dict(act_bf16=True)),   # per-channel decay with bf16 activations
+    ("prefix_mix", 8, 64, dict(act_bf16=True)),  # staggered windows, bf16 buffered keys, close lists
 ]
 
 
@@ -279,6 +280,7 @@ def test_outputs_free_running(name, bits, steps, kw):
     ("kda_int4", 8, 16, None, {}),
     ("tiny_gdn", 8, 5, [1], {}),            # partial window, one sequence of two
     ("prefix_mix", 8, 11, [0, 3, 5], {}),   # partial windows, a close list
+    ("prefix_mix", 8, 11, [0, 3, 5], dict(act_bf16=True)),  # the same with bf16 buffered keys
     ("qwen_gdn", 6, 16, None, {}),
     ("tiny_gdn", 6, 5, [1], {}),            # d = 32: four threads share a low-bit word
     ("tiny_gdn", 6, 7, [0], dict(d_k=64, d_v=64)),             # d = 64: two threads share it
