@@ -488,9 +488,10 @@ struct HeadStep {
           float row[CPL], gm[CPL], gsc = h.Gm[k];
           if (e0 == 0) {
             key_widen<BF16>(e, a.r, h.kr[k], row);
+            if constexpr (KDA) {
 #pragma unroll
-            for (int x = 0; x < CPL; ++x)
-              if constexpr (KDA) gm[x] = h.gr[k][x];
+              for (int x = 0; x < CPL; ++x) gm[x] = h.gr[k][x];
+            }
           } else {  // entries beyond the prefetched ones (long windows)
             float w[CPL];
             key_load<BF16, D>(rk, e, a.r, i0, w);
