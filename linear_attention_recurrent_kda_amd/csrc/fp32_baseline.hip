@@ -9,8 +9,13 @@
 // floats, so each column's update is independent:
 //   u_j = beta (v_j - sum_i alpha_i S_ij k_i),
 //   S_ij <- alpha_i S_ij + k_i u_j,   o_j = sum_i S_ij q_i.
-// One workgroup of 2*D threads per head; D/16 lanes share a column, each lane
-// owns 16 key channels (64 bytes, four 16-byte loads).
+// One workgroup of 2*D threads per head; D/16 lanes share a column and each
+// lane owns 16 key channels as four 16-byte pieces. Piece w of lane li is
+// float4 number (D/16) w + li of the column, so one load or store instruction
+// of a column's lanes covers D contiguous bytes (whole cache lines); lanes
+// holding interleaved channels only changes which partial sums meet in the
+// cross-lane reduction. The state is streamed once per token, so its loads
+// and stores carry the non-temporal hint.
 #include "lq_common.h"
 #include "lq_launch.h"
 
@@ -20,6 +25,7 @@ namespace {
 
 template <int D, bool KDA, bool BF16>
 __global__ void __launch_bounds__(2 * D) baseline_kernel(BaselineArgs a) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
   constexpr int NT = 2 * D;
   constexpr int LPC = D / 16;
   constexpr int NG = NT / LPC;
@@ -29,13 +35,17 @@ __global__ void __launch_bounds__(2 * D) baseline_kernel(BaselineArgs a) {
   __shared__ __align__(16) float s_al[KDA ? D : 4];
 
   const int bh = blockIdx.x, t = threadIdx.x;
-  const int grp = t / LPC, li = t % LPC, i0 = li * 16;
+  const int grp = t / LPC, li = t % LPC;
   const size_t hD = size_t(bh) * D;
-  float* Sh = a.S + hD * D;
+  f4* const Sh = reinterpret_cast<f4*>(a.S + hD * D);
+  // float4 index of piece w of this lane in column j
+  auto at = [&](int j, int w) { return size_t(j) * (D / 4) + LPC * w + li; };
 
-  float S[CPT][16];
+  f4 S[CPT][4];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) load16(Sh + size_t(grp + NG * c) * D + i0, S[c]);
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) S[c][w] = __builtin_nontemporal_load(Sh + at(grp + NG * c, w));
   float vj[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) vj[c] = load_act<BF16>(a.v, hD + grp + NG * c);
@@ -49,39 +59,39 @@ __global__ void __launch_bounds__(2 * D) baseline_kernel(BaselineArgs a) {
   }
   __syncthreads();
 
-  float kk[16], qq[16], al[16];
+  // the same channels of k, q and the decay as the lane's pieces of S
+  f4 kk[4], qq[4], al[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const float4 k4 = reinterpret_cast<const float4*>(&s_k[i0])[w];
-    const float4 q4 = reinterpret_cast<const float4*>(&s_q[i0])[w];
-    kk[4 * w] = k4.x, kk[4 * w + 1] = k4.y, kk[4 * w + 2] = k4.z, kk[4 * w + 3] = k4.w;
-    qq[4 * w] = q4.x, qq[4 * w + 1] = q4.y, qq[4 * w + 2] = q4.z, qq[4 * w + 3] = q4.w;
-    if constexpr (KDA) {
-      const float4 a4 = reinterpret_cast<const float4*>(&s_al[i0])[w];
-      al[4 * w] = a4.x, al[4 * w + 1] = a4.y, al[4 * w + 2] = a4.z, al[4 * w + 3] = a4.w;
-    } else {
-      al[4 * w] = al[4 * w + 1] = al[4 * w + 2] = al[4 * w + 3] = alpha;
-    }
+    kk[w] = reinterpret_cast<const f4*>(s_k)[LPC * w + li];
+    qq[w] = reinterpret_cast<const f4*>(s_q)[LPC * w + li];
+    if constexpr (KDA) al[w] = reinterpret_cast<const f4*>(s_al)[LPC * w + li];
+    else al[w] = f4{alpha, alpha, alpha, alpha};
   }
 
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     float dk = 0.f;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      S[c][x] *= al[x];
-      dk = fmaf(S[c][x], kk[x], dk);
-    }
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        S[c][w][e] *= al[w][e];
+        dk = fmaf(S[c][w][e], kk[w][e], dk);
+      }
     dk = group_sum<LPC>(dk);
     const float u = beta * (vj[c] - dk);
     float dq = 0.f;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      S[c][x] = fmaf(kk[x], u, S[c][x]);
-      dq = fmaf(S[c][x], qq[x], dq);
-    }
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        S[c][w][e] = fmaf(kk[w][e], u, S[c][w][e]);
+        dq = fmaf(S[c][w][e], qq[w][e], dq);
+      }
     dq = group_sum<LPC>(dq);
-    store16(Sh + size_t(grp + NG * c) * D + i0, S[c]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) __builtin_nontemporal_store(S[c][w], Sh + at(grp + NG * c, w));
     if (li == 0) a.o[hD + grp + NG * c] = dq;
   }
 }
