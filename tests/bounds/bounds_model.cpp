@@ -1,6 +1,7 @@
-// Host model of the device addressing of the decode step and the window close
+// Host model of the device addressing of the decode step, the window close
 // (csrc/decode_step.hip, csrc/window_close.hip, with or without the window's
-// last token taken inside the close): every global load and store,
+// last token taken inside the close) and the FP32-state baseline
+// (csrc/fp32_baseline.hip): every global load and store,
 // buffer-descriptor range and LDS index those kernels form, written out again
 // on the host and checked, for every thread of the workgroup, against the
 // sizes the C ABI documents (lq_state_sizes) and the kernels' LDS arrays.
@@ -20,8 +21,8 @@
 #include <cstdlib>
 
 // Planted-mistake switches for the model's own test (defaults are the real
-// sizes): the kappa rows of the decode step's LDS, and slack taken off the
-// entry rows a state holds per head.
+// sizes): the kappa rows of the decode step's LDS, slack taken off the entry
+// rows a state holds per head, and a shift of the FP32 baseline's pieces.
 #ifndef MODEL_KAPPA_ROWS
 #define MODEL_KAPPA_ROWS (8 + 64 + 1)
 #endif
@@ -30,6 +31,9 @@
 #endif
 #ifndef MODEL_ENTRY_SLACK
 #define MODEL_ENTRY_SLACK 0
+#endif
+#ifndef MODEL_BL_PIECE_OFF  // shift of the FP32 baseline's float4 pieces
+#define MODEL_BL_PIECE_OFF 0
 #endif
 
 namespace {
@@ -413,6 +417,35 @@ void close_kernel(const Cfg& c, bool dense, bool warm, bool step = false) {
 
 }  // namespace
 
+// FP32-state baseline: one workgroup of 2D threads per head over a [d_v][d_k]
+// fp32 state; D/16 lanes share a value column and lane li holds float4 pieces
+// (D/16) w + li, w < 4, of columns grp + NG c. Every piece lies inside its own
+// head's state and every float4 of the head is held by exactly one thread.
+void baseline(const Cfg& c) {
+  const int D = c.D, NT = 2 * D, LPC = D / 16, NG = NT / LPC, CPT = D / NG;
+  const long long head = 4LL * D * D, lo = head * c.bh, hi = lo + head;
+  static int held[128 * 128 / 4];
+  for (int x = 0; x < D * D / 4; ++x) held[x] = 0;
+  for (int t = 0; t < NT; ++t) {
+    const int grp = t / LPC, li = t % LPC;
+    for (int cc = 0; cc < CPT; ++cc) {
+      const long long j = grp + NG * cc;
+      in(c, "baseline v/o column", 4LL * (c.bh * (long long)D + j), 4, 4LL * c.bh * D, 4LL * (c.bh + 1) * D, t);
+      for (int w = 0; w < 4; ++w) {
+        const long long piece = j * (D / 4) + LPC * w + li + MODEL_BL_PIECE_OFF;  // float4 index inside the head
+        in(c, "baseline state piece", lo + 16 * piece, 16, lo, hi, t);
+        ++held[piece];
+      }
+    }
+    for (int w = 0; w < 4; ++w) in(c, "baseline lds k/q/decay", 16LL * (LPC * w + li), 16, 0, 4LL * D, t);
+    if (t < D) in(c, "baseline lds fill", 4LL * t, 4, 0, 4LL * D, t);
+  }
+  for (int x = 0; x < D * D / 4; ++x) {
+    ++checks;
+    if (held[x] != 1) fail(c, "baseline state coverage (pieces held once)", x, held[x], 1, -1);
+  }
+}
+
 int main() {
   const int dims[] = {32, 64, 128}, bits[] = {8, 6, 4};
   const int wmaxes[] = {1, 2, 3, 4, 7, 8, 15, 16, 17, 20, 23, 24, 25, 31, 32, 33, 47, 48, 49, 63, 64};
@@ -443,6 +476,11 @@ int main() {
                   ++configs;
                 }
             }
+  for (int D : dims)
+    for (int bh = 0; bh < BH; ++bh) {
+      baseline(Cfg{D, 0, 0, 0, 0, 0, 0, bh, BH});
+      ++configs;
+    }
   std::printf("bounds model: %lld launch configurations, %lld access checks, all inside their buffers\n", configs,
               checks);
   return 0;
