@@ -3,7 +3,7 @@
 // paragraphs; LeapQuant abstract): the buffer is empty, so a head is fully
 // described by its codes, its two scale vectors and its r compensators.
 // Snapshot and restore copy exactly that, one workgroup per head, in 16-byte
-// pieces.
+// pieces, with non-temporal loads and stores (each byte is moved once).
 //
 // Record of one head, in this order (bytes): codes D*D*bits/8, row scales 4D,
 // column scales 4D, compensator keys 4rD, compensator values 4rD. Every
@@ -16,9 +16,11 @@ namespace lq {
 namespace {
 
 __device__ __forceinline__ void copy16(const void* src, void* dst, size_t bytes) {
-  const uint4* s = static_cast<const uint4*>(src);
-  uint4* d = static_cast<uint4*>(dst);
-  for (size_t i = threadIdx.x; i < bytes / 16; i += blockDim.x) d[i] = s[i];
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const u4* s = static_cast<const u4*>(src);
+  u4* d = static_cast<u4*>(dst);
+  for (size_t i = threadIdx.x; i < bytes / 16; i += blockDim.x)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
 }
 
 template <bool SAVE>
